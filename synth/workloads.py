@@ -1,0 +1,347 @@
+"""Seeded synthetic inputs for the activation-sparse gated FFN workloads.
+
+Every array is drawn in fp64 from a stream keyed by (config, seed, stream
+id[, token, attempt]) with numpy's SeedSequence, then rounded once to the
+storage type (fp32 or bf16, round-to-nearest-even directly from fp64). The
+rounded values are what both the CPU oracle (as fp64) and the HIP library (as
+raw fp32 / bf16 bits) receive, so the two sides start from bit-identical
+inputs.
+
+The five workloads are the shapes and distributions the pages' method is
+quoted on (gated FFN with ReLU or SiLU gate, full-rank or rank-d/8 gate,
+bias / threshold / WINA top-k selection, decode and prefill token counts).
+
+Selection inputs (per-token bias, per-token threshold) are defined by the
+active-neuron counts the workload asks for, so placing them needs the gate
+pre-activation. ``_Calib`` computes it in fp64 for that purpose only and
+places every cut in the middle of a gap of at least 2*delta between
+neighbouring pre-activations (or scores, for top-k), re-drawing a token's x
+from its next attempt stream when no such gap exists at the required count.
+That guard band makes the active set unique under any fp32 evaluation whose
+error stays below delta; the test-suite re-checks the band with the oracle.
+Nothing here produces an expected output.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# rounding helpers (input storage types)
+# ---------------------------------------------------------------------------
+
+
+def round_bf16(a) -> np.ndarray:
+    """Nearest bf16 value of each fp64 entry (ties to even), as fp64.
+
+    bf16 keeps 8 significant bits and fp32's exponent range; magnitudes
+    below 2**-126 are flushed to zero (inputs never need denormals).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    out = np.empty_like(a)
+    flat_in, flat_out = a.reshape(-1), out.reshape(-1)
+    step = 1 << 16
+    for s in range(0, flat_in.size, step):
+        blk = flat_in[s:s + step]
+        mant, expo = np.frexp(blk)                  # blk = mant * 2**expo, 0.5 <= |mant| < 1
+        r = np.ldexp(np.rint(mant * 256.0), expo - 8)  # np.rint rounds half to even
+        r[np.abs(blk) < 2.0 ** -126] = 0.0
+        flat_out[s:s + step] = r
+    return out
+
+
+def round_f32(a) -> np.ndarray:
+    """Nearest fp32 value of each fp64 entry (ties to even), as fp64."""
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16_bits(a) -> np.ndarray:
+    """Raw bf16 bit patterns (uint16) of fp64 values already on the bf16 grid."""
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    bits = f.view(np.uint32)
+    if np.any(bits & 0xFFFF):
+        raise ValueError("bf16_bits: value not on the bf16 grid")
+    return (bits >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# workload table
+# ---------------------------------------------------------------------------
+
+# Each entry: shapes, storage type, activation, selection rule, TwELL tile
+# width T and ELL width E, token counts. Names say what the workload is.
+CONFIGS = {
+    "c1": dict(num=1, name="tiny-relu-f32-256x1024", d=256, f=1024, rank=0, ms=(4,),
+               dtype="f32", act="relu", sel="bias", T=64, E=64),
+    "c2": dict(num=2, name="decode-relu-bf16-2048x8192", d=2048, f=8192, rank=0, ms=(1, 16),
+               dtype="bf16", act="relu", sel="bias", T=128, E=64),
+    "c3": dict(num=3, name="lopa-relu-thresh-bf16-4096x14336-r512", d=4096, f=14336, rank=512,
+               ms=(1, 8, 64), dtype="bf16", act="relu", sel="thresh", T=128, E=64),
+    "c4": dict(num=4, name="wina-silu-topk-bf16-4096x11008", d=4096, f=11008, rank=0, ms=(1, 32),
+               dtype="bf16", act="silu", sel="topk", T=128, E=128),
+    "c5": dict(num=5, name="prefill-hybrid-relu-bf16-2048x8192", d=2048, f=8192, rank=0,
+               ms=(4096,), dtype="bf16", act="relu", sel="bias", T=1024, E=128),
+}
+
+# stream ids
+_S_WGATE, _S_WUP, _S_WDOWN, _S_U, _S_V, _S_X, _S_COUNT, _S_MIX, _S_OUTLIER = range(1, 10)
+
+_C1_BIAS = -1.28            # scalar gate bias giving ~10% active (P(N(0,1) > 1.28) = 0.1003)
+_C2_LOG_MEDIAN = math.log(0.01)
+_C2_SIGMA = math.log(8.0) / 2.3263478740408408   # p99 / median = 8 for a lognormal
+_C5_P_BUSY = 0.05
+_C5_BIAS_QUIET = -2.3263478740408408    # -Phi^-1(0.99): ~1% active
+_C5_BIAS_BUSY = -0.5244005127080407     # -Phi^-1(0.70): ~30% active
+_SPARSITY_THRESH = 0.90     # per-token sparsity of the threshold workload
+_TOPK_KEEP = 0.35           # fraction kept by WINA top-k
+_OUTLIER_FRAC = 0.01        # fraction of x channels scaled by 20 (top-k workload)
+_OUTLIER_SCALE = 20.0
+_MAX_ATTEMPTS = 64
+
+
+def _rng(*path) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(p) for p in path]))
+
+
+@dataclass
+class Workload:
+    """One seeded instance: fp64 values of the rounded inputs plus metadata.
+
+    Layouts (row-major): x [m, d]; w_gate, w_up [f, d]; u [f, r]; v [r, d];
+    w_down [d, f] (output-major, the usual down-projection layout).
+    bias / tau are per-token fp32 values held as fp64 (bias_scalar when the
+    workload uses one scalar bias). ``delta`` is the certified half-width of
+    the guard band around every cut.
+    """
+    cid: str
+    name: str
+    d: int
+    f: int
+    rank: int
+    m: int
+    dtype: str
+    act: str
+    sel: str
+    T: int
+    E: int
+    k: int
+    seed: int
+    x: np.ndarray
+    w_up: np.ndarray
+    w_down: np.ndarray
+    w_gate: np.ndarray | None = None
+    u: np.ndarray | None = None
+    v: np.ndarray | None = None
+    bias: np.ndarray | None = None
+    bias_scalar: float | None = None
+    tau: np.ndarray | None = None
+    delta: np.ndarray | None = None
+    attempts: np.ndarray | None = None
+    info: dict = field(default_factory=dict)
+
+    def storage(self, a: np.ndarray) -> np.ndarray:
+        """Array in the device storage type: fp32, or bf16 bit patterns."""
+        if self.dtype == "f32":
+            return np.ascontiguousarray(a.astype(np.float32))
+        return np.ascontiguousarray(bf16_bits(a))
+
+    def bias_per_token(self) -> np.ndarray:
+        if self.bias is not None:
+            return self.bias
+        b = 0.0 if self.bias_scalar is None else self.bias_scalar
+        return np.full(self.m, b, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# calibration (placement of cuts; see module docstring)
+# ---------------------------------------------------------------------------
+
+
+class _Calib:
+    """fp64 gate pre-activation and WINA scores used only to place cuts."""
+
+    def __init__(self, w_gate=None, u=None, v=None, w_up=None, w_down=None):
+        self.w_gate, self.u, self.v, self.w_up = w_gate, u, v, w_up
+        self.col_norm = None
+        if w_down is not None:
+            self.col_norm = np.sqrt(np.einsum("oi,oi->i", w_down, w_down))
+
+    def gate(self, xs: np.ndarray) -> np.ndarray:
+        """Pre-activation for tokens xs [n, d] -> [n, f]."""
+        if self.w_gate is not None:
+            return xs @ self.w_gate.T
+        return (xs @ self.v.T) @ self.u.T
+
+    def wina_scores(self, xs: np.ndarray, bias: float = 0.0) -> np.ndarray:
+        z = self.gate(xs) + bias
+        a = z / (1.0 + np.exp(-z))
+        return np.abs(a * (xs @ self.w_up.T)) * self.col_norm
+
+
+def _rms(g: np.ndarray) -> float:
+    return float(np.sqrt(np.mean(g * g)))
+
+
+def _gap_cut(g: np.ndarray, target: int, delta: float):
+    """Cut value c with exactly n entries of g above c and every |g - c| >= delta.
+
+    Picks the n nearest to ``target`` (the smaller n on a tie) among those
+    whose gap between the n-th and (n+1)-th largest is >= 2*delta; returns
+    (c, n) or None.
+    """
+    s = np.sort(g)[::-1]
+    gaps = s[:-1] - s[1:]                      # gaps[n-1] lies between the n-th and (n+1)-th
+    ns = np.nonzero(gaps >= 2.0 * delta)[0] + 1
+    if ns.size == 0:
+        return None
+    dist = np.abs(ns - target) * 2 + (ns > target)
+    n = int(ns[np.argmin(dist)])
+    return 0.5 * (s[n - 1] + s[n]), n
+
+
+def _draw_x(cfg, cid_num, seed, t, attempt, d, outliers):
+    x = _rng(cid_num, seed, _S_X, t, attempt).standard_normal(d)
+    if outliers is not None:
+        x[outliers] *= _OUTLIER_SCALE
+    return x
+
+
+def _place_cut(cid, cfg, t, g, sc, f, k, num, seed, bias, tau, delta, info) -> bool:
+    """Place token t's cut with a certified guard band; False asks for a re-draw."""
+    if cid == "c1":
+        # one scalar fp32 bias for all tokens; band 2**-14 * rms
+        b = float(np.float32(_C1_BIAS))
+        dl = 2.0 ** -14 * _rms(g)
+        z = g + b
+        if np.min(np.abs(z)) < dl:
+            return False
+        bias[t] = b
+        delta[t] = dl
+        info["target_count"][t] = info["count"][t] = int(np.sum(z > 0))
+        return True
+    if cfg["sel"] == "thresh":
+        # exactly k active: threshold between the k-th and (k+1)-th largest
+        dl = 2.0 ** -12 * _rms(g)
+        s = np.sort(g)[::-1]
+        if s[k - 1] - s[k] < 2.0 * dl:
+            return False
+        tt = float(np.float32(0.5 * (s[k - 1] + s[k])))
+        if np.min(np.abs(g - tt)) < dl or int(np.sum(g > tt)) != k or tt <= 0:
+            return False
+        tau[t] = tt
+        delta[t] = dl
+        info["target_count"][t] = info["count"][t] = k
+        return True
+    if cfg["sel"] == "topk":
+        s = np.sort(sc)[::-1]
+        if 0 < k < f and s[k - 1] - s[k] < 2.0 ** -11 * s[k - 1]:
+            return False
+        delta[t] = 0.0 if k in (0, f) else float(s[k - 1] - s[k]) / 2.0
+        info["target_count"][t] = info["count"][t] = k
+        return True
+    # per-token bias: count from the workload's distribution, cut gap-centred
+    if cid == "c2":
+        p = math.exp(_C2_LOG_MEDIAN + _C2_SIGMA * _rng(num, seed, _S_COUNT, t).standard_normal())
+        target = int(min(max(round(p * f), 1), f))
+    else:
+        busy = _rng(num, seed, _S_MIX, t).random() < _C5_P_BUSY
+        bnom = _C5_BIAS_BUSY if busy else _C5_BIAS_QUIET
+        target = int(min(max(int(np.sum(g + bnom > 0)), 1), f - 1))
+    dl = 2.0 ** -12 * _rms(g)
+    res = _gap_cut(g, target, dl)
+    if res is None:
+        return False
+    cut, n = res
+    b = float(np.float32(-cut))
+    z = g + b
+    if np.min(np.abs(z)) < dl or int(np.sum(z > 0)) != n:
+        return False
+    bias[t] = b
+    delta[t] = dl
+    info["target_count"][t] = target
+    info["count"][t] = n
+    return True
+
+
+def make_workload(cid: str, m: int | None = None, seed: int = 0, *, d: int | None = None,
+                  f: int | None = None, rank: int | None = None, T: int | None = None,
+                  E: int | None = None, k: int | None = None) -> Workload:
+    """Build one seeded instance of workload ``cid`` ("c1".."c5").
+
+    ``d``, ``f``, ``rank``, ``T``, ``E`` and ``k`` override the table for
+    reduced-size test instances; the distributions and rules are unchanged.
+    """
+    cfg = dict(CONFIGS[cid])
+    num = cfg["num"]
+    d = cfg["d"] if d is None else d
+    f = cfg["f"] if f is None else f
+    r = cfg["rank"] if rank is None else rank
+    m = cfg["ms"][0] if m is None else m
+    T = cfg["T"] if T is None else T
+    E = cfg["E"] if E is None else E
+    rnd = round_f32 if cfg["dtype"] == "f32" else round_bf16
+
+    def draw(stream, shape, fan_in):
+        return rnd(_rng(num, seed, stream).standard_normal(shape) / math.sqrt(fan_in))
+
+    w_gate = u = v = None
+    if r:
+        u = draw(_S_U, (f, r), r)
+        v = draw(_S_V, (r, d), d)
+    else:
+        w_gate = draw(_S_WGATE, (f, d), d)
+    w_up = draw(_S_WUP, (f, d), d)
+    w_down = draw(_S_WDOWN, (d, f), f)
+
+    outliers = None
+    if cfg["sel"] == "topk":
+        n_out = int(math.ceil(_OUTLIER_FRAC * d))
+        outliers = np.sort(_rng(num, seed, _S_OUTLIER).choice(d, size=n_out, replace=False))
+
+    calib = _Calib(w_gate, u, v, w_up, w_down if cfg["sel"] == "topk" else None)
+    x = np.zeros((m, d))
+    attempts = np.zeros(m, dtype=np.int64)
+    delta = np.zeros(m)
+    bias = np.zeros(m) if cfg["sel"] != "topk" else None
+    tau = None
+    bias_scalar = None
+    if k is None:
+        if cfg["sel"] == "topk":
+            k = int(round(_TOPK_KEEP * f))
+        elif cfg["sel"] == "thresh":
+            k = f - int(round(_SPARSITY_THRESH * f))
+        else:
+            k = 0
+    if cfg["sel"] == "thresh":
+        tau = np.zeros(m)
+    info = {"target_count": np.zeros(m, dtype=np.int64), "count": np.zeros(m, dtype=np.int64)}
+
+    pending = np.arange(m)
+    for a in range(_MAX_ATTEMPTS):
+        if pending.size == 0:
+            break
+        xs = np.stack([rnd(_draw_x(cfg, num, seed, t, a, d, outliers)) for t in pending])
+        gs = calib.gate(xs)
+        scs = calib.wina_scores(xs) if cfg["sel"] == "topk" else None
+        failed = []
+        for row, t in enumerate(pending):
+            ok = _place_cut(cid, cfg, t, gs[row], None if scs is None else scs[row], f, k,
+                            num, seed, bias, tau, delta, info)
+            if ok:
+                x[t] = xs[row]
+                attempts[t] = a
+            else:
+                failed.append(t)
+        pending = np.asarray(failed, dtype=np.int64)
+    if pending.size:
+        raise RuntimeError(f"no certified draw for tokens {pending[:8]} of {cid}")
+    if cid == "c1":
+        bias_scalar = float(np.float32(_C1_BIAS))
+
+    return Workload(cid=cid, name=cfg["name"], d=d, f=f, rank=r, m=m, dtype=cfg["dtype"],
+                    act=cfg["act"], sel=cfg["sel"], T=T, E=E, k=int(k), seed=seed, x=x,
+                    w_up=w_up, w_down=w_down, w_gate=w_gate, u=u, v=v,
+                    bias=bias if cid != "c1" else None, bias_scalar=bias_scalar,
+                    tau=tau, delta=delta, attempts=attempts, info=info)
