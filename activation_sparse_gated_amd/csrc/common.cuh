@@ -1,0 +1,133 @@
+// Device helpers shared by the gfx950 kernels of the sparse gated FFN.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define FFN_WAVE 64
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace ffn {
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// 8 bf16 packed in a uint4 -> 8 floats (element e of the 16-byte chunk -> f[e]).
+__device__ __forceinline__ void unpack8(const uint4 v, float* f) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------- wave ops
+// Butterfly sum: every lane ends with the same value (fp add is commutative).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, FFN_WAVE);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, FFN_WAVE);
+  return v;
+}
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (FFN_WAVE - 1); }
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Inclusive scan of ints across the wave (Hillis-Steele with shuffles).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, FFN_WAVE);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan over a block of NT threads (NT multiple of 64, <= 1024);
+// `scratch` holds NT/64 ints. Returns the exclusive prefix; *total = sum.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
+  const int w = threadIdx.x / FFN_WAVE, l = lane_id();
+  int inc = wave_incl_scan(v);
+  if (l == 63) scratch[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / FFN_WAVE; ++i) {
+    int s = scratch[i];
+    if (i < w) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// ---------------------------------------------------------------- atomics
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store64_relaxed(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load64_relaxed(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup-wide "last one out" ticket: every thread fences its prior global
+// writes, thread 0 takes a ticket; returns true in the block that arrives last
+// (which then sees every other block's writes). The counter is reset to 0 by
+// that block, so it is ready for the next launch.
+__device__ __forceinline__ bool block_last_arrival(uint32_t* counter, uint32_t total, int* s_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = atomic_add_agent(counter, 1u);
+    bool last = (t == total - 1);
+    if (last) atomic_store_agent(counter, 0u);
+    *s_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  bool last = *s_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// ---------------------------------------------------------------- control words
+// Layout of the per-handle control block in the workspace (uint32 words).
+enum CtrlWord : int {
+  CTRL_EPOCH = 0,       // incremented once per gate pass; tags look-back words
+  CTRL_GATE_DONE = 1,   // completion ticket of the gate kernel
+  CTRL_VSTAGE_DONE = 2, // reserved
+  CTRL_TOPK_DONE = 3,   // completion ticket of the top-k kernel
+  CTRL_TILE_TICKETS = 64  // per-tile split-K tickets start here
+};
+
+}  // namespace ffn

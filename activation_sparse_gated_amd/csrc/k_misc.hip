@@ -1,0 +1,76 @@
+// Set-up kernels: W_down layout change, WINA column norms, buffer fill.
+#include "common.cuh"
+#include "kernels.cuh"
+
+namespace ffn {
+
+// dst[c][r] = src[r][c] through a 64 x 64 LDS tile (coalesced on both sides).
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T* __restrict__ dst,
+                                                  int rows, int cols) {
+  __shared__ T buf[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) buf[i][tx] = src[(size_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) dst[(size_t)c * rows + r] = buf[tx][i];
+  }
+}
+
+hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int esize, hipStream_t s) {
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+  if (esize == 2)
+    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src, (uint16_t*)dst, rows, cols);
+  else
+    hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s, (const float*)src, (float*)dst, rows, cols);
+  return hipGetLastError();
+}
+
+// One wave per neuron row of the neuron-major W_down^T [F x d]: the column
+// norm ||W_down[:, i]||_2 of the WINA score (WINA page, section 3.1). Each
+// lane sums the squares of its strided elements in order, the wave combines
+// them by butterfly, and the square root is taken in double, which rounds the
+// fp32 result correctly.
+__global__ __launch_bounds__(256) void k_rownorm(const void* __restrict__ w, float* __restrict__ c,
+                                                 int F, int d, int dtype) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= F) return;
+  float s = 0.f;
+  if (dtype == DT_BF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(w) + (size_t)row * d;
+    for (int k = lane; k < d; k += 64) {
+      const float v = bf2f(p[k]);
+      s = fmaf(v, v, s);
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(w) + (size_t)row * d;
+    for (int k = lane; k < d; k += 64) s = fmaf(p[k], p[k], s);
+  }
+  s = wave_sum(s);
+  if (lane == 0) c[row] = (float)sqrt((double)s);
+}
+
+hipError_t launch_rownorm(const void* w, float* c, int F, int d, int dtype, hipStream_t s) {
+  hipLaunchKernelGGL(k_rownorm, dim3((F + 3) / 4), dim3(256), 0, s, w, c, F, d, dtype);
+  return hipGetLastError();
+}
+
+__global__ void k_fill_u32(uint32_t* p, uint32_t v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace ffn

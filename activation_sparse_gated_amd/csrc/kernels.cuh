@@ -1,0 +1,98 @@
+// Internal interface between the C ABI layer and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffn {
+
+enum Dtype : int { DT_F32 = 0, DT_BF16 = 1 };
+enum Act : int { ACT_RELU = 0, ACT_SILU = 1 };
+enum Sel : int { SEL_BIAS = 0, SEL_THRESH = 1, SEL_TOPK = 2 };
+enum BMode : int { B_NATIVE = 0, B_F32_SPLIT = 1 };
+enum EpiKind : int { EPI_STORE_F32 = 0, EPI_TWELL = 1, EPI_WINA = 2, EPI_DENSE_H = 3, EPI_Y = 4 };
+
+// C[n, m] = sum_k A[n, k] * B[m, k]: A holds weight rows (one or two matrices
+// stacked per tile), B holds token rows. Both are K-contiguous.
+struct GemmDesc {
+  int dtype;              // element type of A (and of B unless bmode = B_F32_SPLIT)
+  const void* A0;         // rows [0, nrows) of matrix 0
+  const void* A1;         // matrix 1 (nmat == 2): the second half of every tile
+  int nmat;               // 1 or 2
+  int nrows;              // rows per matrix
+  int lda;                // elements
+  int K;                  // contraction length (multiple of 32)
+  const void* B;          // token rows
+  int ldb;                // elements
+  int bmode;              // B_NATIVE or B_F32_SPLIT (fp32 B split into bf16 hi + lo)
+  int M;                  // token count bound known on the host
+  const int32_t* gather;  // B row of token slot m is gather[m]; null = m
+  const int32_t* m_dev;   // device-side token count (dense backup); null = M
+  int nt;                 // rows per workgroup tile (16, 32, 64, 128; per matrix * nmat)
+  int mt;                 // tokens per workgroup (16, 32 or 64)
+  int ks;                 // workgroups splitting K (>= 1)
+  float* partial;         // split-K partial tiles (ks > 1)
+  uint32_t* tickets;      // split-K tickets, one per (tile, token block), zero on entry
+  uint32_t* ctrl;         // control block
+};
+
+struct EpiDesc {
+  int kind;               // EpiKind
+  int F;                  // neurons (rows per matrix)
+  int out_f32;            // outputs in fp32 (fp32 configs) instead of bf16
+  const int32_t* tok_of;  // token id of slot m (dense backup); null = m
+  const float* bias;      // [tokens] or null
+  float bias_scalar;
+  const float* tau;       // [tokens] (THRESH)
+  int sel, act;
+  float* g_debug;         // [tokens x F] gate before bias
+  float* s_debug;         // [tokens x F] WINA scores
+  // EPI_STORE_F32
+  float* out; int ldo;
+  // EPI_TWELL
+  int T, E;
+  int32_t* cnt; uint16_t* idx; void* val;
+  uint8_t* route; int32_t* dense_list; int32_t* n_dense;
+  int32_t* offs;          // [M + 1] entry prefix of non-routed tokens (sparse schedule)
+  uint64_t* lb;           // look-back words [M x F / nt]
+  // EPI_WINA
+  const float* colnorm; float* s_buf; float* h_buf;
+  // EPI_DENSE_H
+  void* hout; int ldh; const float* g_ext;
+  // EPI_Y
+  void* y; int ldy; const int32_t* yrows;
+};
+
+hipError_t launch_gemm(const GemmDesc& g, const EpiDesc& e, hipStream_t s);
+
+// Transpose rows x cols (row-major) -> cols x rows, element size 2 or 4 bytes.
+hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int esize, hipStream_t s);
+// c[i] = || row i of the neuron-major matrix [F x d] ||_2 (fp32, correctly rounded sqrt).
+hipError_t launch_rownorm(const void* w, float* c, int F, int d, int dtype, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+
+struct TopkDesc {
+  int M, F, k, T, dtype;
+  const float* s_buf; const float* h_buf;
+  int32_t* cnt; uint16_t* idx; void* val;
+  uint8_t* route; int32_t* dense_list; int32_t* n_dense; int32_t* offs;
+  uint32_t* ctrl;
+};
+hipError_t launch_topk(const TopkDesc& d, hipStream_t s);
+
+struct UpdownDesc {
+  int dtype, M, d, F, T, E;
+  int down_only;          // TOPK: pack values are h, no up product
+  const void* x; const void* w_up; const void* w_down_nm;
+  const int32_t* cnt; const uint16_t* idx; const void* val; const uint8_t* route;
+  const int32_t* offs;    // [M + 1]
+  void* y;
+  float* partial;         // [(grid + M) x d]
+  int grid;               // workgroups of the sparse kernel
+  int min_chunk;          // minimum entries per workgroup
+};
+// Fused sparse up + down over the pack, then the cross-workgroup sum of
+// partial rows (two launches, timed separately by the caller).
+hipError_t launch_updown(const UpdownDesc& u, hipStream_t s);
+hipError_t launch_updown_reduce(const UpdownDesc& u, hipStream_t s);
+
+}  // namespace ffn

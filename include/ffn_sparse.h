@@ -1,0 +1,205 @@
+/*
+ * ffn_sparse.h -- C ABI of the activation-sparse gated FFN library (MI355X / gfx950).
+ *
+ * The block computed is y = W_down (a(z) * (W_up x)), z = G(x) + b, where G is
+ * the gate projection (full rank, W_gate x, or low rank, U (V x)), a(.) is the
+ * gate activation and only the neurons the selection rule keeps take part.
+ *   - Gated FFN order, per-token unstructured sparsity, low-rank gate with rank
+ *     ratio 1/8: LoPA page ("Meta FAIR and Inria's LoPA Gating Hits 3.31x Real
+ *     GPU Speedup for LLM Inference"), section "How LoPA Gating Restructures FFN
+ *     Computation".
+ *   - ReLU sparsity, tile-wise ELLPACK (TwELL) written by the gate epilogue, one
+ *     pass for the up and down products, dense backup for busy tokens:
+ *     Sparser/Faster/Lighter page (news.neo-ai.one article 2802 on "Sparser,
+ *     Faster, Lighter Transformer Language Models"), sections "稀疏不等於提速",
+ *     "TwELL 減掉轉換開銷" and "Hybrid 應對非均勻稀疏".
+ *   - WINA score |h_i| * ||W_down[:, i]||_2 with top-k: WINA page
+ *     ("大语言模型推理加速新突破：解读WINA框架的核心原理与实践价值"), section 3.1.
+ *
+ * Conventions for every entry point
+ *   - Pointers named w_*, x, y, pack fields, workspace and the debug outputs are
+ *     DEVICE pointers allocated by the caller; the library never allocates or
+ *     frees device memory and never synchronises the stream.
+ *   - Matrices are row-major and dense: W_gate, W_up [d_ff x d_model];
+ *     U [d_ff x rank]; V [rank x d_model]; W_down [d_model x d_ff] (output-major)
+ *     or, with wdown_out_major = 0, its transpose [d_ff x d_model] (neuron-major);
+ *     x, y [m x d_model]. Element type: fp32 or bf16 (raw 16-bit patterns) per
+ *     config.dtype; accumulation is fp32.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream). Arguments are validated before anything is launched; on an error
+ *     nothing is written. FFN_E_HIP reports a failed launch, after which the
+ *     handle must be re-initialised.
+ *   - A handle owns host memory only and is bound to the workspace it was
+ *     initialised with; calls on one handle must be serialised on one stream.
+ *   - Required alignment: 16 bytes for every device pointer.
+ */
+#ifndef FFN_SPARSE_H
+#define FFN_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FFN_SPARSE_ABI_VERSION 1
+
+typedef enum {
+  FFN_OK = 0,
+  FFN_E_INVALID = -1,      /* bad argument: null, misaligned, out of range      */
+  FFN_E_UNSUPPORTED = -2,  /* valid but not built: shape / mode combination      */
+  FFN_E_WORKSPACE = -3,    /* workspace smaller than ffn_sparse_workspace_bytes  */
+  FFN_E_HIP = -4           /* a HIP launch failed                                */
+} ffn_status;
+
+typedef enum { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype;
+typedef enum { FFN_RELU = 0, FFN_SILU = 1 } ffn_act;
+
+/* Selection rule.
+ *   BIAS:   active <=> z > 0 (ReLU gate); value a = z.
+ *   THRESH: active <=> z > max(tau_t, 0) (ReLU gate); value a = z (passes through).
+ *   TOPK_WINA: h = a(z) * (W_up x) for every neuron, score s_i = |h_i| * c_i with
+ *           c_i = ||W_down[:, i]||_2; the k largest scores per token are kept,
+ *           ties to the lower index; pack values are h_i. Requires ell_w == tile_w. */
+typedef enum { FFN_SEL_BIAS = 0, FFN_SEL_THRESH = 1, FFN_SEL_TOPK_WINA = 2 } ffn_select;
+
+typedef struct {
+  int32_t d_model;          /* multiple of 64, 64..4096                               */
+  int32_t d_ff;             /* multiple of tile_w                                      */
+  int32_t rank;             /* 0: full gate W_gate; > 0 (multiple of 32): U, V factors */
+  int32_t dtype;            /* ffn_dtype                                               */
+  int32_t act;              /* ffn_act (BIAS/THRESH need RELU)                         */
+  int32_t sel;              /* ffn_select                                              */
+  int32_t tile_w;           /* TwELL tile width T: multiple of 16, 16..1024             */
+  int32_t ell_w;            /* TwELL ELL width E: 0 <= E <= T                          */
+  int32_t wdown_out_major;  /* 1: w_down is [d_model x d_ff]; 0: [d_ff x d_model]      */
+  int32_t max_m;            /* largest token count a call may pass (>= 1)              */
+} ffn_sparse_config;
+
+/* TwELL pack (tile-wise ELLPACK) of the selected activations, token-major.
+ * With NT = d_ff / tile_w tiles per token:
+ *   cnt        int32  [m x NT]      true number of active neurons in tile j
+ *   idx        uint16 [m x NT x E]  first min(cnt, E) active local offsets
+ *                                   (0..T-1), ascending; padding 0xFFFF
+ *   val        [m x NT x E]         their values a_i (h_i for TOPK): bf16 bits for
+ *                                   bf16 configs, fp32 for fp32; padding 0
+ *   route      uint8  [m]           1 when some tile of the token has cnt > E
+ *   dense_list int32  [m]           routed token ids, ascending (first n_dense valid)
+ *   n_dense    int32  [1]           number of routed tokens
+ * All device pointers, caller-owned. */
+typedef struct {
+  int32_t *cnt;
+  uint16_t *idx;
+  void *val;
+  uint8_t *route;
+  int32_t *dense_list;
+  int32_t *n_dense;
+} ffn_twell_pack;
+
+typedef struct ffn_sparse_handle ffn_sparse_handle;
+
+/* ABI version compiled into the library (FFN_SPARSE_ABI_VERSION). */
+int32_t ffn_sparse_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char *ffn_sparse_status_string(ffn_status s);
+
+/* Validate a config without touching the GPU: FFN_OK, FFN_E_INVALID or
+ * FFN_E_UNSUPPORTED. */
+ffn_status ffn_sparse_check_config(const ffn_sparse_config *cfg);
+
+/* Bytes of device workspace a handle needs for this config (0 if the config
+ * is not valid). The workspace holds the neuron-major (or output-major) copy of
+ * W_down, WINA column norms, the low-rank intermediate, the sparse-path
+ * schedule, partial sums and counters. */
+size_t ffn_sparse_workspace_bytes(const ffn_sparse_config *cfg);
+
+/* Bytes of the six pack fields for m tokens, each field rounded up to 256 bytes,
+ * in the order cnt, idx, val, route, dense_list, n_dense (0 if invalid). */
+size_t ffn_sparse_pack_bytes(const ffn_sparse_config *cfg, int32_t m);
+
+/* Create a handle. w_gate_or_u is W_gate (rank 0) or U (rank > 0); v_or_null is
+ * V (rank > 0) or NULL. The weights are borrowed (not copied) and must outlive
+ * the handle. Launches, on `stream`, the W_down transpose into the workspace,
+ * the WINA column-norm pass (TOPK configs) and the counter reset.
+ * Column norms: WINA page, section 3.1. */
+ffn_status ffn_sparse_init(const ffn_sparse_config *cfg, const void *w_gate_or_u,
+                           const void *v_or_null, const void *w_up, const void *w_down,
+                           void *workspace, size_t workspace_bytes, void *stream,
+                           ffn_sparse_handle **out);
+
+/* Gate projection + activation + selection, writing the TwELL pack directly
+ * from the gate kernel's epilogue (no separate conversion pass), then routing
+ * (route / dense_list / n_dense).
+ *   x          [m x d_model] device
+ *   bias       [m] fp32 device per-token gate bias, or NULL to use bias_scalar
+ *   tau        [m] fp32 device thresholds (THRESH only), else NULL
+ *   k          kept neurons per token (TOPK only), 0 <= k <= d_ff
+ *   g_debug    NULL, or [m x d_ff] fp32 device: the gate projection G(x) before bias
+ *   s_debug    NULL, or [m x d_ff] fp32 device: WINA scores (TOPK only)
+ * Source: Sparser/Faster/Lighter page, "TwELL 減掉轉換開銷" (pack emitted in the
+ * gate epilogue); "Hybrid 應對非均勻稀疏" (routing). 0 <= m <= max_m. */
+ffn_status ffn_sparse_gate_pack(ffn_sparse_handle *h, const void *x, int32_t m,
+                                const float *bias, float bias_scalar, const float *tau,
+                                int32_t k, ffn_twell_pack *pack, float *g_debug,
+                                float *s_debug, void *stream);
+
+/* Fused sparse up + down over the pack for every non-routed token: for each
+ * packed neuron i, u_i = <W_up[i,:], x>, h_i = val_i * u_i (TOPK: h_i = val_i,
+ * no up product), y += h_i * W_down[:, i]; h stays in registers. Writes y rows
+ * of non-routed tokens (zero rows for tokens with no active neuron); routed
+ * rows are left untouched. Requires the pack written by ffn_sparse_gate_pack on
+ * this handle for the same x and m.
+ * Source: Sparser/Faster/Lighter page, "TwELL 減掉轉換開銷" (single pass over up
+ * and down without storing h). */
+ffn_status ffn_sparse_updown(ffn_sparse_handle *h, const void *x, int32_t m,
+                             const ffn_twell_pack *pack, void *y, void *stream);
+
+/* Dense backup for the routed tokens (dense_list[0..n_dense)): recomputes the
+ * gate for those tokens and evaluates the same function densely on matrix
+ * cores, writing their y rows. Same selection arguments as gate_pack.
+ * Source: Sparser/Faster/Lighter page, "Hybrid 應對非均勻稀疏". */
+ffn_status ffn_sparse_dense_fallback(ffn_sparse_handle *h, const void *x, int32_t m,
+                                     const float *bias, float bias_scalar, const float *tau,
+                                     int32_t k, const ffn_twell_pack *pack, void *y,
+                                     void *stream);
+
+/* gate_pack + updown + dense_fallback: the whole sparse forward pass. */
+ffn_status ffn_sparse_forward(ffn_sparse_handle *h, const void *x, int32_t m,
+                              const float *bias, float bias_scalar, const float *tau,
+                              int32_t k, ffn_twell_pack *pack, void *y, void *stream);
+
+/* The same function evaluated densely over every neuron (the comparison
+ * baseline): bias / threshold gates keep their elementwise mask; a TOPK config
+ * keeps every neuron (k = d_ff). */
+ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t m,
+                                    const float *bias, float bias_scalar, const float *tau,
+                                    void *y, void *stream);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around each
+ * kernel. enable = 1 starts recording (up to `capacity` launches per kernel
+ * kind), 0 stops. ffn_sparse_timing_read synchronises on the recorded events
+ * and returns, for kernel kind `kind` (see ffn_kernel_kind), the number of
+ * launches and their total milliseconds, then clears that kind. */
+typedef enum {
+  FFN_K_GATE = 0,      /* gate GEMM + selection epilogue (+ TwELL, routing)    */
+  FFN_K_LOWRANK_V = 1, /* low-rank gate first stage t = V x                    */
+  FFN_K_TOPK = 2,      /* WINA top-k selection + pack                          */
+  FFN_K_UPDOWN = 3,    /* fused sparse up + down                               */
+  FFN_K_REDUCE = 4,    /* cross-workgroup sum of partial y rows                */
+  FFN_K_FALLBACK = 5,  /* dense backup kernels                                 */
+  FFN_K_DENSE = 6,     /* dense baseline kernels                               */
+  FFN_K_COUNT = 7
+} ffn_kernel_kind;
+ffn_status ffn_sparse_timing_enable(ffn_sparse_handle *h, int32_t enable, int32_t capacity);
+ffn_status ffn_sparse_timing_read(ffn_sparse_handle *h, int32_t kind, int32_t *launches,
+                                  double *total_ms);
+
+/* Free the host-side handle (device memory belongs to the caller). */
+void ffn_sparse_destroy(ffn_sparse_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FFN_SPARSE_H */
