@@ -13,7 +13,7 @@ import pytest
 
 from oracle import ffn_oracle as O
 from synth import Workload, make_workload
-from tests.gpu_util import (check_gate_band, check_pack, check_y, f32_dev, host, make_ffn, sel_args,
+from tests.gpu_util import (check_gate_band, check_pack, check_scores, check_y, f32_dev, host, make_ffn, sel_args,
                             to_dev, y_to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -36,9 +36,7 @@ def run_full(wl, ref, *, E=None, check_band=True):
     if check_band and wl.sel != "topk":
         check_gate_band(wl, g_dbg.cpu().numpy(), ref)
     if wl.sel == "topk":
-        s = s_dbg.cpu().numpy().astype(np.float64)
-        rel = np.abs(s - ref["scores"]) / np.maximum(ref["scores"], 1e-30)
-        assert np.max(rel[ref["scores"] > 1e-6]) <= 2.0 ** -13
+        check_scores(wl, s_dbg.cpu().numpy(), ref)
     check_pack(wl, pack, ref, E=E)
     y = ffn.updown(x, pack)
     ffn.dense_fallback(x, pack, y, **kw)
@@ -48,7 +46,8 @@ def run_full(wl, ref, *, E=None, check_band=True):
     y2, pack2 = ffn.forward(x, **kw)
     torch.cuda.synchronize()
     assert np.array_equal(host(y2)[: wl.m], host(y)[: wl.m])
-    assert np.array_equal(host(pack2.idx), host(pack.idx))
+    if (wl.E if E is None else E) > 0:
+        assert np.array_equal(host(pack2.idx)[: wl.m], host(pack.idx)[: wl.m])
     return worst
 
 
