@@ -4,12 +4,14 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
 
 #include "../../include/ffn_sparse.h"
 #include "kernels.cuh"
+#include "gemm_core.cuh"
 
 using namespace ffn;
 
@@ -43,25 +45,33 @@ int pick_nt(int nrows, int nmat, int T, int mblocks, int want, bool f32) {
 
 int pick_mt(int m) { return m <= 16 ? 16 : (m <= 32 ? 32 : 64); }
 
+// Token counts up to this are "decode": the sparse kernel also evaluates
+// routed tokens (no extra launches); larger counts use the dense backup GEMMs.
+constexpr int kDecodeMaxM = 64;
+
 struct Workspace {
   uint32_t* ctrl;       // kCtrlWords control words + kTicketWords tickets
   void* wdown_alt;      // the W_down layout the caller did not pass
   float* colnorm;       // [F]
-  float* lr_t;          // [max_m x rank]
-  float* lr_t_fb;       // [max_m x rank] (dense backup)
-  float* g_ext;         // [max_m x F] low-rank gate values of the dense paths
-  float* splitk;        // split-K partial tiles
-  size_t splitk_floats;
-  float* wina_s;        // [max_m x F]
-  float* wina_h;        // [max_m x F]
-  uint64_t* lb;         // [max_m x F / 16]
-  int32_t* offs;        // [max_m + 1]
-  float* ud_partial;    // [(ud_grid + max_m) x d]
-  void* hbuf;           // [max_m x F] dense hidden
+  float* lr_slabs;       // [kMaxSlabs x max_m x rank] first-stage partial slabs
+  float* lr_t;           // [max_m x rank] summed intermediate
+  float* g_ext;          // [max_m x F] low-rank gate values of the dense paths
+  float* wina_s;         // [max_m x F]
+  float* wina_h;         // [max_m x F]
+  uint64_t* lb;          // [max_m x F / 16]
+  float* ud_partial;     // [ud_rows x d]
+  size_t ud_rows;
+  void* hbuf;            // [max_m x F] dense hidden
   size_t total;
 };
 
-int ud_grid_for(int cus) { return std::max(64, cus); }
+constexpr int kMaxSlabs = 8;
+// Partial y rows of the sparse kernel: enough for 4 per CU, and for every
+// token at the coarsest grouping (64 tiles per workgroup).
+size_t ud_rows_for(const ffn_sparse_config& c, int cus) {
+  const size_t ntiles = c.d_ff / c.tile_w;
+  return std::max<size_t>((size_t)4 * cus, (size_t)c.max_m * ((ntiles + 63) / 64));
+}
 
 // Carves the workspace (base may be null to only compute the size).
 Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
@@ -74,23 +84,18 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
   };
   const size_t es = esize_of(c.dtype);
   const size_t F = c.d_ff, d = c.d_model, r = c.rank, M = c.max_m;
-  const size_t Mp = (M + 63) / 64 * 64;
   w.ctrl = (uint32_t*)take((kCtrlWords + kTicketWords) * sizeof(uint32_t));
   w.wdown_alt = take(F * d * es);
   w.colnorm = (float*)take(F * sizeof(float));
+  w.lr_slabs = (float*)take(std::max<size_t>(1, kMaxSlabs * M * r) * sizeof(float));
   w.lr_t = (float*)take(std::max<size_t>(1, M * r) * sizeof(float));
-  w.lr_t_fb = (float*)take(std::max<size_t>(1, M * r) * sizeof(float));
   w.g_ext = (float*)take(r ? M * F * sizeof(float) : 16);
-  // split-K partials: worst case is a 16-row tile split 16 ways over every row
-  // of the larger of rank / d_model, for all token blocks
-  w.splitk_floats = std::max<size_t>(r, d) * 16 * Mp + 4096;
-  w.splitk = (float*)take(w.splitk_floats * sizeof(float));
   const bool topk = c.sel == FFN_SEL_TOPK_WINA;
   w.wina_s = (float*)take(topk ? M * F * sizeof(float) : 16);
   w.wina_h = (float*)take(topk ? M * F * sizeof(float) : 16);
   w.lb = (uint64_t*)take(M * (F / 16) * sizeof(uint64_t));
-  w.offs = (int32_t*)take((M + 1) * sizeof(int32_t));
-  w.ud_partial = (float*)take((ud_grid_for(cus) + M) * d * sizeof(float));
+  w.ud_rows = ud_rows_for(c, cus);
+  w.ud_partial = (float*)take(w.ud_rows * d * sizeof(float));
   w.hbuf = take(M * F * es);
   w.total = off;
   return w;
@@ -107,11 +112,25 @@ int device_cus() {
 
 }  // namespace
 
+// Optional launch-shape overrides (0 = automatic), read once at init from the
+// environment: FFN_SPARSE_GATE_NT, FFN_SPARSE_GATE_WAVES, FFN_SPARSE_UD_SPLIT,
+// FFN_SPARSE_UD_GROUP, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
+// at decode sizes). They change launch shapes only.
+struct Tuning {
+  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, v_ks = 0, no_gemv = 0;
+};
+
+static int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+
 struct ffn_sparse_handle {
   ffn_sparse_config cfg;
   const void *w_gate, *u, *v, *w_up, *w_down_om, *w_down_nm;
   Workspace ws;
   int cus;
+  Tuning tune;
   // timing
   bool timing = false;
   int cap = 0;
@@ -145,28 +164,80 @@ GemmDesc gemm_base(const ffn_sparse_handle* h) {
   g.dtype = h->cfg.dtype;
   g.nmat = 1;
   g.ks = 1;
-  g.partial = h->ws.splitk;
-  g.tickets = h->ws.ctrl + kCtrlWords;
+  g.b_nsum = 1;
+  g.nwaves = 4;
   g.ctrl = h->ws.ctrl;
   g.bmode = B_NATIVE;
   return g;
 }
 
-// Fills nt / mt / ks for a GEMM of nrows x nmat rows, K, M tokens.
-bool plan(GemmDesc& g, const ffn_sparse_handle* h, int T, int want_wg) {
+// Decode GEMV shape (bf16, M <= 8, K <= 4096): rows per workgroup from
+// 128..4 (dividing the TwELL tile T when T > 0), the largest that still gives
+// `want` workgroups; 16 waves for tiles of 64+ rows, else 4.
+bool plan_gemv(GemmDesc& g, const ffn_sparse_handle* h, int T, int want) {
+  if (g.dtype != FFN_BF16 || g.M > 8 || g.M < 1) return false;
+  const int cands[6] = {128, 64, 32, 16, 8, 4};
+  int best = 0;
+  for (int nt : cands) {
+    if (nt < 2 * g.nmat) continue;
+    const int rpm = nt / g.nmat;
+    if (T > 0 && (T % nt != 0)) continue;
+    if (g.nrows % rpm != 0) continue;
+    best = nt;
+    if ((g.nrows / rpm) >= want) break;
+  }
+  if (h->tune.gate_nt && T > 0 && T % h->tune.gate_nt == 0 && h->tune.gate_nt <= 128) best = h->tune.gate_nt;
+  if (best == 0) return false;
+  GemmDesc t = g;
+  t.gemv = 1;
+  t.nt = best;
+  t.mt = 16;
+  t.ks = 1;
+  t.nwaves = best >= 64 ? 16 : 4;
+  if (T > 0 && (h->tune.gate_waves == 4 || h->tune.gate_waves == 16)) t.nwaves = h->tune.gate_waves;
+  if (!gemv_ok(t)) return false;
+  g = t;
+  return true;
+}
+
+// Tile shape of a GEMM without a TwELL constraint: rows per workgroup from
+// 128/64/32/16 (the largest that still gives >= cus workgroups), 16 waves
+// when there are few workgroups (more bytes in flight per CU), else 4.
+bool plan_plain(GemmDesc& g, const ffn_sparse_handle* h) {
+  if (!h->tune.no_gemv && plan_gemv(g, h, 0, 3 * h->cus / 4)) return true;
+  g.gemv = 0;
   const bool f32 = g.dtype == FFN_F32;
   g.mt = f32 ? 16 : pick_mt(g.M);
   const int mblocks = ceil_div(g.M, g.mt);
-  g.nt = pick_nt(g.nrows, g.nmat, T, mblocks, want_wg, f32);
+  g.nt = pick_nt(g.nrows, g.nmat, 0, mblocks, h->cus, f32);
   if (g.nt == 0) return false;
-  const int tiles = g.nrows * g.nmat / g.nt;
+  const int wgs = g.nrows * g.nmat / g.nt * mblocks;
+  g.nwaves = (!f32 && wgs <= 2 * h->cus) ? 16 : 4;
   g.ks = 1;
-  if (!f32) {
-    const int kch = g.K / 32;
-    while (tiles * mblocks * g.ks < want_wg && g.ks < 16 && kch / (g.ks * 2) >= 4) g.ks *= 2;
-    const size_t need = (size_t)tiles * mblocks * g.ks * g.nt * g.mt;
-    if (need > h->ws.splitk_floats || (size_t)tiles * mblocks > (size_t)kTicketWords) g.ks = 1;
+  return true;
+}
+
+// The gate with the TwELL epilogue: one workgroup per TwELL tile when there
+// are enough tiles (no look-back), else sub-tiles of the TwELL tile.
+bool plan_twell(GemmDesc& g, const ffn_sparse_handle* h) {
+  const auto& c = h->cfg;
+  if (!h->tune.no_gemv && plan_gemv(g, h, c.tile_w, 3 * h->cus / 4)) return true;
+  g.gemv = 0;
+  const bool f32 = g.dtype == FFN_F32;
+  g.mt = f32 ? 16 : pick_mt(g.M);
+  const int mblocks = ceil_div(g.M, g.mt);
+  const int T = c.tile_w;
+  if (!f32 && T <= 128 && (c.d_ff / T) * mblocks * 8 >= 3 * h->cus) {
+    g.nt = T;
+  } else {
+    g.nt = pick_nt(c.d_ff, 1, T, mblocks, h->cus, f32);
   }
+  if (h->tune.gate_nt && T % h->tune.gate_nt == 0 && h->tune.gate_nt <= (f32 ? 64 : 128)) g.nt = h->tune.gate_nt;
+  if (g.nt == 0) return false;
+  const int wgs = c.d_ff / g.nt * mblocks;
+  g.nwaves = (!f32 && wgs <= 2 * h->cus) ? 16 : 4;
+  if (!f32 && (h->tune.gate_waves == 4 || h->tune.gate_waves == 16)) g.nwaves = h->tune.gate_waves;
+  g.ks = 1;
   return true;
 }
 
@@ -198,9 +269,11 @@ EpiDesc epi_base(const ffn_sparse_handle* h, const float* bias, float bias_scala
   return e;
 }
 
-// t = V x for `m` token slots (optionally gathered), fp32 out.
-hipError_t run_lowrank_v(ffn_sparse_handle* h, const void* x, int m, const int32_t* gather,
-                         const int32_t* m_dev, float* t_out, hipStream_t s) {
+// First stage of the low-rank gate, t = V x, for `m` token slots (optionally
+// gathered): ks workgroups split K and each writes an fp32 slab
+// [m x rank] at lr_slabs + slab * max_m * rank. Returns the slab count.
+int run_lowrank_v(ffn_sparse_handle* h, const void* x, int m, const int32_t* gather, const int32_t* m_dev,
+                  hipStream_t s, hipError_t* err) {
   const auto& c = h->cfg;
   GemmDesc g = gemm_base(h);
   g.A0 = h->v;
@@ -212,14 +285,57 @@ hipError_t run_lowrank_v(ffn_sparse_handle* h, const void* x, int m, const int32
   g.M = m;
   g.gather = gather;
   g.m_dev = m_dev;
-  if (!plan(g, h, 0, h->cus)) return hipErrorInvalidValue;
+  if (!plan_plain(g, h)) {
+    *err = hipErrorInvalidValue;
+    return 0;
+  }
+  if (g.gemv) {                                   // decode: no K split needed
+    EpiDesc e{};
+    e.kind = EPI_STORE_F32;
+    e.F = c.rank;
+    e.out = h->ws.lr_slabs;
+    e.ldo = c.rank;
+    e.out_slab = (long long)c.max_m * c.rank;
+    Timed tm(h, FFN_K_LOWRANK_V, s);
+    *err = launch_gemm(g, e, s);
+    return 1;
+  }
+  // rank rows are few, so ks workgroups split K (4 waves each) to bring >= 128
+  // workgroups to the stream; each writes an fp32 slab that the consumer sums
+  // (in order, all slab loads in flight together) when it loads t.
+  int ks = 1;
+  if (c.dtype == FFN_BF16) {
+    g.nwaves = 4;
+    const int wgs = g.nrows / g.nt * ceil_div(m, g.mt);
+    const int kch = g.K / 32;
+    while (wgs * ks < 128 && ks < 8 && kch / (ks * 2 * g.nwaves) >= 4) ks *= 2;
+    if (m > 16) ks = std::min(ks, 2);
+    if (h->tune.v_ks > 0) {
+      int want = h->tune.v_ks;
+      ks = (want >= 8) ? 8 : (want >= 4 ? 4 : (want >= 2 ? 2 : 1));
+      while (ks > 1 && kch / (ks * g.nwaves) < 1) ks /= 2;
+    }
+  }
+  g.ks = ks;
   EpiDesc e{};
   e.kind = EPI_STORE_F32;
   e.F = c.rank;
-  e.out = t_out;
+  e.out = h->ws.lr_slabs;
   e.ldo = c.rank;
+  e.out_slab = (long long)c.max_m * c.rank;
   Timed tm(h, FFN_K_LOWRANK_V, s);
-  return launch_gemm(g, e, s);
+  *err = launch_gemm(g, e, s);
+  return ks;
+}
+
+// Points a GEMM's B operand at the first-stage slabs (summed on load).
+void b_from_slabs(GemmDesc& g, const ffn_sparse_handle* h, int nslabs) {
+  g.B = h->ws.lr_slabs;
+  g.ldb = h->cfg.rank;
+  g.K = h->cfg.rank;
+  g.bmode = h->cfg.dtype == FFN_BF16 ? B_F32_SPLIT : B_NATIVE;
+  g.b_nsum = nslabs;
+  g.b_slab = (long long)h->cfg.max_m * h->cfg.rank;
 }
 
 // Dense hidden h (bf16/fp32 [slots x F] in hbuf) for `m` slots; gathered when
@@ -246,26 +362,23 @@ hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const in
     g.K = c.d_model;
     g.B = x;
     g.ldb = c.d_model;
-    if (!plan(g, h, 0, h->cus)) return hipErrorInvalidValue;
+    if (!plan_plain(g, h)) return hipErrorInvalidValue;
     Timed tm(h, kind, s);
     return launch_gemm(g, e, s);
   }
-  // low-rank gate: t = V x, g = U t (fp32 into g_ext), then the up GEMM
-  float* t = list ? h->ws.lr_t_fb : h->ws.lr_t;
-  hipError_t err = run_lowrank_v(h, x, m, list, m_dev, t, s);
+  // low-rank gate: t = V x (slabs), g = U t (fp32 into g_ext), then the up GEMM
+  hipError_t err = hipSuccess;
+  const int nslabs = run_lowrank_v(h, x, m, list, m_dev, s, &err);
   if (err != hipSuccess) return err;
   {
     GemmDesc gu = gemm_base(h);
     gu.A0 = h->u;
     gu.nrows = c.d_ff;
     gu.lda = c.rank;
-    gu.K = c.rank;
-    gu.B = t;
-    gu.ldb = c.rank;
-    gu.bmode = c.dtype == FFN_BF16 ? B_F32_SPLIT : B_NATIVE;
     gu.M = m;
     gu.m_dev = m_dev;
-    if (!plan(gu, h, 0, h->cus)) return hipErrorInvalidValue;
+    b_from_slabs(gu, h, nslabs);
+    if (!plan_plain(gu, h)) return hipErrorInvalidValue;
     EpiDesc eg{};
     eg.kind = EPI_STORE_F32;
     eg.F = c.d_ff;
@@ -282,7 +395,7 @@ hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const in
   g.B = x;
   g.ldb = c.d_model;
   e.g_ext = h->ws.g_ext;
-  if (!plan(g, h, 0, h->cus)) return hipErrorInvalidValue;
+  if (!plan_plain(g, h)) return hipErrorInvalidValue;
   Timed tm(h, kind, s);
   return launch_gemm(g, e, s);
 }
@@ -300,7 +413,7 @@ hipError_t run_dense_down(ffn_sparse_handle* h, int m, const int32_t* list, cons
   g.ldb = c.d_ff;
   g.M = m;
   g.m_dev = m_dev;
-  if (!plan(g, h, 0, h->cus)) return hipErrorInvalidValue;
+  if (!plan_plain(g, h)) return hipErrorInvalidValue;
   EpiDesc e{};
   e.kind = EPI_Y;
   e.F = c.d_model;
@@ -312,6 +425,96 @@ hipError_t run_dense_down(ffn_sparse_handle* h, int m, const int32_t* list, cons
   return launch_gemm(g, e, s);
 }
 
+RouteDesc route_desc(const ffn_sparse_handle* h, int m, const ffn_twell_pack* p) {
+  RouteDesc r{};
+  r.M = m;
+  r.ntiles = h->cfg.d_ff / h->cfg.tile_w;
+  r.E = h->cfg.ell_w;
+  r.cnt = p->cnt;
+  r.route = p->route;
+  r.dense_list = p->dense_list;
+  r.n_dense = p->n_dense;
+  r.ctrl = h->ws.ctrl;
+  return r;
+}
+
+// Gate pass writing cnt / idx / val (no routing; see run_route / updown).
+ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const float* bias, float bias_scalar,
+                          const float* tau, int k, ffn_twell_pack* pack, float* g_debug, float* s_debug,
+                          hipStream_t s, bool* routed_by_topk) {
+  const auto& c = h->cfg;
+  *routed_by_topk = false;
+  EpiDesc e = epi_base(h, bias, bias_scalar, tau);
+  e.g_debug = g_debug;
+  e.s_debug = s_debug;
+  e.cnt = pack->cnt;
+  e.idx = pack->idx;
+  e.val = pack->val;
+  e.lb = h->ws.lb;
+  GemmDesc g = gemm_base(h);
+  g.M = m;
+  if (c.sel == FFN_SEL_TOPK_WINA) {
+    g.A0 = h->w_gate;
+    g.A1 = h->w_up;
+    g.nmat = 2;
+    g.nrows = c.d_ff;
+    g.lda = c.d_model;
+    g.K = c.d_model;
+    g.B = x;
+    g.ldb = c.d_model;
+    if (!plan_plain(g, h)) return FFN_E_UNSUPPORTED;
+    e.kind = EPI_WINA;
+    e.colnorm = h->ws.colnorm;
+    e.s_buf = h->ws.wina_s;
+    e.h_buf = h->ws.wina_h;
+    hipError_t err;
+    {
+      Timed tm(h, FFN_K_GATE, s);
+      err = launch_gemm(g, e, s);
+    }
+    if (err != hipSuccess) return FFN_E_HIP;
+    TopkDesc td{};
+    td.M = m;
+    td.F = c.d_ff;
+    td.k = k;
+    td.T = c.tile_w;
+    td.dtype = c.dtype;
+    td.s_buf = h->ws.wina_s;
+    td.h_buf = h->ws.wina_h;
+    td.cnt = pack->cnt;
+    td.idx = pack->idx;
+    td.val = pack->val;
+    td.route = pack->route;
+    td.dense_list = pack->dense_list;
+    td.n_dense = pack->n_dense;
+    *routed_by_topk = true;
+    Timed tm(h, FFN_K_TOPK, s);
+    return hip_status(launch_topk(td, s));
+  }
+  if (c.rank > 0) {
+    hipError_t err = hipSuccess;
+    const int nslabs = run_lowrank_v(h, x, m, nullptr, nullptr, s, &err);
+    if (err != hipSuccess) return FFN_E_HIP;
+    g.A0 = h->u;
+    g.lda = c.rank;
+    b_from_slabs(g, h, nslabs);
+    e.t_out = h->ws.lr_t;
+  } else {
+    g.A0 = h->w_gate;
+    g.lda = c.d_model;
+    g.K = c.d_model;
+    g.B = x;
+    g.ldb = c.d_model;
+  }
+  g.nrows = c.d_ff;
+  if (!plan_twell(g, h)) return FFN_E_UNSUPPORTED;
+  e.kind = EPI_TWELL;
+  Timed tm(h, FFN_K_GATE, s);
+  return hip_status(launch_gemm(g, e, s));
+}
+
+// Launch shape of the sparse kernel: (token, group of G tiles, phase s of S)
+// workgroups; at least ~cus workgroups, partial rows bounded by the workspace.
 UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const ffn_twell_pack* p, void* y) {
   const auto& c = h->cfg;
   UpdownDesc u{};
@@ -328,13 +531,46 @@ UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const f
   u.cnt = p->cnt;
   u.idx = p->idx;
   u.val = p->val;
-  u.route = p->route;
-  u.offs = h->ws.offs;
   u.y = y;
   u.partial = h->ws.ud_partial;
-  u.grid = ud_grid_for(h->cus);
-  u.min_chunk = 8;
+  const int ntiles = c.d_ff / c.tile_w;
+  const long long units = (long long)m * ntiles;
+  int G = 1, S = 1;
+  u.nwaves = 8;
+  if (units >= h->cus) {
+    G = (int)std::min<long long>(std::min(ntiles, 64), std::max<long long>(1, units / h->cus));
+    if (units >= 4 * h->cus) u.nwaves = 4;
+  } else if (2 * units <= h->cus) {
+    S = (int)std::min<long long>(4, std::max<long long>(1, h->cus / units));
+  }
+  if (h->tune.ud_group > 0) G = std::min(std::min(ntiles, 64), h->tune.ud_group);
+  if (h->tune.ud_split > 0) S = std::min(16, h->tune.ud_split);
+  auto nparts = [&]() { return (long long)((ntiles + G - 1) / G) * S; };
+  while (nparts() > 1 && (size_t)(m * nparts()) > h->ws.ud_rows) {
+    if (S > 1) S /= 2;
+    else G = std::min(std::min(ntiles, 64), G * 2);
+    if (G == std::min(ntiles, 64) && S == 1) break;
+  }
+  u.tiles_per_group = G;
+  u.slot_split = S;
+  u.w_gate = h->w_gate;
+  u.u_rows = h->u;
+  u.lr_t = h->ws.lr_t;
+  u.rank = c.rank;
+  u.sel = c.sel;
   return u;
+}
+
+ffn_status run_updown(ffn_sparse_handle* h, UpdownDesc& u, hipStream_t s) {
+  hipError_t err;
+  {
+    Timed tm(h, FFN_K_UPDOWN, s);
+    err = launch_updown(u, s);
+  }
+  if (err != hipSuccess) return FFN_E_HIP;
+  if (ud_groups(u) * u.slot_split == 1) return FFN_OK;
+  Timed tm(h, FFN_K_REDUCE, s);
+  return hip_status(launch_updown_reduce(u, s));
 }
 
 }  // namespace
@@ -372,7 +608,6 @@ ffn_status ffn_sparse_check_config(const ffn_sparse_config* c) {
   if (c->sel == FFN_SEL_TOPK_WINA && (c->ell_w != c->tile_w || c->d_ff > 32768 || c->rank != 0))
     return FFN_E_UNSUPPORTED;
   if (c->d_ff / c->tile_w > 1024) return FFN_E_UNSUPPORTED;
-  if (c->dtype == FFN_F32 && c->tile_w % 32 != 0 && c->tile_w != 16) return FFN_E_UNSUPPORTED;
   return FFN_OK;
 }
 
@@ -408,6 +643,12 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->cfg = *cfg;
   h->ws = ws;
   h->cus = cus;
+  h->tune.gate_nt = env_int("FFN_SPARSE_GATE_NT");
+  h->tune.gate_waves = env_int("FFN_SPARSE_GATE_WAVES");
+  h->tune.ud_split = env_int("FFN_SPARSE_UD_SPLIT");
+  h->tune.ud_group = env_int("FFN_SPARSE_UD_GROUP");
+  h->tune.v_ks = env_int("FFN_SPARSE_V_KS");
+  h->tune.no_gemv = env_int("FFN_SPARSE_NO_GEMV");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;
@@ -447,87 +688,14 @@ ffn_status ffn_sparse_gate_pack(ffn_sparse_handle* h, const void* x, int32_t m, 
   ffn_status st = check_call(h, x, m, tau, k);
   if (st != FFN_OK) return st;
   if (!pack_ok(pack)) return FFN_E_INVALID;
-  const auto& c = h->cfg;
-  if (s_debug && c.sel != FFN_SEL_TOPK_WINA) return FFN_E_INVALID;
+  if (s_debug && h->cfg.sel != FFN_SEL_TOPK_WINA) return FFN_E_INVALID;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (m == 0) {
-    hipError_t e1 = launch_fill_u32(reinterpret_cast<uint32_t*>(pack->n_dense), 0u, 1, s);
-    hipError_t e2 = launch_fill_u32(reinterpret_cast<uint32_t*>(h->ws.offs), 0u, 1, s);
-    return hip_status(e1 != hipSuccess ? e1 : e2);
-  }
-  EpiDesc e = epi_base(h, bias, bias_scalar, tau);
-  e.g_debug = g_debug;
-  e.s_debug = s_debug;
-  e.cnt = pack->cnt;
-  e.idx = pack->idx;
-  e.val = pack->val;
-  e.route = pack->route;
-  e.dense_list = pack->dense_list;
-  e.n_dense = pack->n_dense;
-  e.offs = h->ws.offs;
-  e.lb = h->ws.lb;
-  GemmDesc g = gemm_base(h);
-  g.M = m;
-  hipError_t err = hipSuccess;
-  if (c.sel == FFN_SEL_TOPK_WINA) {
-    g.A0 = h->w_gate;
-    g.A1 = h->w_up;
-    g.nmat = 2;
-    g.nrows = c.d_ff;
-    g.lda = c.d_model;
-    g.K = c.d_model;
-    g.B = x;
-    g.ldb = c.d_model;
-    if (!plan(g, h, 0, h->cus)) return FFN_E_UNSUPPORTED;
-    e.kind = EPI_WINA;
-    e.colnorm = h->ws.colnorm;
-    e.s_buf = h->ws.wina_s;
-    e.h_buf = h->ws.wina_h;
-    {
-      Timed tm(h, FFN_K_GATE, s);
-      err = launch_gemm(g, e, s);
-    }
-    if (err != hipSuccess) return FFN_E_HIP;
-    TopkDesc td{};
-    td.M = m;
-    td.F = c.d_ff;
-    td.k = k;
-    td.T = c.tile_w;
-    td.dtype = c.dtype;
-    td.s_buf = h->ws.wina_s;
-    td.h_buf = h->ws.wina_h;
-    td.cnt = pack->cnt;
-    td.idx = pack->idx;
-    td.val = pack->val;
-    td.route = pack->route;
-    td.dense_list = pack->dense_list;
-    td.n_dense = pack->n_dense;
-    td.offs = h->ws.offs;
-    td.ctrl = h->ws.ctrl;
-    Timed tm(h, FFN_K_TOPK, s);
-    return hip_status(launch_topk(td, s));
-  }
-  if (c.rank > 0) {
-    err = run_lowrank_v(h, x, m, nullptr, nullptr, h->ws.lr_t, s);
-    if (err != hipSuccess) return FFN_E_HIP;
-    g.A0 = h->u;
-    g.lda = c.rank;
-    g.K = c.rank;
-    g.B = h->ws.lr_t;
-    g.ldb = c.rank;
-    g.bmode = c.dtype == FFN_BF16 ? B_F32_SPLIT : B_NATIVE;
-  } else {
-    g.A0 = h->w_gate;
-    g.lda = c.d_model;
-    g.K = c.d_model;
-    g.B = x;
-    g.ldb = c.d_model;
-  }
-  g.nrows = c.d_ff;
-  if (!plan(g, h, c.tile_w, h->cus)) return FFN_E_UNSUPPORTED;
-  e.kind = EPI_TWELL;
-  Timed tm(h, FFN_K_GATE, s);
-  return hip_status(launch_gemm(g, e, s));
+  if (m == 0) return hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pack->n_dense), 0u, 1, s));
+  bool routed_by_topk = false;
+  st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, g_debug, s_debug, s, &routed_by_topk);
+  if (st != FFN_OK || routed_by_topk) return st;
+  Timed tm(h, FFN_K_ROUTE, s);
+  return hip_status(launch_route(route_desc(h, m, pack), s));
 }
 
 ffn_status ffn_sparse_updown(ffn_sparse_handle* h, const void* x, int32_t m, const ffn_twell_pack* pack,
@@ -538,14 +706,7 @@ ffn_status ffn_sparse_updown(ffn_sparse_handle* h, const void* x, int32_t m, con
   if (m == 0) return FFN_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   UpdownDesc u = updown_desc(h, x, m, pack, y);
-  hipError_t err;
-  {
-    Timed tm(h, FFN_K_UPDOWN, s);
-    err = launch_updown(u, s);
-  }
-  if (err != hipSuccess) return FFN_E_HIP;
-  Timed tm(h, FFN_K_REDUCE, s);
-  return hip_status(launch_updown_reduce(u, s));
+  return run_updown(h, u, s);
 }
 
 ffn_status ffn_sparse_dense_fallback(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
@@ -567,11 +728,30 @@ ffn_status ffn_sparse_dense_fallback(ffn_sparse_handle* h, const void* x, int32_
 ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
                               float bias_scalar, const float* tau, int32_t k, ffn_twell_pack* pack,
                               void* y, void* stream) {
-  ffn_status st = ffn_sparse_gate_pack(h, x, m, bias, bias_scalar, tau, k, pack, nullptr, nullptr, stream);
+  ffn_status st = check_call(h, x, m, tau, k);
   if (st != FFN_OK) return st;
-  st = ffn_sparse_updown(h, x, m, pack, y, stream);
+  if (!pack_ok(pack) || (m > 0 && (!y || !aligned16(y)))) return FFN_E_INVALID;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (m == 0) return hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pack->n_dense), 0u, 1, s));
+  bool routed_by_topk = false;
+  st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, nullptr, nullptr, s, &routed_by_topk);
   if (st != FFN_OK) return st;
-  return ffn_sparse_dense_fallback(h, x, m, bias, bias_scalar, tau, k, pack, y, stream);
+  const auto& c = h->cfg;
+  const bool can_route = c.sel != FFN_SEL_TOPK_WINA && c.ell_w < c.tile_w;
+  const bool decode = m <= kDecodeMaxM;
+  UpdownDesc u = updown_desc(h, x, m, pack, y);
+  u.route_pass = routed_by_topk ? 0 : 1;          // block 0 routes the pack (top-k already did)
+  u.route = route_desc(h, m, pack);
+  u.include_routed = decode ? 1 : 0;
+  u.bias = bias;
+  u.bias_scalar = bias_scalar;
+  u.tau = tau;
+  st = run_updown(h, u, s);
+  if (st != FFN_OK || decode || !can_route) return st;
+  hipError_t err = run_dense_hidden(h, x, m, pack->dense_list, pack->n_dense, bias, bias_scalar, tau,
+                                    FFN_K_FALLBACK, s);
+  if (err != hipSuccess) return FFN_E_HIP;
+  return hip_status(run_dense_down(h, m, pack->dense_list, pack->n_dense, y, FFN_K_FALLBACK, s));
 }
 
 ffn_status ffn_sparse_dense_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,

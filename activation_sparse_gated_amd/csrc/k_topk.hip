@@ -101,11 +101,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   // routing: with E == T no tile can overflow; every token holds exactly k entries
   if (tid == 0) {
     d.route[tok] = 0;
-    d.offs[tok] = tok * k;
-    if (tok == 0) {
-      *d.n_dense = 0;
-      d.offs[d.M] = d.M * k;
-    }
+    if (tok == 0) *d.n_dense = 0;
   }
 }
 

@@ -24,15 +24,17 @@ struct GemmDesc {
   const void* B;          // token rows
   int ldb;                // elements
   int bmode;              // B_NATIVE or B_F32_SPLIT (fp32 B split into bf16 hi + lo)
+  int b_nsum;             // B is the sum of b_nsum fp32 slabs (B_F32_SPLIT / fp32), >= 1
+  long long b_slab;       // elements between consecutive B slabs
   int M;                  // token count bound known on the host
   const int32_t* gather;  // B row of token slot m is gather[m]; null = m
   const int32_t* m_dev;   // device-side token count (dense backup); null = M
   int nt;                 // rows per workgroup tile (16, 32, 64, 128; per matrix * nmat)
   int mt;                 // tokens per workgroup (16, 32 or 64)
-  int ks;                 // workgroups splitting K (>= 1)
-  float* partial;         // split-K partial tiles (ks > 1)
-  uint32_t* tickets;      // split-K tickets, one per (tile, token block), zero on entry
-  uint32_t* ctrl;         // control block
+  int nwaves;             // waves per workgroup (4 or 16)
+  int gemv;               // decode GEMV (VALU) instead of MFMA tiles (bf16, M <= 8)
+  int ks;                 // workgroups splitting K; each writes its own output slab (>= 1)
+  const uint32_t* ctrl;   // control block (epoch of the look-back words)
 };
 
 struct EpiDesc {
@@ -46,14 +48,13 @@ struct EpiDesc {
   int sel, act;
   float* g_debug;         // [tokens x F] gate before bias
   float* s_debug;         // [tokens x F] WINA scores
-  // EPI_STORE_F32
-  float* out; int ldo;
+  // EPI_STORE_F32: out + ksi * out_slab + m * ldo + n
+  float* out; int ldo; long long out_slab;
+  float* t_out;           // EPI_TWELL on the low-rank gate: tile 0 stores the summed t here
   // EPI_TWELL
   int T, E;
   int32_t* cnt; uint16_t* idx; void* val;
-  uint8_t* route; int32_t* dense_list; int32_t* n_dense;
-  int32_t* offs;          // [M + 1] entry prefix of non-routed tokens (sparse schedule)
-  uint64_t* lb;           // look-back words [M x F / nt]
+  uint64_t* lb;           // look-back words [M x F / nt] (sub-tiled TwELL tiles)
   // EPI_WINA
   const float* colnorm; float* s_buf; float* h_buf;
   // EPI_DENSE_H
@@ -74,24 +75,43 @@ struct TopkDesc {
   int M, F, k, T, dtype;
   const float* s_buf; const float* h_buf;
   int32_t* cnt; uint16_t* idx; void* val;
-  uint8_t* route; int32_t* dense_list; int32_t* n_dense; int32_t* offs;
-  uint32_t* ctrl;
+  uint8_t* route; int32_t* dense_list; int32_t* n_dense;
 };
 hipError_t launch_topk(const TopkDesc& d, hipStream_t s);
+
+// Routing of a TwELL pack: route_t = any tile with cnt > E, dense_list = the
+// routed ids ascending, n_dense; also advances the look-back epoch.
+struct RouteDesc {
+  int M, ntiles, E;
+  const int32_t* cnt;
+  uint8_t* route; int32_t* dense_list; int32_t* n_dense;
+  uint32_t* ctrl;
+};
+hipError_t launch_route(const RouteDesc& r, hipStream_t s);
 
 struct UpdownDesc {
   int dtype, M, d, F, T, E;
   int down_only;          // TOPK: pack values are h, no up product
   const void* x; const void* w_up; const void* w_down_nm;
-  const int32_t* cnt; const uint16_t* idx; const void* val; const uint8_t* route;
-  const int32_t* offs;    // [M + 1]
+  const int32_t* cnt; const uint16_t* idx; const void* val;
   void* y;
-  float* partial;         // [(grid + M) x d]
-  int grid;               // workgroups of the sparse kernel
-  int min_chunk;          // minimum entries per workgroup
+  float* partial;         // [M x ngroups x slot_split x d]
+  int tiles_per_group;    // G: tiles handled by one workgroup
+  int slot_split;         // S: workgroups sharing one tile group (entry phase)
+  int nwaves;             // waves per workgroup (4 or 8)
+  int route_pass;         // block 0 also routes the pack (route / dense_list / n_dense, epoch)
+  RouteDesc route;
+  int include_routed;     // evaluate routed tokens here: overflowing tiles densely
+  // gate recompute for routed tokens
+  const void* w_gate;     // full gate rows [F x d], or null for the low-rank gate
+  const void* u_rows;     // low-rank U [F x rank]
+  const float* lr_t;      // low-rank intermediate t [M x rank] (fp32)
+  int rank;
+  const float* bias; float bias_scalar; const float* tau; int sel;
 };
-// Fused sparse up + down over the pack, then the cross-workgroup sum of
-// partial rows (two launches, timed separately by the caller).
+__host__ __device__ inline int ud_groups(const UpdownDesc& u) { return (u.F / u.T + u.tiles_per_group - 1) / u.tiles_per_group; }
+// Fused sparse up + down over the pack; then the ordered sum of the partial
+// rows (skipped by the caller when every token fits one workgroup).
 hipError_t launch_updown(const UpdownDesc& u, hipStream_t s);
 hipError_t launch_updown_reduce(const UpdownDesc& u, hipStream_t s);
 

@@ -165,7 +165,11 @@ ffn_status ffn_sparse_dense_fallback(ffn_sparse_handle *h, const void *x, int32_
                                      int32_t k, const ffn_twell_pack *pack, void *y,
                                      void *stream);
 
-/* gate_pack + updown + dense_fallback: the whole sparse forward pass. */
+/* gate_pack + updown + dense_fallback: the whole sparse forward pass; writes
+ * every y row and the complete pack. For m <= 64 the routed tokens are
+ * evaluated by the sparse kernel itself (each overflowing tile densely, gate
+ * recomputed); for larger m they go through the dense backup on matrix cores.
+ * Routing is done inside the sparse kernel (no separate pass). */
 ffn_status ffn_sparse_forward(ffn_sparse_handle *h, const void *x, int32_t m,
                               const float *bias, float bias_scalar, const float *tau,
                               int32_t k, ffn_twell_pack *pack, void *y, void *stream);
@@ -183,14 +187,15 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t
  * and returns, for kernel kind `kind` (see ffn_kernel_kind), the number of
  * launches and their total milliseconds, then clears that kind. */
 typedef enum {
-  FFN_K_GATE = 0,      /* gate GEMM + selection epilogue (+ TwELL, routing)    */
+  FFN_K_GATE = 0,      /* gate GEMM + selection epilogue (+ TwELL pack)        */
   FFN_K_LOWRANK_V = 1, /* low-rank gate first stage t = V x                    */
   FFN_K_TOPK = 2,      /* WINA top-k selection + pack                          */
   FFN_K_UPDOWN = 3,    /* fused sparse up + down                               */
   FFN_K_REDUCE = 4,    /* cross-workgroup sum of partial y rows                */
   FFN_K_FALLBACK = 5,  /* dense backup kernels                                 */
   FFN_K_DENSE = 6,     /* dense baseline kernels                               */
-  FFN_K_COUNT = 7
+  FFN_K_ROUTE = 7,     /* routing pass of a standalone gate_pack               */
+  FFN_K_COUNT = 8
 } ffn_kernel_kind;
 ffn_status ffn_sparse_timing_enable(ffn_sparse_handle *h, int32_t enable, int32_t capacity);
 ffn_status ffn_sparse_timing_read(ffn_sparse_handle *h, int32_t kind, int32_t *launches,

@@ -42,10 +42,15 @@ def run_full(wl, ref, *, E=None, check_band=True):
     ffn.dense_fallback(x, pack, y, **kw)
     torch.cuda.synchronize()
     worst = check_y(y_to_f64(wl, y)[: wl.m], ref["y"])
-    # the one-call forward gives the same bits
+    # the one-call forward: same pack; non-routed rows bit-identical (same
+    # kernel); routed rows come from the in-kernel dense evaluation at decode
+    # sizes (a different but equally exact path), checked against the oracle
     y2, pack2 = ffn.forward(x, **kw)
     torch.cuda.synchronize()
-    assert np.array_equal(host(y2)[: wl.m], host(y)[: wl.m])
+    check_pack(wl, pack2, ref, E=E)
+    keep = ref["route"][: wl.m] == 0
+    assert np.array_equal(host(y2)[: wl.m][keep], host(y)[: wl.m][keep])
+    check_y(y_to_f64(wl, y2)[: wl.m], ref["y"])
     if (wl.E if E is None else E) > 0:
         assert np.array_equal(host(pack2.idx)[: wl.m], host(pack.idx)[: wl.m])
     return worst
