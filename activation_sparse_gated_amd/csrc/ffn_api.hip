@@ -70,7 +70,9 @@ constexpr int kMaxSlabs = 8;
 // token at the coarsest grouping (64 tiles per workgroup).
 size_t ud_rows_for(const ffn_sparse_config& c, int cus) {
   const size_t ntiles = c.d_ff / c.tile_w;
-  return std::max<size_t>((size_t)4 * cus, (size_t)c.max_m * ((ntiles + 63) / 64));
+  const size_t per_tile = std::max(1, std::max(c.ell_w, c.tile_w));
+  const size_t gmin = std::max<size_t>(1, std::min<size_t>(std::min<size_t>(ntiles, 64), kUpdownCap / per_tile));
+  return std::max<size_t>((size_t)4 * cus, (size_t)c.max_m * ((ntiles + gmin - 1) / gmin));
 }
 
 // Carves the workspace (base may be null to only compute the size).
@@ -114,10 +116,10 @@ int device_cus() {
 
 // Optional launch-shape overrides (0 = automatic), read once at init from the
 // environment: FFN_SPARSE_GATE_NT, FFN_SPARSE_GATE_WAVES, FFN_SPARSE_UD_SPLIT,
-// FFN_SPARSE_UD_GROUP, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
+// FFN_SPARSE_UD_GROUP, FFN_SPARSE_UD_WAVES, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
 // at decode sizes). They change launch shapes only.
 struct Tuning {
-  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, v_ks = 0, no_gemv = 0;
+  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0;
 };
 
 static int env_int(const char* name) {
@@ -514,8 +516,11 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
 }
 
 // Launch shape of the sparse kernel: (token, group of G tiles, phase s of S)
-// workgroups; at least ~cus workgroups, partial rows bounded by the workspace.
-UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const ffn_twell_pack* p, void* y) {
+// workgroups of 8 waves; about two workgroups per CU at most, G bounded by the
+// entries a workgroup holds in LDS (a routed token evaluated here can bring T
+// entries per tile), partial rows bounded by the workspace.
+UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const ffn_twell_pack* p, void* y,
+                       bool include_routed) {
   const auto& c = h->cfg;
   UpdownDesc u{};
   u.dtype = c.dtype;
@@ -533,23 +538,22 @@ UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const f
   u.val = p->val;
   u.y = y;
   u.partial = h->ws.ud_partial;
+  u.include_routed = include_routed ? 1 : 0;
   const int ntiles = c.d_ff / c.tile_w;
+  const int per_tile = std::max(1, include_routed ? std::max(c.ell_w, c.tile_w) : c.ell_w);
+  const int gcap = std::max(1, std::min(std::min(ntiles, 64), kUpdownCap / per_tile));
   const long long units = (long long)m * ntiles;
   int G = 1, S = 1;
-  u.nwaves = 8;
-  if (units >= h->cus) {
-    G = (int)std::min<long long>(std::min(ntiles, 64), std::max<long long>(1, units / h->cus));
-    if (units >= 4 * h->cus) u.nwaves = 4;
-  } else if (2 * units <= h->cus) {
-    S = (int)std::min<long long>(4, std::max<long long>(1, h->cus / units));
-  }
-  if (h->tune.ud_group > 0) G = std::min(std::min(ntiles, 64), h->tune.ud_group);
+  if (units > 2LL * h->cus) G = (int)std::min<long long>(gcap, units / (2LL * h->cus));
+  if (h->tune.ud_group > 0) G = std::min(gcap, h->tune.ud_group);
   if (h->tune.ud_split > 0) S = std::min(16, h->tune.ud_split);
+  const int epc = c.dtype == FFN_BF16 ? 8 : 4;
+  u.nwaves = (h->tune.ud_waves == 4 && c.d_model / epc <= 4 * 64) ? 4 : 8;
   auto nparts = [&]() { return (long long)((ntiles + G - 1) / G) * S; };
   while (nparts() > 1 && (size_t)(m * nparts()) > h->ws.ud_rows) {
     if (S > 1) S /= 2;
-    else G = std::min(std::min(ntiles, 64), G * 2);
-    if (G == std::min(ntiles, 64) && S == 1) break;
+    else if (G < gcap) G = std::min(gcap, G * 2);
+    else break;
   }
   u.tiles_per_group = G;
   u.slot_split = S;
@@ -562,6 +566,8 @@ UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const f
 }
 
 ffn_status run_updown(ffn_sparse_handle* h, UpdownDesc& u, hipStream_t s) {
+  const long long nparts = (long long)ud_groups(u) * u.slot_split;
+  if (nparts > 1 && (size_t)(u.M * nparts) > h->ws.ud_rows) return FFN_E_UNSUPPORTED;
   hipError_t err;
   {
     Timed tm(h, FFN_K_UPDOWN, s);
@@ -649,6 +655,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.ud_group = env_int("FFN_SPARSE_UD_GROUP");
   h->tune.v_ks = env_int("FFN_SPARSE_V_KS");
   h->tune.no_gemv = env_int("FFN_SPARSE_NO_GEMV");
+  h->tune.ud_waves = env_int("FFN_SPARSE_UD_WAVES");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;
@@ -705,7 +712,7 @@ ffn_status ffn_sparse_updown(ffn_sparse_handle* h, const void* x, int32_t m, con
   if (!pack_ok(pack) || (m > 0 && (!y || !aligned16(y)))) return FFN_E_INVALID;
   if (m == 0) return FFN_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  UpdownDesc u = updown_desc(h, x, m, pack, y);
+  UpdownDesc u = updown_desc(h, x, m, pack, y, false);
   return run_updown(h, u, s);
 }
 
@@ -739,10 +746,9 @@ ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, co
   const auto& c = h->cfg;
   const bool can_route = c.sel != FFN_SEL_TOPK_WINA && c.ell_w < c.tile_w;
   const bool decode = m <= kDecodeMaxM;
-  UpdownDesc u = updown_desc(h, x, m, pack, y);
+  UpdownDesc u = updown_desc(h, x, m, pack, y, decode && can_route);
   u.route_pass = routed_by_topk ? 0 : 1;          // block 0 routes the pack (top-k already did)
   u.route = route_desc(h, m, pack);
-  u.include_routed = decode ? 1 : 0;
   u.bias = bias;
   u.bias_scalar = bias_scalar;
   u.tau = tau;

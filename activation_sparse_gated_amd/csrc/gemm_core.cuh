@@ -64,10 +64,13 @@ __device__ __forceinline__ void epi_store_f32(const EpiDesc& e, const TileView& 
 // TwELL emission: one wave per token slot; the tile covers nt neurons
 // [n0, n0 + nt), sub-tile q of TwELL tile j (Q = T / nt). Active neurons are
 // compacted in ascending order with a ballot + prefix popcount.
-__device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, uint32_t epoch) {
+__device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, const uint32_t* ctrl) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int Q = e.T / v.nt, q = (v.n0 % e.T) / v.nt, j = v.n0 / e.T;
   const int ntiles = e.F / e.T, nsub = e.F / v.nt;
+  // pass epoch of the look-back words (advanced by the routing pass after
+  // every gate pass); only sub-tiled TwELL tiles need it
+  const uint32_t epoch = Q > 1 ? __hip_atomic_load(&ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
   for (int m = wave; m < v.mcnt; m += nw) {
     const int tok = v.m0 + m;
     const float b = bias_of(e, tok), cut = cut_of(e, tok);
@@ -168,12 +171,12 @@ __device__ __forceinline__ void epi_y(const EpiDesc& e, const TileView& v) {
 }
 
 template <int NMAT, int EPI>
-__device__ __forceinline__ void run_epilogue(const EpiDesc& e, const TileView& v, uint32_t epoch, int ksi) {
+__device__ __forceinline__ void run_epilogue(const EpiDesc& e, const TileView& v, const uint32_t* ctrl, int ksi) {
   if (EPI == EPI_STORE_F32) epi_store_f32(e, v, ksi);
   if (EPI == EPI_WINA) epi_wina(e, v);
   if (EPI == EPI_DENSE_H) epi_dense_h<NMAT>(e, v);
   if (EPI == EPI_Y) epi_y(e, v);
-  if (EPI == EPI_TWELL) epi_twell(e, v, epoch);
+  if (EPI == EPI_TWELL) epi_twell(e, v, ctrl);
 }
 
 // Low-rank gate: the workgroups of weight tile 0 also store the summed
@@ -210,7 +213,6 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_bf16(const GemmDesc g, co
   constexpr int NT = 16 * RB * WN, MT = 16 * MB, LDT = MT + 1, RPM = NT / NMAT;
   constexpr int U = UnrollOf<RB, MB, BM>::value;
   __shared__ float tile[NT * LDT];
-  __shared__ uint32_t s_epoch;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave % WN, wk = wave / WN;
   const int tile_id = blockIdx.x / g.ks, ksi = blockIdx.x % g.ks;
@@ -220,7 +222,6 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_bf16(const GemmDesc g, co
   if (m0 >= Mtot) return;
   const int mcnt = min(MT, Mtot - m0);
   const int n0 = tile_id * RPM;
-  if (EPI == EPI_TWELL && threadIdx.x == 0) s_epoch = __hip_atomic_load(&g.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
   const int kct = g.K >> 5;
   const int per_ks = (kct + g.ks - 1) / g.ks;
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_bf16(const GemmDesc g, co
   }
   if (EPI == EPI_TWELL && BM == B_F32_SPLIT && e.t_out && tile_id == 0) store_summed_t(g, e, m0, mcnt);
   const TileView v{tile, LDT, NT, n0, m0, mcnt, RPM};
-  run_epilogue<NMAT, EPI>(e, v, s_epoch, ksi);
+  run_epilogue<NMAT, EPI>(e, v, g.ctrl, ksi);
 }
 
 // ------------------------------------------------------------------ decode GEMV (VALU)
@@ -361,7 +362,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_bf16(const GemmDesc g, const E
   constexpr int BW = BF32 ? 2 : 1;                // uint4 per token per piece
   constexpr int RPG = 8 / NKC;                    // rows per group of 8 pieces
   __shared__ float tile[128 * LDT];
-  __shared__ uint32_t s_epoch;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int NT = g.nt, RPM = NT / NMAT;
   const int tile_id = blockIdx.x;
@@ -371,7 +371,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_bf16(const GemmDesc g, const E
   if (m0 >= Mtot) return;
   const int mcnt = min(MAXM, Mtot - m0);
   const int n0 = tile_id * RPM;
-  if (EPI == EPI_TWELL && threadIdx.x == 0) s_epoch = __hip_atomic_load(&g.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   const int nkc = (g.K + 511) / 512;              // pieces per row (<= NKC); the last may be partial
   // does this lane's 8-element slice of piece c exist?
   auto lane_in = [&](int c) { return c < nkc && c * 512 + lane * 8 < g.K; };
@@ -447,7 +446,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_bf16(const GemmDesc g, const E
   __syncthreads();
   if (EPI == EPI_TWELL && BF32 && e.t_out && tile_id == 0) store_summed_t(g, e, m0, mcnt);
   const TileView v{tile, LDT, NT, n0, m0, mcnt, RPM};
-  run_epilogue<NMAT, EPI>(e, v, s_epoch, 0);
+  run_epilogue<NMAT, EPI>(e, v, g.ctrl, 0);
 }
 
 // registers held for the tokens' inputs: NKC * MAXM * BW uint4 (<= 32)
@@ -507,7 +506,6 @@ template <int NT, int NMAT, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(const GemmDesc g, const EpiDesc e) {
   constexpr int MT = 16, LDT = MT + 1, RPM = NT / NMAT;
   __shared__ float tile[NT * LDT];
-  __shared__ uint32_t s_epoch;
   const int tile_id = blockIdx.x / g.ks, ksi = blockIdx.x % g.ks;
   const int m0 = blockIdx.y * MT;
   int Mtot = g.M;
@@ -515,7 +513,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const GemmDesc g, const EpiDes
   if (m0 >= Mtot) return;
   const int mcnt = min(MT, Mtot - m0);
   const int n0 = tile_id * RPM;
-  if (EPI == EPI_TWELL && threadIdx.x == 0) s_epoch = __hip_atomic_load(&g.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   const int kct = g.K / 4;
   const int per_ks = (kct + g.ks - 1) / g.ks;
   const int k0 = min(kct, ksi * per_ks) * 4, k1 = min(kct, ksi * per_ks + per_ks) * 4;
@@ -543,7 +540,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const GemmDesc g, const EpiDes
   __syncthreads();
   if (EPI == EPI_TWELL && e.t_out && tile_id == 0) store_summed_t(g, e, m0, mcnt);
   const TileView v{tile, LDT, NT, n0, m0, mcnt, RPM};
-  run_epilogue<NMAT, EPI>(e, v, s_epoch, ksi);
+  run_epilogue<NMAT, EPI>(e, v, g.ctrl, ksi);
 }
 
 // ------------------------------------------------------------------ dispatch helpers

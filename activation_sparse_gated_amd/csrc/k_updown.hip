@@ -28,7 +28,6 @@
 
 namespace ffn {
 
-constexpr int UD_WAVES = 4;
 
 template <int DT>
 struct ElemTraits;
@@ -134,190 +133,236 @@ __device__ __forceinline__ float gate_recompute(const UpdownDesc& u, int t, int 
   return wave_sum(s);
 }
 
-// Preloaded pack slots per workgroup (idx + value), when the group is small.
-constexpr int UD_PRELOAD = 2048;
+// Entries (and preloaded pack slots) one workgroup holds in LDS.
+constexpr int UD_CAP = kUpdownCap;
+// phase-B rows in flight per wave
+constexpr int UD_BATCH = 16;
 
-template <int CPL, int DT, int NW>
+// Two phases inside one workgroup (h stays on chip):
+//   A  every wave takes entries round-robin: u_i = <W_up[i, :], x_t> over the
+//      full row, h_i = a_i u_i into LDS (top-k packs already hold h_i);
+//   B  every wave owns a slice of d and accumulates sum_i h_i W_down[i, slice]
+//      over all entries of the workgroup. Its first batch of down-row loads
+//      does not depend on h, so it is issued before the barrier and overlaps A.
+// The workgroup's y contribution leaves as one partial row (no cross-wave
+// reduction: the slices are disjoint).
+template <int DT, int NW>
 __global__ __launch_bounds__(64 * NW) void k_updown(const UpdownDesc u) {
   using TR = ElemTraits<DT>;
   constexpr int EPC = TR::EPC;
-  constexpr int VPL = CPL * EPC;                  // values per lane
-  constexpr int HALF = NW > 4 ? NW / 2 : NW;      // waves whose partial rows live in LDS
-  __shared__ float s_y[HALF][CPL * 64 * EPC];
-  __shared__ uint4 s_x[CPL * 64];                 // x_t in its storage type, 16-byte chunks
-  __shared__ int s_lim[64];                       // entries per tile of the group
-  __shared__ uint16_t s_idx[UD_PRELOAD];
-  __shared__ float s_val[UD_PRELOAD];
+  constexpr int CPL = 8;                          // row chunks per lane in phase A (d / EPC <= 512)
+  __shared__ uint4 s_x[512];                      // x_t in its storage type, 16-byte chunks
+  __shared__ int s_pre[65];                       // entry prefix over the group's tiles
+  __shared__ uint8_t s_dense[64];                 // tile overflows: evaluated densely
+  __shared__ uint16_t s_idx[UD_CAP];
+  __shared__ float s_val[UD_CAP];                 // packed value; then a_i of entry i
+  __shared__ int s_nrn[UD_CAP];                   // neuron of entry i (negative: dense candidate)
+  __shared__ float s_h[UD_CAP];
   const int d = u.d, T = u.T, E = u.E;
   const int ntiles = u.F / T, nch = d / EPC;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = u.tiles_per_group, S = u.slot_split, ngroups = ud_groups(u);
+  // the last workgroup (when asked for) only routes the pack, alongside the others
+  if (u.route_pass && blockIdx.x == gridDim.x - 1) {
+    route_pass(u.route);
+    return;
+  }
   int bid = blockIdx.x;
   const int s = bid % S;
   bid /= S;
   const int g = bid % ngroups, t = bid / ngroups;
-  if (u.route_pass && blockIdx.x == 0) route_pass(u.route);
 
-  // one round of independent loads: the token's tile counts (routing test),
-  // x_t, and this group's pack slots
+  // ---- one round of independent loads: tile counts, x_t, the group's slots
   const int j0 = g * G, j1 = min(j0 + G, ntiles), ng = j1 - j0;
   const int32_t* crow = u.cnt + (size_t)t * ntiles;
   int over = 0;
   for (int j = threadIdx.x; j < ntiles; j += blockDim.x) over |= crow[j] > E;
   for (int c = threadIdx.x; c < nch; c += blockDim.x)
     s_x[c] = ldg16((const char*)u.x + ((size_t)t * d + (size_t)c * EPC) * TR::ES);
-  const bool preload = ng * E <= UD_PRELOAD;
-  if (preload) {
+  {
     const size_t slot0 = ((size_t)t * ntiles + j0) * E;
-    for (int q = threadIdx.x; q < ng * E; q += blockDim.x) {
+    for (int q = threadIdx.x; q < ng * E && q < UD_CAP; q += blockDim.x) {
       s_idx[q] = u.idx[slot0 + q];
       s_val[q] = TR::scalar(u.val, slot0 + q);
     }
   }
-  for (int jj = threadIdx.x; jj < ng; jj += blockDim.x) {
-    const int c = crow[j0 + jj];
-    s_lim[jj] = c > E ? T : c;                    // an overflowing tile is evaluated densely
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int jj = 0; jj < ng; ++jj) {
+      s_pre[jj] = acc;
+      const int c = crow[j0 + jj];
+      s_dense[jj] = c > E ? 1 : 0;
+      acc += c > E ? T : c;                      // an overflowing tile is evaluated densely
+    }
+    s_pre[ng] = min(acc, UD_CAP);
   }
   const bool routed = __syncthreads_or(over) != 0;
   if (routed && !u.include_routed) return;
+  const int n_all = s_pre[ng];
+  // this workgroup's entries: every S-th starting at s
+  const int n = n_all > s ? (n_all - s + S - 1) / S : 0;
 
-  // selection inputs are read only for a routed token evaluated here (the
-  // standalone sparse pass passes no bias / threshold pointers)
-  float b = 0.f, cut = 0.f;
+  float b = 0.f, cut = 0.f;                       // selection inputs: routed tokens only
   if (routed) {
     b = u.bias ? u.bias[t] : u.bias_scalar;
     cut = (u.sel == SEL_THRESH && u.tau) ? fmaxf(u.tau[t], 0.f) : 0.f;
   }
-  float ya[VPL];
-#pragma unroll
-  for (int q = 0; q < VPL; ++q) ya[q] = 0.f;
-
-  // this wave's candidates: slots k = s + S*wave + S*NW*i of every tile of the
-  // group, valid while k < s_lim (ascending tile, then slot)
-  const int kfirst = s + S * wave, kstep = S * NW;
-  int cj = 0, ck = kfirst;
-  auto next = [&](int& j, int& k) -> bool {
-    while (cj < ng && ck >= s_lim[cj]) {
-      ++cj;
-      ck = kfirst;
+  // resolve every entry of this workgroup once, in parallel: entry i is slot
+  // p = s + i*S of the group; a dense candidate is stored as -(neuron + 1)
+  {
+    float av[8];
+    int nv[8];
+    int cnt_here = 0;
+    for (int i = threadIdx.x; i < n && cnt_here < 8; i += blockDim.x, ++cnt_here) {
+      const int p = s + i * S;
+      int jj = 0;
+      while (jj + 1 < ng && s_pre[jj + 1] <= p) ++jj;
+      const int k = p - s_pre[jj], j = j0 + jj;
+      if (s_dense[jj]) {
+        nv[cnt_here] = -(j * T + k) - 1;
+        av[cnt_here] = 0.f;
+      } else {
+        nv[cnt_here] = j * T + s_idx[jj * E + k];
+        av[cnt_here] = s_val[jj * E + k];
+      }
     }
-    if (cj >= ng) return false;
-    j = cj;
-    k = ck;
-    ck += kstep;
-    return true;
-  };
-  auto entry = [&](int jj, int k, int& neuron, float& a, bool& dense) {
-    const int j = j0 + jj;
-    dense = crow[j] > E;
-    if (dense) {
-      neuron = j * T + k;
-      a = 0.f;
-    } else if (preload) {
-      neuron = j * T + s_idx[jj * E + k];
-      a = s_val[jj * E + k];
-    } else {
-      const size_t ent = ((size_t)t * ntiles + j) * E + k;
-      neuron = j * T + u.idx[ent];
-      a = TR::scalar(u.val, ent);
+    __syncthreads();                              // s_val is rewritten below
+    cnt_here = 0;
+    for (int i = threadIdx.x; i < n && cnt_here < 8; i += blockDim.x, ++cnt_here) {
+      s_nrn[i] = nv[cnt_here];
+      s_val[i] = av[cnt_here];
     }
+    __syncthreads();
+  }
+  auto entry = [&](int i, int& neuron, float& a, bool& dense) {
+    const int v = s_nrn[i];
+    dense = v < 0;
+    neuron = dense ? -v - 1 : v;
+    a = s_val[i];
   };
 
+  // phase-B slice of this wave: chunks [wave*cw, wave*cw + cw), one per lane
+  const int cw = (nch + NW - 1) / NW;
+  const int myc = wave * cw + lane;
+  const bool bl = lane < cw && myc < nch;
+  const size_t rowb = (size_t)d * TR::ES;
+
+  // ---- phase A (+ the first phase-B batch issued early)
   const bool need_up = !u.down_only;
-  // 4-wave workgroups keep two entries' rows in flight per wave, 8-wave ones
-  // one (same bytes in flight per CU, half the registers)
-  constexpr bool PAIR = NW <= 4;
-  int ja, ka, jb = 0, kb = 0;
-  while (next(ja, ka)) {
-    const bool has2 = PAIR && next(jb, kb);
-    int n1, n2 = 0;
-    float a1, a2 = 0.f;
-    bool d1, d2 = false;
-    entry(ja, ka, n1, a1, d1);
-    if (has2) entry(jb, kb, n2, a2, d2);
-    if (d1) {                                      // densely evaluated tile: recompute the gate
+  uint4 pre[UD_BATCH];
+  bool prefetched = false;
+  for (int i0 = wave; i0 < n || !prefetched; i0 += 2 * NW) {
+    const int i1 = i0 + NW;
+    const bool v0 = i0 < n, v1 = i1 < n;
+    int n0 = 0, n1 = 0;
+    float a0 = 0.f, a1 = 0.f;
+    bool d0 = false, d1 = false;
+    if (v0) entry(i0, n0, a0, d0);
+    if (v1) entry(i1, n1, a1, d1);
+    if (v0 && d0) {                               // densely evaluated tile: recompute the gate
+      const float z = gate_recompute<DT>(u, t, n0, s_x, lane, nch) + b;
+      a0 = z > cut ? z : 0.f;
+    }
+    if (v1 && d1) {
       const float z = gate_recompute<DT>(u, t, n1, s_x, lane, nch) + b;
       a1 = z > cut ? z : 0.f;
     }
-    if (has2 && d2) {
-      const float z = gate_recompute<DT>(u, t, n2, s_x, lane, nch) + b;
-      a2 = z > cut ? z : 0.f;
-    }
-    const bool go1 = a1 != 0.f || !d1, go2 = has2 && (a2 != 0.f || !d2);
-    const char* up1 = (const char*)u.w_up + (size_t)n1 * d * TR::ES;
-    const char* dn1 = (const char*)u.w_down_nm + (size_t)n1 * d * TR::ES;
-    const char* up2 = (const char*)u.w_up + (size_t)n2 * d * TR::ES;
-    const char* dn2 = (const char*)u.w_down_nm + (size_t)n2 * d * TR::ES;
-    constexpr int C2 = PAIR ? CPL : 1;
-    uint4 ur1[CPL], dr1[CPL], ur2[C2], dr2[C2];
+    const bool g0 = v0 && need_up && a0 != 0.f, g1 = v1 && need_up && a1 != 0.f;
+    uint4 r0[CPL], r1[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = lane + 64 * i;
-      const bool ok = c < nch;
-      ur1[i] = (ok && go1 && need_up) ? ldg16(up1 + (size_t)c * 16) : uint4{0, 0, 0, 0};
-      dr1[i] = (ok && go1) ? ldg16(dn1 + (size_t)c * 16) : uint4{0, 0, 0, 0};
-      if (PAIR) {
-        ur2[i % C2] = (ok && go2 && need_up) ? ldg16(up2 + (size_t)c * 16) : uint4{0, 0, 0, 0};
-        dr2[i % C2] = (ok && go2) ? ldg16(dn2 + (size_t)c * 16) : uint4{0, 0, 0, 0};
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      r0[c] = (g0 && ch < nch) ? ldg16((const char*)u.w_up + (size_t)n0 * rowb + (size_t)ch * 16) : uint4{0, 0, 0, 0};
+      r1[c] = (g1 && ch < nch) ? ldg16((const char*)u.w_up + (size_t)n1 * rowb + (size_t)ch * 16) : uint4{0, 0, 0, 0};
+    }
+    if (!prefetched) {                            // first phase-B batch (independent of h)
+      int nq[UD_BATCH];
+#pragma unroll
+      for (int q = 0; q < UD_BATCH; ++q) {
+        float aq;
+        bool dq;
+        nq[q] = 0;
+        if (q < n) entry(q, nq[q], aq, dq);
       }
+#pragma unroll
+      for (int q = 0; q < UD_BATCH; ++q)
+        pre[q] = (q < n && bl) ? ldg16((const char*)u.w_down_nm + (size_t)nq[q] * rowb + (size_t)myc * 16) : uint4{0, 0, 0, 0};
+      prefetched = true;
     }
-    float h1 = a1, h2 = a2;
-    if (need_up) {
-      float s1 = 0.f, s2 = 0.f;
+    if (v0 || v1) {
+      float s0 = 0.f, s1 = 0.f;
+      if (need_up) {
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
-        float f1[EPC], f2[EPC], xv[EPC];
-        TR::to_f32(ur1[i], f1);
-        TR::to_f32(PAIR ? ur2[i % C2] : uint4{0, 0, 0, 0}, f2);
-        TR::to_f32(c < nch ? s_x[c] : uint4{0, 0, 0, 0}, xv);
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = lane + 64 * c;
+          float f0[EPC], f1[EPC], xv[EPC];
+          TR::to_f32(r0[c], f0);
+          TR::to_f32(r1[c], f1);
+          TR::to_f32(ch < nch ? s_x[ch] : uint4{0, 0, 0, 0}, xv);
 #pragma unroll
-        for (int q = 0; q < EPC; ++q) {
-          s1 = fmaf(f1[q], xv[q], s1);
-          s2 = fmaf(f2[q], xv[q], s2);
+          for (int q = 0; q < EPC; ++q) {
+            s0 = fmaf(f0[q], xv[q], s0);
+            s1 = fmaf(f1[q], xv[q], s1);
+          }
         }
+        s0 = wave_sum(s0);
+        s1 = wave_sum(s1);
       }
-      h1 = a1 * wave_sum(s1);
-      h2 = a2 * wave_sum(s2);
+      if (lane == 0) {
+        if (v0) s_h[i0] = need_up ? a0 * s0 : a0;
+        if (v1) s_h[i1] = need_up ? a1 * s1 : a1;
+      }
     }
-    if (!go1) h1 = 0.f;
-    if (!go2) h2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      float f1[EPC], f2[EPC];
-      TR::to_f32(dr1[i], f1);
-      TR::to_f32(PAIR ? dr2[i % C2] : uint4{0, 0, 0, 0}, f2);
-#pragma unroll
-      for (int q = 0; q < EPC; ++q)
-        ya[i * EPC + q] = PAIR ? fmaf(h2, f2[q], fmaf(h1, f1[q], ya[i * EPC + q])) : fmaf(h1, f1[q], ya[i * EPC + q]);
-    }
-    if (PAIR && !has2) break;
-  }
-
-  // combine the waves in a fixed order: the first HALF store, the rest add
-  // into the same rows, then the rows are summed
-  if (wave < HALF) {
-#pragma unroll
-    for (int i = 0; i < CPL; ++i)
-#pragma unroll
-      for (int q = 0; q < EPC; ++q) s_y[wave][(i * 64 + lane) * EPC + q] = ya[i * EPC + q];
   }
   __syncthreads();
-  if (NW > HALF && wave >= HALF) {
+
+  // ---- phase B: this wave's slice of y over every entry
+  float ya[EPC];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i)
+  for (int q = 0; q < EPC; ++q) ya[q] = 0.f;
 #pragma unroll
-      for (int q = 0; q < EPC; ++q) s_y[wave - HALF][(i * 64 + lane) * EPC + q] += ya[i * EPC + q];
+  for (int q = 0; q < UD_BATCH; ++q) {
+    if (q < n) {
+      const float h = s_h[q];
+      float f[EPC];
+      TR::to_f32(pre[q], f);
+#pragma unroll
+      for (int k = 0; k < EPC; ++k) ya[k] = fmaf(h, f[k], ya[k]);
+    }
   }
-  if (NW > HALF) __syncthreads();
+  for (int i0 = UD_BATCH; i0 < n; i0 += UD_BATCH) {
+    uint4 rr[UD_BATCH];
+    int nq[UD_BATCH];
+#pragma unroll
+    for (int q = 0; q < UD_BATCH; ++q) {
+      float aq;
+      bool dq;
+      nq[q] = 0;
+      if (i0 + q < n) entry(i0 + q, nq[q], aq, dq);
+    }
+#pragma unroll
+    for (int q = 0; q < UD_BATCH; ++q)
+      rr[q] = (i0 + q < n && bl) ? ldg16((const char*)u.w_down_nm + (size_t)nq[q] * rowb + (size_t)myc * 16) : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < UD_BATCH; ++q) {
+      if (i0 + q < n) {
+        const float h = s_h[i0 + q];
+        float f[EPC];
+        TR::to_f32(rr[q], f);
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) ya[k] = fmaf(h, f[k], ya[k]);
+      }
+    }
+  }
   const int nparts = ngroups * S;
   const size_t part = ((size_t)t * ngroups + g) * S + s;
-  for (int e = threadIdx.x; e < d; e += blockDim.x) {
-    float v = s_y[0][e];
+  if (bl) {
 #pragma unroll
-    for (int w = 1; w < HALF; ++w) v += s_y[w][e];
-    if (nparts == 1) TR::store(u.y, (size_t)t * d + e, v);
-    else u.partial[part * d + e] = v;
+    for (int k = 0; k < EPC; ++k) {
+      const int e = myc * EPC + k;
+      if (nparts == 1) TR::store(u.y, (size_t)t * d + e, ya[k]);
+      else u.partial[part * d + e] = ya[k];
+    }
   }
 }
 
@@ -357,31 +402,19 @@ __global__ __launch_bounds__(64 * RED_GROUPS) void k_ud_reduce(const UpdownDesc 
   }
 }
 
-template <int DT, int NW>
-static hipError_t go_updown_nw(const UpdownDesc& u, hipStream_t s) {
-  const int epc = DT == DT_BF16 ? 8 : 4;
-  const int cpl = (u.d / epc + 63) / 64;
-  dim3 grid(u.M * ud_groups(u) * u.slot_split), blk(64 * NW);
-  switch (cpl) {
-    case 1: hipLaunchKernelGGL((k_updown<1, DT, NW>), grid, blk, 0, s, u); break;
-    case 2: hipLaunchKernelGGL((k_updown<2, DT, NW>), grid, blk, 0, s, u); break;
-    case 3:
-    case 4: hipLaunchKernelGGL((k_updown<4, DT, NW>), grid, blk, 0, s, u); break;
-    case 5: case 6: case 7:
-    case 8: hipLaunchKernelGGL((k_updown<8, DT, NW>), grid, blk, 0, s, u); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 template <int DT>
 static hipError_t go_updown(const UpdownDesc& u, hipStream_t s) {
-  return u.nwaves == 8 ? go_updown_nw<DT, 8>(u, s) : go_updown_nw<DT, 4>(u, s);
+  dim3 grid(u.M * ud_groups(u) * u.slot_split + (u.route_pass ? 1 : 0));
+  if (u.nwaves == 8) hipLaunchKernelGGL((k_updown<DT, 8>), grid, dim3(512), 0, s, u);
+  else hipLaunchKernelGGL((k_updown<DT, 4>), grid, dim3(256), 0, s, u);
+  return hipGetLastError();
 }
 
 hipError_t launch_updown(const UpdownDesc& u, hipStream_t s) {
   if (u.M <= 0) return hipSuccess;
   if (u.tiles_per_group < 1 || u.tiles_per_group > 64 || u.slot_split < 1) return hipErrorInvalidValue;
+  const int epc = u.dtype == DT_BF16 ? 8 : 4;
+  if (u.d / epc > 512 || (u.d / epc + u.nwaves - 1) / u.nwaves > 64) return hipErrorInvalidValue;
   return u.dtype == DT_BF16 ? go_updown<DT_BF16>(u, s) : go_updown<DT_F32>(u, s);
 }
 

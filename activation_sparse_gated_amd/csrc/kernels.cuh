@@ -109,6 +109,8 @@ struct UpdownDesc {
   int rank;
   const float* bias; float bias_scalar; const float* tau; int sel;
 };
+// Entries one sparse workgroup holds in LDS (tiles per group * max entries per tile).
+constexpr int kUpdownCap = 2048;
 __host__ __device__ inline int ud_groups(const UpdownDesc& u) { return (u.F / u.T + u.tiles_per_group - 1) / u.tiles_per_group; }
 // Fused sparse up + down over the pack; then the ordered sum of the partial
 // rows (skipped by the caller when every token fits one workgroup).
