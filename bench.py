@@ -31,8 +31,6 @@ WORKLOADS = {
     "c4": "wina-silu-topk-bf16-4096x11008",
     "c5": "prefill-hybrid-relu-bf16-2048x8192",
 }
-KERNEL_SOURCES = {"updown": "k_updown.hip", "gate": "k_gate.hip", "lowrank_v": "k_gate.hip",
-                  "topk": "k_topk.hip", "reduce": "k_updown.hip", "fallback": "k_gate.hip"}
 
 
 def parse():
@@ -56,10 +54,15 @@ def note(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def src_hash(name: str) -> str:
-    p = os.path.join(ROOT, "activation_sparse_gated_amd", "csrc", name)
-    with open(p, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def src_hash() -> str:
+    """Hash of every kernel source: stored counter readings apply only to the
+    kernels they were taken on."""
+    d = os.path.join(ROOT, "activation_sparse_gated_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
 
 
 def main():
@@ -227,7 +230,7 @@ def main():
     if os.path.exists(tfile):
         with open(tfile) as fh:
             tinfo = json.load(fh).get(f"{cid}-m{m}", {}).get(dom)
-        if tinfo and tinfo.get("source_sha") == src_hash(KERNEL_SOURCES[dom]):
+        if tinfo and tinfo.get("source_sha") == src_hash():
             traffic = tinfo.get("bytes_per_launch")
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
