@@ -19,7 +19,7 @@ EXPORTS = [
     "ffn_sparse_abi_version", "ffn_sparse_status_string", "ffn_sparse_check_config",
     "ffn_sparse_workspace_bytes", "ffn_sparse_pack_bytes", "ffn_sparse_init", "ffn_sparse_gate_pack",
     "ffn_sparse_updown", "ffn_sparse_dense_fallback", "ffn_sparse_forward", "ffn_sparse_dense_forward",
-    "ffn_sparse_timing_enable", "ffn_sparse_timing_read", "ffn_sparse_destroy",
+    "ffn_sparse_forward_path", "ffn_sparse_timing_enable", "ffn_sparse_timing_read", "ffn_sparse_destroy",
 ]
 
 
@@ -70,6 +70,7 @@ def load() -> ctypes.CDLL:
                                          c_int32, P(Pack), c_void_p, c_void_p]),
         "ffn_sparse_dense_forward": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_float, c_void_p,
                                                c_void_p, c_void_p]),
+        "ffn_sparse_forward_path": (c_int32, [c_void_p, c_int32]),
         "ffn_sparse_timing_enable": (c_int32, [c_void_p, c_int32, c_int32]),
         "ffn_sparse_timing_read": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_double)]),
         "ffn_sparse_destroy": (None, [c_void_p]),

@@ -62,6 +62,10 @@ struct Workspace {
   float* ud_partial;     // [ud_rows x d]
   size_t ud_rows;
   void* hbuf;            // [max_m x F] dense hidden
+  uint64_t* dec_lb;      // [kDecMaxM x F / 2] look-back words of the decode gate
+  int32_t* hl_cnt;       // [F / 2] hidden-list entries per decode sub-tile
+  int32_t* hl_nrn;       // [F]
+  float* hl_h;           // [F x kDecMaxM]
   size_t total;
 };
 
@@ -99,8 +103,20 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
   w.ud_rows = ud_rows_for(c, cus);
   w.ud_partial = (float*)take(w.ud_rows * d * sizeof(float));
   w.hbuf = take(M * F * es);
+  w.dec_lb = (uint64_t*)take((size_t)kDecMaxM * (F / 2) * sizeof(uint64_t));
+  w.hl_cnt = (int32_t*)take((F / 2) * sizeof(int32_t));
+  w.hl_nrn = (int32_t*)take(F * sizeof(int32_t));
+  w.hl_h = (float*)take(F * kDecMaxM * sizeof(float));
   w.total = off;
   return w;
+}
+
+int device_lds_max() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+    return v;
+  return 64 * 1024;
 }
 
 int device_cus() {
@@ -117,9 +133,11 @@ int device_cus() {
 // Optional launch-shape overrides (0 = automatic), read once at init from the
 // environment: FFN_SPARSE_GATE_NT, FFN_SPARSE_GATE_WAVES, FFN_SPARSE_UD_SPLIT,
 // FFN_SPARSE_UD_GROUP, FFN_SPARSE_UD_WAVES, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
-// at decode sizes). They change launch shapes only.
+// at decode sizes), FFN_SPARSE_NO_DECODE (1: the general kernels at 1..8 tokens
+// too). They change launch shapes and kernel choice only, never the result
+// beyond floating-point summation order.
 struct Tuning {
-  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0;
+  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0;
 };
 
 static int env_int(const char* name) {
@@ -132,6 +150,7 @@ struct ffn_sparse_handle {
   const void *w_gate, *u, *v, *w_up, *w_down_om, *w_down_nm;
   Workspace ws;
   int cus;
+  int lds_max;
   Tuning tune;
   // timing
   bool timing = false;
@@ -515,6 +534,77 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
   return hip_status(launch_gemm(g, e, s));
 }
 
+// Decode path (k_decode.hip) for bf16 bias / threshold configs at 1..8
+// tokens: 16-wave gate workgroups of R = 16 * IPW / P rows (P = pieces of 512
+// elements per gate row, IPW pieces per wave, R dividing the TwELL tile), all
+// token inputs staged in LDS.
+bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
+  const auto& c = h->cfg;
+  if (c.dtype != FFN_BF16 || c.sel == FFN_SEL_TOPK_WINA || m < 1 || m > kDecMaxM) return false;
+  if (h->tune.no_decode) return false;
+  DecodeDesc d{};
+  d.M = m;
+  d.d = c.d_model;
+  d.F = c.d_ff;
+  d.T = c.tile_w;
+  d.E = c.ell_w;
+  d.rank = c.rank;
+  d.K = c.rank ? c.rank : c.d_model;
+  d.sel = c.sel;
+  int P = 1;
+  while (P * 512 < d.K) P <<= 1;
+  if (P > 8) return false;
+  d.ipw = 0;
+  for (int ipw = 4; ipw >= 1; ipw >>= 1) {
+    const int R = kDecWaves * ipw / P;
+    if (R >= 1 && R <= 64 && c.tile_w % R == 0) {
+      d.ipw = ipw;
+      d.R = R;
+      break;
+    }
+  }
+  // the look-back sums up to 63 predecessor counts across one wave
+  if (d.ipw == 0 || d.R < 2 || d.F / d.R > 4096 || c.tile_w / d.R > 64) return false;
+  const size_t stat = 8 * 1024;    // static LDS of the decode kernels, upper bound
+  if (dec_gate_lds(d) + stat > (size_t)h->lds_max) return false;
+  if (c.rank && dec_lowrank_lds(d) + stat > (size_t)h->lds_max) return false;
+  d.a_gate = c.rank ? h->u : h->w_gate;
+  d.v = h->v;
+  d.w_up = h->w_up;
+  d.w_down_nm = h->w_down_nm;
+  d.t = h->ws.lr_t;
+  d.lb = h->ws.dec_lb;
+  d.ctrl = h->ws.ctrl;
+  d.hl_cnt = h->ws.hl_cnt;
+  d.hl_nrn = h->ws.hl_nrn;
+  d.hl_h = h->ws.hl_h;
+  *out = d;
+  return true;
+}
+
+// Gate pass of the decode path: t = V x (low rank), then the gate kernel
+// (pack; with `up`, also the hidden list).
+ffn_status run_dec_gate(ffn_sparse_handle* h, DecodeDesc& d, const void* x, const float* bias, float bias_scalar,
+                        const float* tau, ffn_twell_pack* pack, float* g_debug, bool up, hipStream_t s) {
+  d.x = x;
+  d.bias = bias;
+  d.bias_scalar = bias_scalar;
+  d.tau = tau;
+  d.cnt = pack->cnt;
+  d.idx = pack->idx;
+  d.val = pack->val;
+  d.g_debug = g_debug;
+  d.up = up ? 1 : 0;
+  hipError_t err = hipSuccess;
+  if (d.rank) {
+    Timed tm(h, FFN_K_LOWRANK_V, s);
+    err = launch_dec_lowrank(d, s);
+  }
+  if (err != hipSuccess) return FFN_E_HIP;
+  Timed tm(h, FFN_K_GATE, s);
+  return hip_status(launch_dec_gate(d, s));
+}
+
 // Launch shape of the sparse kernel: (token, group of G tiles, phase s of S)
 // workgroups of 8 waves; about two workgroups per CU at most, G bounded by the
 // entries a workgroup holds in LDS (a routed token evaluated here can bring T
@@ -649,6 +739,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->cfg = *cfg;
   h->ws = ws;
   h->cus = cus;
+  h->lds_max = device_lds_max();
   h->tune.gate_nt = env_int("FFN_SPARSE_GATE_NT");
   h->tune.gate_waves = env_int("FFN_SPARSE_GATE_WAVES");
   h->tune.ud_split = env_int("FFN_SPARSE_UD_SPLIT");
@@ -656,6 +747,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.v_ks = env_int("FFN_SPARSE_V_KS");
   h->tune.no_gemv = env_int("FFN_SPARSE_NO_GEMV");
   h->tune.ud_waves = env_int("FFN_SPARSE_UD_WAVES");
+  h->tune.no_decode = env_int("FFN_SPARSE_NO_DECODE");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;
@@ -681,6 +773,8 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   if (err == hipSuccess)
     err = launch_fill_u32(reinterpret_cast<uint32_t*>(ws.lb), 0u,
                           (size_t)cfg->max_m * (cfg->d_ff / 16) * 2, s);
+  if (err == hipSuccess)
+    err = launch_fill_u32(reinterpret_cast<uint32_t*>(ws.dec_lb), 0u, (size_t)kDecMaxM * (cfg->d_ff / 2) * 2, s);
   if (err != hipSuccess) {
     delete h;
     return FFN_E_HIP;
@@ -699,7 +793,9 @@ ffn_status ffn_sparse_gate_pack(ffn_sparse_handle* h, const void* x, int32_t m, 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (m == 0) return hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pack->n_dense), 0u, 1, s));
   bool routed_by_topk = false;
-  st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, g_debug, s_debug, s, &routed_by_topk);
+  DecodeDesc dd;
+  if (plan_decode(h, m, &dd)) st = run_dec_gate(h, dd, x, bias, bias_scalar, tau, pack, g_debug, false, s);
+  else st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, g_debug, s_debug, s, &routed_by_topk);
   if (st != FFN_OK || routed_by_topk) return st;
   Timed tm(h, FFN_K_ROUTE, s);
   return hip_status(launch_route(route_desc(h, m, pack), s));
@@ -740,6 +836,16 @@ ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, co
   if (!pack_ok(pack) || (m > 0 && (!y || !aligned16(y)))) return FFN_E_INVALID;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (m == 0) return hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pack->n_dense), 0u, 1, s));
+  DecodeDesc dd;
+  if (plan_decode(h, m, &dd)) {
+    st = run_dec_gate(h, dd, x, bias, bias_scalar, tau, pack, nullptr, true, s);
+    if (st != FFN_OK) return st;
+    dd.y = y;
+    dd.route_pass = 1;
+    dd.route = route_desc(h, m, pack);
+    Timed tm(h, FFN_K_UPDOWN, s);
+    return hip_status(launch_dec_down(dd, s));
+  }
   bool routed_by_topk = false;
   st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, nullptr, nullptr, s, &routed_by_topk);
   if (st != FFN_OK) return st;
@@ -770,6 +876,12 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle* h, const void* x, int32_t
   hipError_t err = run_dense_hidden(h, x, m, nullptr, nullptr, bias, bias_scalar, tau, FFN_K_DENSE, s);
   if (err != hipSuccess) return FFN_E_HIP;
   return hip_status(run_dense_down(h, m, nullptr, nullptr, y, FFN_K_DENSE, s));
+}
+
+int32_t ffn_sparse_forward_path(const ffn_sparse_handle* h, int32_t m) {
+  if (!h || m < 0 || m > h->cfg.max_m) return -1;
+  DecodeDesc dd;
+  return plan_decode(h, m, &dd) ? 1 : 0;
 }
 
 ffn_status ffn_sparse_timing_enable(ffn_sparse_handle* h, int32_t enable, int32_t capacity) {

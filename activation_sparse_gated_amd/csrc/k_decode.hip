@@ -1,0 +1,524 @@
+// Decode path of the sparse gated FFN on gfx950: bf16 weights, at most 8
+// tokens, ReLU gate with a bias or threshold selection.
+//
+// At a handful of tokens every product is a memory-bound weight stream
+// (about one FLOP per byte), so the path is organised around reading each
+// touched weight byte once, with all 256 CUs busy and every load of a wave
+// issued before the first is used:
+//
+//   k_dec_lowrank  t = V x (low-rank gate only; LoPA page, "How LoPA Gating
+//                  Restructures FFN Computation"): 1 KB pieces of V's rows,
+//                  several per wave, reduced in LDS.
+//   k_dec_gate     one workgroup per sub-tile of R gate rows (R divides the
+//                  TwELL tile width T). The gate rows are streamed and dotted
+//                  with every token; the epilogue applies the selection and
+//                  writes the TwELL pack straight from LDS (Sparser/Faster/
+//                  Lighter page, "TwELL 減掉轉換開銷"): a sub-tile learns its
+//                  slot offset inside the TwELL tile from the counts the
+//                  earlier sub-tiles publish (epoch-tagged words). Before it
+//                  waits for those, the workgroup computes the up products of
+//                  its neurons that are active for any token, u = <W_up[i,:], x>
+//                  (each W_up row read once for all tokens), and stores
+//                  h = a * u with the neuron id in the hidden list. A token
+//                  whose tile overflows the ELL width still has every active
+//                  neuron in the list, so no dense backup is needed at these
+//                  token counts (Sparser/Faster/Lighter page, "Hybrid
+//                  應對非均勻稀疏", routes busy rows; here they cost one more
+//                  list entry per neuron).
+//   k_dec_down     one workgroup per 16-byte column chunk of y: it walks the
+//                  whole hidden list and accumulates h * W_down^T[i, chunk]
+//                  for every token, reduces across its lanes in a fixed
+//                  order and writes y once. No partial rows, no atomics, and
+//                  the result is bitwise reproducible. The eight chunks of a
+//                  128-byte line go to the same XCD (workgroups are dealt to
+//                  the eight XCDs round-robin), so its L2 serves the line to
+//                  all of them. An extra workgroup routes the pack.
+#include "common.cuh"
+#include "kernels.cuh"
+#include "route.cuh"
+
+namespace ffn {
+
+// ------------------------------------------------------------------ wave transpose reduction
+// Reduces N values per lane across the 64 lanes of a wave. Each halving step
+// keeps one half of the values and swaps the other half with the partner lane,
+// so N - 1 + (6 - log2 N) shuffles replace N full butterflies. Afterwards
+// v[0] of lane L holds the wave total of value index L >> (6 - log2 N).
+template <int N, int O>
+struct WaveTRed {
+  template <int V>
+  __device__ __forceinline__ static void run(float (&v)[V], int lane) {
+    const bool upper = (lane & O) != 0;
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      const float lo = v[j], hi = v[j + N / 2];
+      const float keep = upper ? hi : lo;
+      const float send = upper ? lo : hi;
+      v[j] = keep + __shfl_xor(send, O, FFN_WAVE);
+    }
+    WaveTRed<N / 2, O / 2>::run(v, lane);
+  }
+};
+template <int O>
+struct WaveTRed<1, O> {
+  template <int V>
+  __device__ __forceinline__ static void run(float (&v)[V], int lane) {
+    v[0] += __shfl_xor(v[0], O, FFN_WAVE);
+    WaveTRed<1, O / 2>::run(v, lane);
+  }
+};
+template <>
+struct WaveTRed<1, 0> {
+  template <int V>
+  __device__ __forceinline__ static void run(float (&)[V], int) {}
+};
+template <int N>
+struct Log2 {
+  static constexpr int value = N <= 1 ? 0 : 1 + Log2<N / 2>::value;
+};
+template <>
+struct Log2<1> {
+  static constexpr int value = 0;
+};
+
+// dot of 8 bf16 weights with 8 bf16 inputs (fp32 products, fixed order)
+__device__ __forceinline__ float dot8_bf(const uint4 a, const uint4 b, float acc) {
+  float fa[8], fb[8];
+  unpack8(a, fa);
+  unpack8(b, fb);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc = fmaf(fa[k], fb[k], acc);
+  return acc;
+}
+__device__ __forceinline__ float dot8_f32(const uint4 a, const float4 b0, const float4 b1, float acc) {
+  float fa[8];
+  unpack8(a, fa);
+  acc = fmaf(fa[0], b0.x, acc); acc = fmaf(fa[1], b0.y, acc);
+  acc = fmaf(fa[2], b0.z, acc); acc = fmaf(fa[3], b0.w, acc);
+  acc = fmaf(fa[4], b1.x, acc); acc = fmaf(fa[5], b1.y, acc);
+  acc = fmaf(fa[6], b1.z, acc); acc = fmaf(fa[7], b1.w, acc);
+  return acc;
+}
+
+// ------------------------------------------------------------------ shared GEMV
+// Dot products of rows [row0, row0 + R) of A (nrows x K bf16, row-major) with
+// the MAXM token rows held in LDS (s_bf: bf16 [MAXM x K]; s_bf32: fp32
+// [MAXM x K]). A row is P pieces of 512 elements (the last may be partly or
+// wholly past K); the workgroup's R * P = NW * IPW pieces are dealt to the
+// waves in row-major order, IPW consecutive pieces per wave, and all of a
+// wave's piece loads are in flight before the first is used. Per piece the
+// lane multiplies its 8 elements; the wave reduces with WaveTRed, piece sums
+// are added per row in piece order. Result: s_g[r * MAXM + m].
+template <int NW, int IPW, int MAXM, bool BF32>
+__device__ __forceinline__ void dec_gemv(const uint16_t* __restrict__ A, int nrows, int K, int P, int row0,
+                                         const uint16_t* s_bf, const float* s_bf32, float* s_part, float* s_g) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int R = NW * IPW / P;
+  uint4 a[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int q = wave * IPW + i, r = q / P, c = q - r * P;
+    const int col = c * 512 + lane * 8;
+    const int row = row0 + r;
+    a[i] = (col < K && row < nrows) ? ldg16(A + (size_t)row * K + col) : uint4{0, 0, 0, 0};
+  }
+  constexpr int V = IPW * MAXM;
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int q = wave * IPW + i, c = q % P;
+    const int col = c * 512 + lane * 8;
+    const bool ok = col < K;
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      float s = 0.f;
+      if (ok) {
+        if (BF32) {
+          const float4 b0 = *reinterpret_cast<const float4*>(s_bf32 + (size_t)m * K + col);
+          const float4 b1 = *reinterpret_cast<const float4*>(s_bf32 + (size_t)m * K + col + 4);
+          s = dot8_f32(a[i], b0, b1, 0.f);
+        } else {
+          s = dot8_bf(a[i], *reinterpret_cast<const uint4*>(s_bf + (size_t)m * K + col), 0.f);
+        }
+      }
+      v[i * MAXM + m] = s;
+    }
+  }
+  WaveTRed<V, 32>::run(v, lane);
+  constexpr int SH = 6 - Log2<V>::value;
+  if ((lane & ((1 << SH) - 1)) == 0) {
+    const int j = lane >> SH, i = j / MAXM, m = j % MAXM;
+    s_part[(wave * IPW + i) * MAXM + m] = v[0];
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < R * MAXM; p += NW * 64) {
+    const int r = p / MAXM, m = p % MAXM;
+    float g = 0.f;
+    for (int c = 0; c < P; ++c) g += s_part[(r * P + c) * MAXM + m];
+    s_g[r * MAXM + m] = g;
+  }
+  __syncthreads();
+}
+
+// Stages `rows` rows of `cols16` 16-byte chunks (row stride ld16 chunks in
+// global memory) into LDS, zero-filling rows [rows, MAXM).
+template <int MAXM>
+__device__ __forceinline__ void stage_rows(uint4* dst, const uint4* src, int rows, int cols16, size_t ld16) {
+  for (int p = threadIdx.x; p < MAXM * cols16; p += blockDim.x) {
+    const int m = p / cols16, c = p - m * cols16;
+    dst[p] = m < rows ? src[(size_t)m * ld16 + c] : uint4{0, 0, 0, 0};
+  }
+}
+
+// ------------------------------------------------------------------ k_dec_lowrank
+template <int IPW, int MAXM>
+__global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank(const DecodeDesc d) {
+  extern __shared__ uint4 s_dyn[];
+  __shared__ float s_part[kDecVWaves * IPW * MAXM];
+  __shared__ float s_g[kDecVWaves * IPW * MAXM];
+  uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn);
+  const int P = d.ipw;                     // pieces per V row (power of two)
+  const int R = kDecVWaves * IPW / P;
+  const int row0 = blockIdx.x * R;
+  stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), d.M, d.d / 8, d.d / 8);
+  __syncthreads();
+  dec_gemv<kDecVWaves, IPW, MAXM, false>(reinterpret_cast<const uint16_t*>(d.v), d.rank, d.d, P, row0, s_x,
+                                         nullptr, s_part, s_g);
+  for (int p = threadIdx.x; p < R * MAXM; p += blockDim.x) {
+    const int r = p / MAXM, m = p % MAXM;
+    if (m < d.M && row0 + r < d.rank) d.t[(size_t)m * d.rank + row0 + r] = s_g[r * MAXM + m];
+  }
+}
+
+// ------------------------------------------------------------------ k_dec_gate
+__device__ __forceinline__ float dec_bias(const DecodeDesc& d, int t) { return d.bias ? d.bias[t] : d.bias_scalar; }
+__device__ __forceinline__ float dec_cut(const DecodeDesc& d, int t) {
+  return d.sel == SEL_THRESH ? fmaxf(d.tau[t], 0.f) : 0.f;
+}
+
+template <int IPW, int MAXM, bool LOWRANK>
+__global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d) {
+  constexpr int NW = kDecWaves;
+  extern __shared__ uint4 s_dyn[];
+  __shared__ float s_part[NW * IPW * MAXM];
+  __shared__ float s_g[64 * MAXM];
+  __shared__ uint64_t s_bal[MAXM];
+  __shared__ int s_urow[64];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int M = d.M, dm = d.d, F = d.F;
+  const int K = d.K;
+  int P = 1;
+  while (P * 512 < K) P <<= 1;
+  const int R = NW * IPW / P;
+  const int sub = blockIdx.x, n0 = sub * R;
+  uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn);                               // [MAXM x d] bf16
+  float* s_t = reinterpret_cast<float*>(reinterpret_cast<char*>(s_dyn) + (size_t)MAXM * dm * 2);  // [MAXM x rank]
+
+  // ---- stage the token inputs (x, and t for the low-rank gate)
+  stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), M, dm / 8, dm / 8);
+  if (LOWRANK)
+    stage_rows<MAXM>(reinterpret_cast<uint4*>(s_t), reinterpret_cast<const uint4*>(d.t), M, d.rank / 4, d.rank / 4);
+  const uint32_t epoch = __hip_atomic_load(&d.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  __syncthreads();
+
+  // ---- gate rows of this sub-tile
+  dec_gemv<NW, IPW, MAXM, LOWRANK>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, s_x, s_t, s_part, s_g);
+
+  // ---- selection: one wave per token; the sub-tile's mask is one ballot (R <= 64)
+  const int T = d.T, Q = T / R, q = (n0 % T) / R, j = n0 / T;
+  const int ntiles = F / T, nsub = F / R;
+  if (wave < M) {
+    const int m = wave;
+    const float b = dec_bias(d, m), cut = dec_cut(d, m);
+    bool act = false;
+    if (lane < R) {
+      const float g = s_g[lane * MAXM + m];
+      if (d.g_debug) d.g_debug[(size_t)m * F + n0 + lane] = g;
+      act = (g + b) > cut;
+    }
+    const uint64_t bal = ballot64(act);
+    if (lane == 0) {
+      s_bal[m] = bal;
+      if (Q > 1)
+        store64_relaxed(d.lb + (size_t)m * nsub + sub, ((uint64_t)epoch << 32) | (uint32_t)__popcll(bal));
+    }
+  }
+  if (threadIdx.x < MAXM && threadIdx.x >= M) s_bal[threadIdx.x] = 0ull;
+  __syncthreads();
+
+  // ---- up products of the neurons active for any token: h = a * <W_up[i,:], x>
+  if (d.up) {
+    uint64_t uni = 0ull;
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) uni |= s_bal[m];
+    const int nu = __popcll(uni);
+    if (wave == 0 && ((uni >> lane) & 1ull)) s_urow[__popcll(uni & lanemask_lt())] = lane;
+    __syncthreads();
+    const int pd = (dm + 511) / 512;
+    for (int k = wave; k < nu; k += NW) {
+      const int r = s_urow[k], n = n0 + r;
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)n * dm;
+      uint4 w[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int col = c * 512 + lane * 8;
+        w[c] = (c < pd && col < dm) ? ldg16(row + col) : uint4{0, 0, 0, 0};
+      }
+      float v[MAXM];
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int col = c * 512 + lane * 8;
+          if (c < pd && col < dm) s = dot8_bf(w[c], *reinterpret_cast<const uint4*>(s_x + (size_t)m * dm + col), s);
+        }
+        v[m] = s;
+      }
+      WaveTRed<MAXM, 32>::run(v, lane);
+      constexpr int SH = 6 - Log2<MAXM>::value;
+      const size_t gi = (size_t)sub * R + k;
+      if ((lane & ((1 << SH) - 1)) == 0) {
+        const int m = lane >> SH;
+        if (m < M) {
+          const bool on = (s_bal[m] >> r) & 1ull;
+          const float a = on ? s_g[r * MAXM + m] + dec_bias(d, m) : 0.f;
+          d.hl_h[gi * kDecMaxM + m] = a * v[0];
+        }
+      }
+      if (lane == 0) d.hl_nrn[gi] = n;
+    }
+    if (threadIdx.x == 0) d.hl_cnt[sub] = nu;
+  }
+
+  // ---- TwELL pack: this sub-tile's entries at their offset inside tile j
+  if (wave < M) {
+    const int m = wave;
+    const uint64_t bal = s_bal[m];
+    int pre = 0;
+    if (Q > 1) {
+      int pv = 0;
+      if (lane < q) {
+        const uint64_t* wp = d.lb + (size_t)m * nsub + (size_t)j * Q + lane;
+        uint64_t w;
+        while (((w = load64_relaxed(wp)) >> 32) != epoch) __builtin_amdgcn_s_sleep(1);
+        pv = (int)(uint32_t)w;
+      }
+      pre = wave_sum_i(pv);
+    }
+    const size_t slot0 = ((size_t)m * ntiles + j) * d.E;
+    const bool act = (bal >> lane) & 1ull;
+    const int pos = pre + __popcll(bal & lanemask_lt());
+    if (act && pos < d.E) {
+      d.idx[slot0 + pos] = (uint16_t)(q * R + lane);
+      const float z = s_g[lane * MAXM + m] + dec_bias(d, m);
+      reinterpret_cast<uint16_t*>(d.val)[slot0 + pos] = (uint16_t)f2bf(z);
+    }
+    if (q == Q - 1) {
+      const int total = pre + __popcll(bal);
+      if (lane == 0) d.cnt[(size_t)m * ntiles + j] = total;
+      for (int s = min(total, d.E) + lane; s < d.E; s += 64) {
+        d.idx[slot0 + s] = 0xFFFF;
+        reinterpret_cast<uint16_t*>(d.val)[slot0 + s] = 0;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ k_dec_down
+constexpr int kDownThreads = 256;
+constexpr int kDownBatch = 8;
+
+template <int MAXM>
+__global__ __launch_bounds__(kDownThreads) void k_dec_down(const DecodeDesc d) {
+  __shared__ int s_pre[4096 + 1];
+  __shared__ int s_scan[kDownThreads / 64];
+  __shared__ float s_red[kDownThreads / 64][8 * MAXM];
+  const int nch = d.d / 8;
+  if (d.route_pass && (int)blockIdx.x == nch) {
+    route_pass(d.route);
+    return;
+  }
+  const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int c = (b & 7) * (nch >> 3) + (b >> 3);       // chunks of one 128-byte line share an XCD
+  const int R = d.R, nsub = d.F / R;
+
+  // exclusive prefix of the per-sub-tile list counts
+  const int per = (nsub + kDownThreads - 1) / kDownThreads;
+  const int s0 = min(nsub, tid * per), s1 = min(nsub, s0 + per);
+  int loc = 0;
+  for (int s = s0; s < s1; ++s) loc += d.hl_cnt[s];
+  int total;
+  int run = block_excl_scan<kDownThreads>(loc, s_scan, &total);
+  for (int s = s0; s < s1; ++s) {
+    s_pre[s] = run;
+    run += d.hl_cnt[s];
+  }
+  if (tid == 0) s_pre[nsub] = total;
+  __syncthreads();
+
+  float acc[MAXM][8];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[m][k] = 0.f;
+  const uint16_t* wd = reinterpret_cast<const uint16_t*>(d.w_down_nm) + (size_t)c * 8;
+  for (int e0 = tid; e0 < total; e0 += kDownThreads * kDownBatch) {
+    uint4 w[kDownBatch];
+    float h[kDownBatch][MAXM];
+#pragma unroll
+    for (int i = 0; i < kDownBatch; ++i) {
+      const int e = e0 + i * kDownThreads;
+      w[i] = uint4{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) h[i][m] = 0.f;
+      if (e < total) {
+        int lo = 0, hi = nsub - 1;            // last sub-tile with s_pre <= e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_pre[mid] <= e) lo = mid;
+          else hi = mid - 1;
+        }
+        const size_t gi = (size_t)lo * R + (e - s_pre[lo]);
+        const int n = d.hl_nrn[gi];
+        w[i] = ldg16(wd + (size_t)n * d.d);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) h[i][m] = m < d.M ? d.hl_h[gi * kDecMaxM + m] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kDownBatch; ++i) {
+      float f[8];
+      unpack8(w[i], f);
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[m][k] = fmaf(h[i][m], f[k], acc[m][k]);
+    }
+  }
+
+  // reduce the 8 * MAXM sums over the workgroup in a fixed order
+  constexpr int V = 8 * MAXM;
+  float v[V];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[m * 8 + k] = acc[m][k];
+  WaveTRed<V, 32>::run(v, lane);
+  constexpr int SH = 6 - Log2<V>::value;
+  if ((lane & ((1 << SH) - 1)) == 0) s_red[wave][lane >> SH] = v[0];
+  __syncthreads();
+  if (tid < V) {
+    const int m = tid / 8, k = tid % 8;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDownThreads / 64; ++w) s += s_red[w][tid];
+    if (m < d.M) reinterpret_cast<uint16_t*>(d.y)[(size_t)m * d.d + c * 8 + k] = (uint16_t)f2bf(s);
+  }
+}
+
+// ------------------------------------------------------------------ launches
+static int pow2_pieces(int K) {
+  int P = 1;
+  while (P * 512 < K) P <<= 1;
+  return P;
+}
+
+static int dec_maxm(int M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
+
+size_t dec_lowrank_lds(const DecodeDesc& d) { return (size_t)dec_maxm(d.M) * d.d * 2; }
+size_t dec_gate_lds(const DecodeDesc& d) {
+  return (size_t)dec_maxm(d.M) * d.d * 2 + (d.rank ? (size_t)dec_maxm(d.M) * d.rank * 4 : 0);
+}
+
+template <typename Kern>
+static hipError_t lds_attr(Kern k, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int IPW, int MAXM>
+static hipError_t go_lowrank(const DecodeDesc& d, hipStream_t s) {
+  const int P = d.ipw, R = kDecVWaves * IPW / P;
+  const size_t lds = dec_lowrank_lds(d);
+  hipError_t e = lds_attr(k_dec_lowrank<IPW, MAXM>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_dec_lowrank<IPW, MAXM>), dim3((d.rank + R - 1) / R), dim3(64 * kDecVWaves), lds, s, d);
+  return hipGetLastError();
+}
+
+// d.ipw carries the pieces per V row here; IPW is chosen so that a workgroup
+// covers whole rows: R = 4 * IPW / P >= 1.
+template <int MAXM>
+static hipError_t go_lowrank_m(const DecodeDesc& d, hipStream_t s) {
+  if (d.ipw >= 8) return go_lowrank<4, MAXM>(d, s);    // P = 8: 2 rows per workgroup
+  if (d.ipw == 4) return go_lowrank<2, MAXM>(d, s);    // P = 4: 2 rows
+  return go_lowrank<2, MAXM>(d, s);                    // P <= 2: 4 or 8 rows
+}
+
+hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s) {
+  if (d.M < 1 || d.M > kDecMaxM || d.rank <= 0) return hipErrorInvalidValue;
+  DecodeDesc e = d;
+  e.ipw = pow2_pieces(d.d);
+  if (e.ipw > 8) return hipErrorInvalidValue;
+  switch (dec_maxm(d.M)) {
+    case 1: return go_lowrank_m<1>(e, s);
+    case 2: return go_lowrank_m<2>(e, s);
+    case 4: return go_lowrank_m<4>(e, s);
+    default: return go_lowrank_m<8>(e, s);
+  }
+}
+
+template <int IPW, int MAXM>
+static hipError_t go_gate(const DecodeDesc& d, hipStream_t s) {
+  const size_t lds = dec_gate_lds(d);
+  const dim3 grid(d.F / d.R), blk(64 * kDecWaves);
+  if (d.rank) {
+    hipError_t e = lds_attr(k_dec_gate<IPW, MAXM, true>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_dec_gate<IPW, MAXM, true>), grid, blk, lds, s, d);
+  } else {
+    hipError_t e = lds_attr(k_dec_gate<IPW, MAXM, false>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_dec_gate<IPW, MAXM, false>), grid, blk, lds, s, d);
+  }
+  return hipGetLastError();
+}
+
+template <int MAXM>
+static hipError_t go_gate_m(const DecodeDesc& d, hipStream_t s) {
+  switch (d.ipw) {
+    case 1: return go_gate<1, MAXM>(d, s);
+    case 2: return go_gate<2, MAXM>(d, s);
+    case 4: return go_gate<4, MAXM>(d, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s) {
+  if (d.M < 1 || d.M > kDecMaxM) return hipErrorInvalidValue;
+  const int P = pow2_pieces(d.K);
+  if (kDecWaves * d.ipw != d.R * P || d.R > 64 || d.R < 2 || d.T % d.R != 0 || d.F % d.R != 0 || d.T / d.R > 64)
+    return hipErrorInvalidValue;
+  switch (dec_maxm(d.M)) {
+    case 1: return go_gate_m<1>(d, s);
+    case 2: return go_gate_m<2>(d, s);
+    case 4: return go_gate_m<4>(d, s);
+    default: return go_gate_m<8>(d, s);
+  }
+}
+
+hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s) {
+  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || d.F / d.R > 4096) return hipErrorInvalidValue;
+  const dim3 grid(d.d / 8 + (d.route_pass ? 1 : 0)), blk(kDownThreads);
+  switch (dec_maxm(d.M)) {
+    case 1: hipLaunchKernelGGL((k_dec_down<1>), grid, blk, 0, s, d); break;
+    case 2: hipLaunchKernelGGL((k_dec_down<2>), grid, blk, 0, s, d); break;
+    case 4: hipLaunchKernelGGL((k_dec_down<4>), grid, blk, 0, s, d); break;
+    default: hipLaunchKernelGGL((k_dec_down<8>), grid, blk, 0, s, d); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ffn

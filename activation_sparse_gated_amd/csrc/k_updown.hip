@@ -25,6 +25,7 @@
 // work is memory-bound either way.
 #include "common.cuh"
 #include "kernels.cuh"
+#include "route.cuh"
 
 namespace ffn {
 
@@ -50,51 +51,6 @@ struct ElemTraits<DT_F32> {
   __device__ static float scalar(const void* p, size_t i) { return reinterpret_cast<const float*>(p)[i]; }
   __device__ static void store(void* p, size_t i, float v) { reinterpret_cast<float*>(p)[i] = v; }
 };
-
-// ------------------------------------------------------------------ routing
-// One workgroup (256 threads): route_t = any tile with cnt > E; dense_list =
-// routed ids ascending; n_dense. Then advances the look-back epoch (the gate
-// pass that wrote this pack has completed).
-__device__ void route_pass(const RouteDesc& r) {
-  __shared__ int s_over[1024];
-  __shared__ int s_scan[4];
-  int base = 0;
-  for (int c0 = 0; c0 < r.M; c0 += 1024) {
-    const int n = min(1024, r.M - c0);
-    for (int i = threadIdx.x; i < 1024; i += blockDim.x) s_over[i] = 0;
-    __syncthreads();
-    for (int p = threadIdx.x; p < n * r.ntiles; p += blockDim.x) {
-      const int t = p / r.ntiles;
-      if (r.cnt[(size_t)(c0 + t) * r.ntiles + (p % r.ntiles)] > r.E) s_over[t] = 1;
-    }
-    __syncthreads();
-    int o[4], ro = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = threadIdx.x * 4 + i;
-      o[i] = t < n ? s_over[t] : 0;
-      ro += o[i];
-    }
-    int tot;
-    int xo = block_excl_scan<256>(ro, s_scan, &tot);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = threadIdx.x * 4 + i;
-      if (t < n) {
-        r.route[c0 + t] = (uint8_t)o[i];
-        if (o[i]) r.dense_list[base + xo] = c0 + t;
-        xo += o[i];
-      }
-    }
-    base += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    *r.n_dense = base;
-    const uint32_t ep = __hip_atomic_load(&r.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&r.ctrl[CTRL_EPOCH], ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
 
 __global__ __launch_bounds__(256) void k_route(const RouteDesc r) { route_pass(r); }
 

@@ -117,4 +117,49 @@ __host__ __device__ inline int ud_groups(const UpdownDesc& u) { return (u.F / u.
 hipError_t launch_updown(const UpdownDesc& u, hipStream_t s);
 hipError_t launch_updown_reduce(const UpdownDesc& u, hipStream_t s);
 
+// Decode path (bf16, bias / threshold selection, at most 8 tokens): three
+// kernels, all on the whole chip.
+//   k_dec_lowrank  t = V x (low-rank gate only), fp32 [M x rank]
+//   k_dec_gate     gate rows of one sub-tile (R rows of a TwELL tile) for all
+//                  tokens, selection, TwELL pack (look-back across the
+//                  sub-tiles of a tile), then u_i = <W_up[i,:], x_t> for the
+//                  neurons active for any token: h = a * u into the hidden list
+//   k_dec_down     one workgroup per 16-byte column chunk of y: y[:, chunk] =
+//                  sum over the hidden list of h * W_down^T[i, chunk], in a
+//                  fixed order; the extra last workgroup routes the pack
+struct DecodeDesc {
+  int M, d, F, T, E, K;        // K: gate contraction length (d, or rank)
+  int rank;                    // 0: full gate
+  int sel;                     // SEL_BIAS / SEL_THRESH
+  const void* a_gate;          // W_gate [F x d] or U [F x rank]
+  const void* v;               // V [rank x d]
+  const void* w_up;            // [F x d]
+  const void* w_down_nm;       // [F x d]
+  const void* x;               // [M x d]
+  void* y;                     // [M x d]
+  float* t;                    // [M x rank] low-rank intermediate
+  const float* bias; float bias_scalar; const float* tau;
+  int32_t* cnt; uint16_t* idx; void* val;   // TwELL pack
+  uint64_t* lb;                // look-back words [8 x F / R]
+  const uint32_t* ctrl;        // control words (look-back epoch)
+  float* g_debug;              // [M x F] or null
+  int R;                       // gate rows per workgroup (divides T)
+  int ipw;                     // gate pieces (1 KB of a row) per wave: 1, 2 or 4
+  int up;                      // 1: compute the hidden list (forward); 0: pack only
+  int32_t* hl_cnt;             // [F / R] list entries per sub-tile
+  int32_t* hl_nrn;             // [F] neuron of each entry (sub-tile s at s * R)
+  float* hl_h;                 // [F x 8] h per token of each entry
+  int route_pass;              // k_dec_down: the last workgroup routes the pack
+  RouteDesc route;
+};
+constexpr int kDecMaxM = 8;
+constexpr int kDecWaves = 16;      // waves of the gate workgroup
+constexpr int kDecVWaves = 4;      // waves of the low-rank first-stage workgroup
+// Dynamic LDS bytes of k_dec_gate / k_dec_lowrank for a descriptor.
+size_t dec_gate_lds(const DecodeDesc& d);
+size_t dec_lowrank_lds(const DecodeDesc& d);
+hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s);
+hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s);
+hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s);
+
 }  // namespace ffn

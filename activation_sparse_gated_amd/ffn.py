@@ -135,6 +135,13 @@ class SparseFFN:
               "ffn_sparse_dense_forward")
         return y
 
+    def forward_path(self, m: int) -> str:
+        """Kernel sequence forward() runs for m tokens: 'decode' or 'general'."""
+        r = self.lib.ffn_sparse_forward_path(self.handle, int(m))
+        if r < 0:
+            raise ValueError(f"invalid token count {m}")
+        return "decode" if r == 1 else "general"
+
     # ------------------------------------------------------------------ timing
     def timing_enable(self, enable: bool = True, capacity: int = 4096) -> None:
         check(self.lib.ffn_sparse_timing_enable(self.handle, 1 if enable else 0, capacity),

@@ -181,6 +181,14 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t
                                     const float *bias, float bias_scalar, const float *tau,
                                     void *y, void *stream);
 
+/* Which kernel sequence ffn_sparse_forward runs for m tokens (host-only
+ * query, no GPU work): 1 = the decode sequence (bf16, bias / threshold
+ * selection, 1 <= m <= 8): low-rank first stage (rank > 0), the gate kernel
+ * (pack + up products of the active neurons), the down kernel (y + routing);
+ * 0 = the general sequence (gate, sparse up + down, partial-row sum, dense
+ * backup); -1 = invalid handle or m. */
+int32_t ffn_sparse_forward_path(const ffn_sparse_handle *h, int32_t m);
+
 /* Per-kernel timing with HIP events recorded on the launch stream around each
  * kernel. enable = 1 starts recording (up to `capacity` launches per kernel
  * kind), 0 stops. ffn_sparse_timing_read synchronises on the recorded events

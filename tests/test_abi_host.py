@@ -113,4 +113,5 @@ def test_calls_reject_null_handle(L):
     assert lib.ffn_sparse_forward(None, 16, 1, None, 0.0, None, 0, ctypes.byref(p), 16, None) == -1
     assert lib.ffn_sparse_dense_forward(None, 16, 1, None, 0.0, None, 16, None) == -1
     assert lib.ffn_sparse_timing_enable(None, 1, 4) == -1
+    assert lib.ffn_sparse_forward_path(None, 1) == -1
     lib.ffn_sparse_destroy(None)

@@ -1,0 +1,116 @@
+"""GPU parity of the decode kernel sequence (bf16, bias / threshold gate,
+1..8 tokens): gate sub-tiles with look-back, the up products in the gate
+workgroups, the column-chunk down kernel. Every case asserts that forward()
+takes that sequence, then checks the pack (bit-exact), the gate against the
+guard band and y against the oracle, through both the standalone entry points
+and forward()."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import ffn_oracle as O
+from synth import make_workload
+from tests.gpu_util import check_pack, check_y, host, make_ffn, sel_args, to_dev, y_to_f64
+from tests.test_gpu_parity import run_full
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+# (workload, tokens, overrides): gate rows per workgroup R = 16 * IPW / P with
+# P = pieces of 512 per gate row; the comment gives (P, R, sub-tiles per TwELL tile)
+DECODE = [
+    ("c2", 1, dict(d=256, f=1024, T=128, E=16)),          # P1 R64 Q2
+    ("c2", 3, dict(d=512, f=2048, T=64, E=8)),            # P1 R64 Q1
+    ("c2", 8, dict(d=1024, f=2048, T=128, E=16)),         # P2 R32 Q4
+    ("c2", 2, dict(d=2048, f=4096, T=128, E=64)),         # P4 R16 Q8
+    ("c2", 4, dict(d=4096, f=2048, T=64, E=8)),           # P8 R8  Q8
+    ("c2", 4, dict(d=192, f=768, T=32, E=4)),             # P1 R32 Q1, partial piece
+    ("c2", 7, dict(d=256, f=1024, T=16, E=16)),           # P1 R16 Q1
+    ("c3", 1, dict(d=512, f=1792, rank=64, T=128, E=16)),
+    ("c3", 6, dict(d=1024, f=2048, rank=128, T=128, E=8)),
+    ("c3", 8, dict(d=2048, f=2048, rank=256, T=64, E=4)),
+    ("c3", 2, dict(d=4096, f=1024, rank=512, T=128, E=64)),
+]
+
+
+@pytest.mark.parametrize("cid,m,kw", DECODE, ids=[f"{c}-m{m}-{i}" for i, (c, m, _) in enumerate(DECODE)])
+def test_decode_parity(cid, m, kw):
+    say("decode", cid, m, kw)
+    wl = make_workload(cid, m, 0, **kw)
+    ffn = make_ffn(wl)
+    assert ffn.forward_path(m) == "decode"
+    ref = O.forward(wl)
+    run_full(wl, ref)
+
+
+@pytest.mark.parametrize("E", [0, 2, 16])
+def test_decode_routed_tokens(E):
+    """Tokens whose tiles overflow E keep every active neuron in the hidden
+    list: y is complete, and route / dense_list still mark them."""
+    say("decode routed E", E)
+    wl = make_workload("c2", 6, 1, d=256, f=1024, T=16, E=16)
+    ref = O.forward(wl, E=E)
+    if E == 0:
+        assert ref["n_dense"] == int((ref["mask"].sum(axis=1) > 0).sum())
+    assert make_ffn(wl, E=E).forward_path(6) == "decode"
+    run_full(wl, ref, E=E)
+
+
+def test_decode_and_general_agree():
+    """The decode sequence and the general one (forced through the tuning
+    switch) give the same pack and y within the parity tolerance."""
+    say("decode vs general")
+    import torch
+    wl = make_workload("c3", 4, 2, d=1024, f=2048, rank=128, T=128, E=16)
+    ref = O.forward(wl)
+    x = to_dev(wl, wl.x)
+    outs = []
+    for force_general in (False, True):
+        if force_general:
+            os.environ["FFN_SPARSE_NO_DECODE"] = "1"
+        try:
+            ffn = make_ffn(wl)
+        finally:
+            os.environ.pop("FFN_SPARSE_NO_DECODE", None)
+        assert ffn.forward_path(wl.m) == ("general" if force_general else "decode")
+        y, pack = ffn.forward(x, **sel_args(wl))
+        torch.cuda.synchronize()
+        check_pack(wl, pack, ref)
+        check_y(y_to_f64(wl, y)[: wl.m], ref["y"])
+        outs.append((host(pack.cnt).copy(), host(pack.idx).copy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_decode_all_masked_and_single_token_repeat():
+    """All-masked tokens give exact zero rows; repeated calls on one handle
+    (look-back epochs advancing) give identical results."""
+    say("decode masked / repeat")
+    import torch
+    from tests.gpu_util import f32_dev
+    wl = make_workload("c2", 3, 0, d=512, f=2048, T=128, E=16)
+    ffn = make_ffn(wl)
+    x = to_dev(wl, wl.x)
+    bias = wl.bias.copy()
+    bias[1] = -1e30
+    y, pack = ffn.forward(x, bias=f32_dev(bias))
+    torch.cuda.synchronize()
+    ref = O.forward(wl, bias=bias)
+    check_pack(wl, pack, ref)
+    assert np.all(host(pack.cnt)[1] == 0)
+    yy = y_to_f64(wl, y)
+    assert np.all(yy[1] == 0.0)
+    check_y(yy[:3], ref["y"])
+    first = host(y).copy()
+    for _ in range(5):
+        y, pack = ffn.forward(x, bias=f32_dev(bias))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), first)

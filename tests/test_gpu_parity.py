@@ -42,14 +42,15 @@ def run_full(wl, ref, *, E=None, check_band=True):
     ffn.dense_fallback(x, pack, y, **kw)
     torch.cuda.synchronize()
     worst = check_y(y_to_f64(wl, y)[: wl.m], ref["y"])
-    # the one-call forward: same pack; non-routed rows bit-identical (same
-    # kernel); routed rows come from the in-kernel dense evaluation at decode
-    # sizes (a different but equally exact path), checked against the oracle
+    # the one-call forward: same pack. On the general path non-routed rows are
+    # bit-identical (same sparse kernel); the decode path (1..8 tokens) sums in
+    # another order, so there only the oracle comparison applies
     y2, pack2 = ffn.forward(x, **kw)
     torch.cuda.synchronize()
     check_pack(wl, pack2, ref, E=E)
-    keep = ref["route"][: wl.m] == 0
-    assert np.array_equal(host(y2)[: wl.m][keep], host(y)[: wl.m][keep])
+    if ffn.forward_path(wl.m) == "general":
+        keep = ref["route"][: wl.m] == 0
+        assert np.array_equal(host(y2)[: wl.m][keep], host(y)[: wl.m][keep])
     check_y(y_to_f64(wl, y2)[: wl.m], ref["y"])
     if (wl.E if E is None else E) > 0:
         assert np.array_equal(host(pack2.idx)[: wl.m], host(pack.idx)[: wl.m])
