@@ -62,10 +62,9 @@ struct Workspace {
   float* ud_partial;     // [ud_rows x d]
   size_t ud_rows;
   void* hbuf;            // [max_m x F] dense hidden
-  uint64_t* dec_lb;      // [kDecMaxM x F / 2] look-back words of the decode gate
-  int32_t* hl_cnt;       // [F / 2] hidden-list entries per decode sub-tile
-  int32_t* hl_nrn;       // [F]
-  float* hl_h;           // [F x kDecMaxM]
+  uint64_t* dec_lb;      // [kDecMaxM x F / 2] per-token look-back words of the decode gate
+  uint64_t* umask;       // [F / 2] decode sub-tiles: neurons active for any token
+  float* hd;             // [kDecMaxM x F] decode hidden values
   size_t total;
 };
 
@@ -104,9 +103,8 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
   w.ud_partial = (float*)take(w.ud_rows * d * sizeof(float));
   w.hbuf = take(M * F * es);
   w.dec_lb = (uint64_t*)take((size_t)kDecMaxM * (F / 2) * sizeof(uint64_t));
-  w.hl_cnt = (int32_t*)take((F / 2) * sizeof(int32_t));
-  w.hl_nrn = (int32_t*)take(F * sizeof(int32_t));
-  w.hl_h = (float*)take(F * kDecMaxM * sizeof(float));
+  w.umask = (uint64_t*)take((F / 2) * sizeof(uint64_t));
+  w.hd = (float*)take(F * kDecMaxM * sizeof(float));
   w.total = off;
   return w;
 }
@@ -564,7 +562,7 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
     }
   }
   // the look-back sums up to 63 predecessor counts across one wave
-  if (d.ipw == 0 || d.R < 2 || d.F / d.R > 4096 || c.tile_w / d.R > 64) return false;
+  if (d.ipw == 0 || d.R < 2 || d.F / d.R > 2048 || c.tile_w / d.R > 64) return false;
   const size_t stat = 8 * 1024;    // static LDS of the decode kernels, upper bound
   if (dec_gate_lds(d) + stat > (size_t)h->lds_max) return false;
   if (c.rank && dec_lowrank_lds(d) + stat > (size_t)h->lds_max) return false;
@@ -575,9 +573,8 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.t = h->ws.lr_t;
   d.lb = h->ws.dec_lb;
   d.ctrl = h->ws.ctrl;
-  d.hl_cnt = h->ws.hl_cnt;
-  d.hl_nrn = h->ws.hl_nrn;
-  d.hl_h = h->ws.hl_h;
+  d.umask = h->ws.umask;
+  d.hd = h->ws.hd;
   *out = d;
   return true;
 }

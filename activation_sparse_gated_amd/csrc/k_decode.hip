@@ -18,15 +18,18 @@
 //                  earlier sub-tiles publish (epoch-tagged words). Before it
 //                  waits for those, the workgroup computes the up products of
 //                  its neurons that are active for any token, u = <W_up[i,:], x>
-//                  (each W_up row read once for all tokens), and stores
-//                  h = a * u with the neuron id in the hidden list. A token
+//                  (each W_up row read once for all tokens), stores h = a * u
+//                  in the dense hidden array h[token, neuron] and the
+//                  sub-tile's union mask (one 64-bit word). A token
 //                  whose tile overflows the ELL width still has every active
 //                  neuron in the list, so no dense backup is needed at these
 //                  token counts (Sparser/Faster/Lighter page, "Hybrid
 //                  應對非均勻稀疏", routes busy rows; here they cost one more
 //                  list entry per neuron).
-//   k_dec_down     one workgroup per 16-byte column chunk of y: it walks the
-//                  whole hidden list and accumulates h * W_down^T[i, chunk]
+//   k_dec_down     one workgroup per 16-byte column chunk of y: it reads the
+//                  union masks in one round, deals their set bits to its
+//                  threads (prefix of popcounts in LDS), then reads h and the
+//                  rows in a second round and accumulates h * W_down^T[i, chunk]
 //                  for every token, reduces across its lanes in a fixed
 //                  order and writes y once. No partial rows, no atomics, and
 //                  the result is bitwise reproducible. The eight chunks of a
@@ -105,16 +108,15 @@ __device__ __forceinline__ float dot8_f32(const uint4 a, const float4 b0, const 
 // the MAXM token rows held in LDS (s_bf: bf16 [MAXM x K]; s_bf32: fp32
 // [MAXM x K]). A row is P pieces of 512 elements (the last may be partly or
 // wholly past K); the workgroup's R * P = NW * IPW pieces are dealt to the
-// waves in row-major order, IPW consecutive pieces per wave, and all of a
-// wave's piece loads are in flight before the first is used. Per piece the
-// lane multiplies its 8 elements; the wave reduces with WaveTRed, piece sums
-// are added per row in piece order. Result: s_g[r * MAXM + m].
-template <int NW, int IPW, int MAXM, bool BF32>
-__device__ __forceinline__ void dec_gemv(const uint16_t* __restrict__ A, int nrows, int K, int P, int row0,
-                                         const uint16_t* s_bf, const float* s_bf32, float* s_part, float* s_g) {
+// waves in row-major order, IPW consecutive pieces per wave.
+// dec_gemv_issue starts the loads of a wave's pieces (they stay in flight
+// while the caller stages the token inputs); dec_gemv_finish multiplies each
+// piece's 8 elements per lane, reduces across the wave with WaveTRed and adds
+// the piece sums of a row in piece order. Result: s_g[r * MAXM + m].
+template <int NW, int IPW>
+__device__ __forceinline__ void dec_gemv_issue(const uint16_t* __restrict__ A, int nrows, int K, int P, int row0,
+                                               uint4 (&a)[IPW]) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int R = NW * IPW / P;
-  uint4 a[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int q = wave * IPW + i, r = q / P, c = q - r * P;
@@ -122,6 +124,13 @@ __device__ __forceinline__ void dec_gemv(const uint16_t* __restrict__ A, int nro
     const int row = row0 + r;
     a[i] = (col < K && row < nrows) ? ldg16(A + (size_t)row * K + col) : uint4{0, 0, 0, 0};
   }
+}
+
+template <int NW, int IPW, int MAXM, bool BF32>
+__device__ __forceinline__ void dec_gemv_finish(const uint4 (&a)[IPW], int K, int P, const uint16_t* s_bf,
+                                                const float* s_bf32, float* s_part, float* s_g) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int R = NW * IPW / P;
   constexpr int V = IPW * MAXM;
   float v[V];
 #pragma unroll
@@ -180,10 +189,11 @@ __global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank(const DecodeDes
   const int P = d.ipw;                     // pieces per V row (power of two)
   const int R = kDecVWaves * IPW / P;
   const int row0 = blockIdx.x * R;
+  uint4 a[IPW];
+  dec_gemv_issue<kDecVWaves, IPW>(reinterpret_cast<const uint16_t*>(d.v), d.rank, d.d, P, row0, a);
   stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), d.M, d.d / 8, d.d / 8);
   __syncthreads();
-  dec_gemv<kDecVWaves, IPW, MAXM, false>(reinterpret_cast<const uint16_t*>(d.v), d.rank, d.d, P, row0, s_x,
-                                         nullptr, s_part, s_g);
+  dec_gemv_finish<kDecVWaves, IPW, MAXM, false>(a, d.d, P, s_x, nullptr, s_part, s_g);
   for (int p = threadIdx.x; p < R * MAXM; p += blockDim.x) {
     const int r = p / MAXM, m = p % MAXM;
     if (m < d.M && row0 + r < d.rank) d.t[(size_t)m * d.rank + row0 + r] = s_g[r * MAXM + m];
@@ -194,6 +204,17 @@ __global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank(const DecodeDes
 __device__ __forceinline__ float dec_bias(const DecodeDesc& d, int t) { return d.bias ? d.bias[t] : d.bias_scalar; }
 __device__ __forceinline__ float dec_cut(const DecodeDesc& d, int t) {
   return d.sel == SEL_THRESH ? fmaxf(d.tau[t], 0.f) : 0.f;
+}
+
+// Waits until an epoch-tagged look-back word carries this pass's epoch and
+// returns its count.
+__device__ __forceinline__ int lb_count(const uint64_t* p, uint32_t epoch, uint64_t first) {
+  uint64_t w = first;
+  while ((uint32_t)(w >> 32) != epoch) {
+    __builtin_amdgcn_s_sleep(1);
+    w = load64_relaxed(p);
+  }
+  return (int)(uint32_t)w;
 }
 
 template <int IPW, int MAXM, bool LOWRANK>
@@ -214,15 +235,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d)
   uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn);                               // [MAXM x d] bf16
   float* s_t = reinterpret_cast<float*>(reinterpret_cast<char*>(s_dyn) + (size_t)MAXM * dm * 2);  // [MAXM x rank]
 
-  // ---- stage the token inputs (x, and t for the low-rank gate)
+  // ---- gate row loads first; the token inputs are staged while they fly
+  uint4 a[IPW];
+  dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
   stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), M, dm / 8, dm / 8);
   if (LOWRANK)
     stage_rows<MAXM>(reinterpret_cast<uint4*>(s_t), reinterpret_cast<const uint4*>(d.t), M, d.rank / 4, d.rank / 4);
   const uint32_t epoch = __hip_atomic_load(&d.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   __syncthreads();
-
-  // ---- gate rows of this sub-tile
-  dec_gemv<NW, IPW, MAXM, LOWRANK>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, s_x, s_t, s_part, s_g);
+  dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
 
   // ---- selection: one wave per token; the sub-tile's mask is one ballot (R <= 64)
   const int T = d.T, Q = T / R, q = (n0 % T) / R, j = n0 / T;
@@ -246,12 +267,20 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d)
   if (threadIdx.x < MAXM && threadIdx.x >= M) s_bal[threadIdx.x] = 0ull;
   __syncthreads();
 
+  // first read of the earlier sub-tiles' counts of tile j (per token), while
+  // this workgroup's up products run
+  const bool tok_wave = wave < M && Q > 1;
+  const uint64_t* twp = d.lb + (size_t)(tok_wave ? wave : 0) * nsub + (size_t)j * Q + lane;
+  uint64_t tw = 0;
+  if (tok_wave && lane < q) tw = load64_relaxed(twp);
+
   // ---- up products of the neurons active for any token: h = a * <W_up[i,:], x>
   if (d.up) {
     uint64_t uni = 0ull;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) uni |= s_bal[m];
     const int nu = __popcll(uni);
+    if (threadIdx.x == 0) d.umask[sub] = uni;
     if (wave == 0 && ((uni >> lane) & 1ull)) s_urow[__popcll(uni & lanemask_lt())] = lane;
     __syncthreads();
     const int pd = (dm + 511) / 512;
@@ -277,18 +306,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d)
       }
       WaveTRed<MAXM, 32>::run(v, lane);
       constexpr int SH = 6 - Log2<MAXM>::value;
-      const size_t gi = (size_t)sub * R + k;
       if ((lane & ((1 << SH) - 1)) == 0) {
         const int m = lane >> SH;
         if (m < M) {
           const bool on = (s_bal[m] >> r) & 1ull;
-          const float a = on ? s_g[r * MAXM + m] + dec_bias(d, m) : 0.f;
-          d.hl_h[gi * kDecMaxM + m] = a * v[0];
+          const float av = on ? s_g[r * MAXM + m] + dec_bias(d, m) : 0.f;
+          d.hd[(size_t)m * F + n] = av * v[0];
         }
       }
-      if (lane == 0) d.hl_nrn[gi] = n;
     }
-    if (threadIdx.x == 0) d.hl_cnt[sub] = nu;
   }
 
   // ---- TwELL pack: this sub-tile's entries at their offset inside tile j
@@ -296,16 +322,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d)
     const int m = wave;
     const uint64_t bal = s_bal[m];
     int pre = 0;
-    if (Q > 1) {
-      int pv = 0;
-      if (lane < q) {
-        const uint64_t* wp = d.lb + (size_t)m * nsub + (size_t)j * Q + lane;
-        uint64_t w;
-        while (((w = load64_relaxed(wp)) >> 32) != epoch) __builtin_amdgcn_s_sleep(1);
-        pv = (int)(uint32_t)w;
-      }
-      pre = wave_sum_i(pv);
-    }
+    if (Q > 1) pre = wave_sum_i(lane < q ? lb_count(twp, epoch, tw) : 0);
     const size_t slot0 = ((size_t)m * ntiles + j) * d.E;
     const bool act = (bal >> lane) & 1ull;
     const int pos = pre + __popcll(bal & lanemask_lt());
@@ -327,11 +344,28 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d)
 
 // ------------------------------------------------------------------ k_dec_down
 constexpr int kDownThreads = 256;
-constexpr int kDownBatch = 8;
+constexpr int kDecMaxSub = 2048;                      // sub-tiles the down kernel's LDS holds
+
+// position of the k-th (from 0) set bit of w (k < popcount(w))
+__device__ __forceinline__ int nth_set_bit(uint64_t w, int k) {
+  int pos = 0;
+#pragma unroll
+  for (int half = 32; half >= 1; half >>= 1) {
+    const int c = __popcll(w & ((1ull << half) - 1ull));
+    if (k >= c) {
+      k -= c;
+      w >>= half;
+      pos += half;
+    }
+  }
+  return pos;
+}
 
 template <int MAXM>
 __global__ __launch_bounds__(kDownThreads) void k_dec_down(const DecodeDesc d) {
-  __shared__ int s_pre[4096 + 1];
+  constexpr int B = MAXM <= 4 ? 8 : 4;               // entries in flight per thread
+  __shared__ uint64_t s_mask[kDecMaxSub];
+  __shared__ int s_pre[kDecMaxSub + 1];
   __shared__ int s_scan[kDownThreads / 64];
   __shared__ float s_red[kDownThreads / 64][8 * MAXM];
   const int nch = d.d / 8;
@@ -342,20 +376,24 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(const DecodeDesc d) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int b = blockIdx.x;
   const int c = (b & 7) * (nch >> 3) + (b >> 3);       // chunks of one 128-byte line share an XCD
-  const int R = d.R, nsub = d.F / R;
+  const int F = d.F, M = d.M, R = d.R, nsub = F / R;
 
-  // exclusive prefix of the per-sub-tile list counts
+  // union masks of a contiguous run of sub-tiles per thread, and the
+  // exclusive prefix of their popcounts
   const int per = (nsub + kDownThreads - 1) / kDownThreads;
   const int s0 = min(nsub, tid * per), s1 = min(nsub, s0 + per);
   int loc = 0;
-  for (int s = s0; s < s1; ++s) loc += d.hl_cnt[s];
+  for (int s = s0; s < s1; ++s) {
+    const uint64_t w = d.umask[s];
+    s_mask[s] = w;
+    loc += __popcll(w);
+  }
   int total;
   int run = block_excl_scan<kDownThreads>(loc, s_scan, &total);
   for (int s = s0; s < s1; ++s) {
     s_pre[s] = run;
-    run += d.hl_cnt[s];
+    run += __popcll(s_mask[s]);
   }
-  if (tid == 0) s_pre[nsub] = total;
   __syncthreads();
 
   float acc[MAXM][8];
@@ -364,31 +402,30 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(const DecodeDesc d) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[m][k] = 0.f;
   const uint16_t* wd = reinterpret_cast<const uint16_t*>(d.w_down_nm) + (size_t)c * 8;
-  for (int e0 = tid; e0 < total; e0 += kDownThreads * kDownBatch) {
-    uint4 w[kDownBatch];
-    float h[kDownBatch][MAXM];
+  for (int e0 = tid; e0 < total; e0 += kDownThreads * B) {
+    uint4 w[B];
+    float h[B][MAXM];
 #pragma unroll
-    for (int i = 0; i < kDownBatch; ++i) {
+    for (int i = 0; i < B; ++i) {
       const int e = e0 + i * kDownThreads;
       w[i] = uint4{0, 0, 0, 0};
 #pragma unroll
       for (int m = 0; m < MAXM; ++m) h[i][m] = 0.f;
       if (e < total) {
-        int lo = 0, hi = nsub - 1;            // last sub-tile with s_pre <= e
+        int lo = 0, hi = nsub - 1;                     // last sub-tile with s_pre <= e
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
           if (s_pre[mid] <= e) lo = mid;
           else hi = mid - 1;
         }
-        const size_t gi = (size_t)lo * R + (e - s_pre[lo]);
-        const int n = d.hl_nrn[gi];
+        const int n = lo * R + nth_set_bit(s_mask[lo], e - s_pre[lo]);
         w[i] = ldg16(wd + (size_t)n * d.d);
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m) h[i][m] = m < d.M ? d.hl_h[gi * kDecMaxM + m] : 0.f;
+        for (int m = 0; m < MAXM; ++m) h[i][m] = m < M ? d.hd[(size_t)m * F + n] : 0.f;
       }
     }
 #pragma unroll
-    for (int i = 0; i < kDownBatch; ++i) {
+    for (int i = 0; i < B; ++i) {
       float f[8];
       unpack8(w[i], f);
 #pragma unroll
@@ -414,7 +451,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(const DecodeDesc d) {
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < kDownThreads / 64; ++w) s += s_red[w][tid];
-    if (m < d.M) reinterpret_cast<uint16_t*>(d.y)[(size_t)m * d.d + c * 8 + k] = (uint16_t)f2bf(s);
+    if (m < M) reinterpret_cast<uint16_t*>(d.y)[(size_t)m * d.d + c * 8 + k] = (uint16_t)f2bf(s);
   }
 }
 
@@ -510,7 +547,7 @@ hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s) {
 }
 
 hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s) {
-  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || d.F / d.R > 4096) return hipErrorInvalidValue;
+  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || d.F / d.R > kDecMaxSub) return hipErrorInvalidValue;
   const dim3 grid(d.d / 8 + (d.route_pass ? 1 : 0)), blk(kDownThreads);
   switch (dec_maxm(d.M)) {
     case 1: hipLaunchKernelGGL((k_dec_down<1>), grid, blk, 0, s, d); break;

@@ -123,7 +123,8 @@ hipError_t launch_updown_reduce(const UpdownDesc& u, hipStream_t s);
 //   k_dec_gate     gate rows of one sub-tile (R rows of a TwELL tile) for all
 //                  tokens, selection, TwELL pack (look-back across the
 //                  sub-tiles of a tile), then u_i = <W_up[i,:], x_t> for the
-//                  neurons active for any token: h = a * u into the hidden list
+//                  neurons active for any token: h = a * u into the dense
+//                  hidden array, and the sub-tile's union mask
 //   k_dec_down     one workgroup per 16-byte column chunk of y: y[:, chunk] =
 //                  sum over the hidden list of h * W_down^T[i, chunk], in a
 //                  fixed order; the extra last workgroup routes the pack
@@ -140,15 +141,14 @@ struct DecodeDesc {
   float* t;                    // [M x rank] low-rank intermediate
   const float* bias; float bias_scalar; const float* tau;
   int32_t* cnt; uint16_t* idx; void* val;   // TwELL pack
-  uint64_t* lb;                // look-back words [8 x F / R]
+  uint64_t* lb;                // per-token look-back words [8 x F / R]
   const uint32_t* ctrl;        // control words (look-back epoch)
   float* g_debug;              // [M x F] or null
   int R;                       // gate rows per workgroup (divides T)
   int ipw;                     // gate pieces (1 KB of a row) per wave: 1, 2 or 4
   int up;                      // 1: compute the hidden list (forward); 0: pack only
-  int32_t* hl_cnt;             // [F / R] list entries per sub-tile
-  int32_t* hl_nrn;             // [F] neuron of each entry (sub-tile s at s * R)
-  float* hl_h;                 // [F x 8] h per token of each entry
+  uint64_t* umask;             // [F / R] neurons of each sub-tile active for any token
+  float* hd;                   // [M x F] h of those neurons (others not written)
   int route_pass;              // k_dec_down: the last workgroup routes the pack
   RouteDesc route;
 };
