@@ -64,7 +64,8 @@ struct Workspace {
   void* hbuf;            // [max_m x F] dense hidden
   uint64_t* dec_lb;      // [kDecMaxM x F / 2] per-token look-back words of the decode gate
   uint64_t* umask;       // [F / 2] decode sub-tiles: neurons active for any token
-  float* hd;             // [kDecMaxM x F] decode hidden values
+  float* hd;             // [kDecMaxM x F] decode hidden values (column-chunk mode)
+  float* dec_part;       // [F / R x min(max_m, 8) x d] decode partial y rows
   size_t total;
 };
 
@@ -105,6 +106,16 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
   w.dec_lb = (uint64_t*)take((size_t)kDecMaxM * (F / 2) * sizeof(uint64_t));
   w.umask = (uint64_t*)take((F / 2) * sizeof(uint64_t));
   w.hd = (float*)take(F * kDecMaxM * sizeof(float));
+  {
+    // the smallest sub-tile (most partial rows) over the token counts 1..8
+    int R = 0;
+    if (c.dtype == FFN_BF16 && c.sel != FFN_SEL_TOPK_WINA) {
+      const int K = c.rank ? c.rank : c.d_model;
+      const int r1 = dec_rows_per_wg(K, c.tile_w, 1, nullptr), r2 = dec_rows_per_wg(K, c.tile_w, 2, nullptr);
+      R = (r1 && r2) ? std::min(r1, r2) : (r1 ? r1 : r2);
+    }
+    w.dec_part = (float*)take(R ? (F / R) * std::min<size_t>(M, kDecMaxM) * d * sizeof(float) : 16);
+  }
   w.total = off;
   return w;
 }
@@ -132,10 +143,11 @@ int device_cus() {
 // environment: FFN_SPARSE_GATE_NT, FFN_SPARSE_GATE_WAVES, FFN_SPARSE_UD_SPLIT,
 // FFN_SPARSE_UD_GROUP, FFN_SPARSE_UD_WAVES, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
 // at decode sizes), FFN_SPARSE_NO_DECODE (1: the general kernels at 1..8 tokens
-// too). They change launch shapes and kernel choice only, never the result
+// too), FFN_SPARSE_DEC_CHUNK (1: decode down projection in column-chunk mode for
+// one token as well). They change launch shapes and kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {
-  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0;
+  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_chunk = 0;
 };
 
 static int env_int(const char* name) {
@@ -549,20 +561,8 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.rank = c.rank;
   d.K = c.rank ? c.rank : c.d_model;
   d.sel = c.sel;
-  int P = 1;
-  while (P * 512 < d.K) P <<= 1;
-  if (P > 8) return false;
-  d.ipw = 0;
-  for (int ipw = 4; ipw >= 1; ipw >>= 1) {
-    const int R = kDecWaves * ipw / P;
-    if (R >= 1 && R <= 64 && c.tile_w % R == 0) {
-      d.ipw = ipw;
-      d.R = R;
-      break;
-    }
-  }
-  // the look-back sums up to 63 predecessor counts across one wave
-  if (d.ipw == 0 || d.R < 2 || d.F / d.R > 2048 || c.tile_w / d.R > 64) return false;
+  d.R = dec_rows_per_wg(d.K, c.tile_w, m, &d.ipw);   // at most 64 sub-tiles per TwELL tile
+  if (d.R == 0 || d.F / d.R > 2048) return false;
   const size_t stat = 8 * 1024;    // static LDS of the decode kernels, upper bound
   if (dec_gate_lds(d) + stat > (size_t)h->lds_max) return false;
   if (c.rank && dec_lowrank_lds(d) + stat > (size_t)h->lds_max) return false;
@@ -575,6 +575,9 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.ctrl = h->ws.ctrl;
   d.umask = h->ws.umask;
   d.hd = h->ws.hd;
+  d.part = h->ws.dec_part;
+  // partial rows cost M x d x 4 bytes per sub-tile: they pay off for one token
+  d.part_mode = (m == 1 && !h->tune.dec_chunk) ? 1 : 0;
   *out = d;
   return true;
 }
@@ -745,6 +748,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.no_gemv = env_int("FFN_SPARSE_NO_GEMV");
   h->tune.ud_waves = env_int("FFN_SPARSE_UD_WAVES");
   h->tune.no_decode = env_int("FFN_SPARSE_NO_DECODE");
+  h->tune.dec_chunk = env_int("FFN_SPARSE_DEC_CHUNK");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;
@@ -841,7 +845,7 @@ ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, co
     dd.route_pass = 1;
     dd.route = route_desc(h, m, pack);
     Timed tm(h, FFN_K_UPDOWN, s);
-    return hip_status(launch_dec_down(dd, s));
+    return hip_status(dd.part_mode ? launch_dec_reduce(dd, s) : launch_dec_down(dd, s));
   }
   bool routed_by_topk = false;
   st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, nullptr, nullptr, s, &routed_by_topk);

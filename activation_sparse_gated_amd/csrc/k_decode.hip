@@ -36,6 +36,8 @@
 //                  128-byte line go to the same XCD (workgroups are dealt to
 //                  the eight XCDs round-robin), so its L2 serves the line to
 //                  all of them. An extra workgroup routes the pack.
+#include <type_traits>
+
 #include "common.cuh"
 #include "kernels.cuh"
 #include "route.cuh"
@@ -217,14 +219,14 @@ __device__ __forceinline__ int lb_count(const uint64_t* p, uint32_t epoch, uint6
   return (int)(uint32_t)w;
 }
 
-template <int IPW, int MAXM, bool LOWRANK>
-__global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d) {
-  constexpr int NW = kDecWaves;
+template <int NW, int IPW, int MAXM, bool LOWRANK, bool PART>
+__global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   extern __shared__ uint4 s_dyn[];
   __shared__ float s_part[NW * IPW * MAXM];
   __shared__ float s_g[64 * MAXM];
   __shared__ uint64_t s_bal[MAXM];
   __shared__ int s_urow[64];
+  __shared__ float s_h[PART ? 64 * MAXM : 1];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int M = d.M, dm = d.d, F = d.F;
   const int K = d.K;
@@ -284,7 +286,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d)
     if (wave == 0 && ((uni >> lane) & 1ull)) s_urow[__popcll(uni & lanemask_lt())] = lane;
     __syncthreads();
     const int pd = (dm + 511) / 512;
-    for (int k = wave; k < nu; k += NW) {
+    // one up product: the owner wave reads W_up[n, :] (8 KB at d = 4096) and
+    // reduces the dot with every token across its lanes
+    auto up_row = [&](int k, bool to_lds) {
       const int r = s_urow[k], n = n0 + r;
       const uint16_t* row = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)n * dm;
       uint4 w[8];
@@ -311,8 +315,67 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate(const DecodeDesc d)
         if (m < M) {
           const bool on = (s_bal[m] >> r) & 1ull;
           const float av = on ? s_g[r * MAXM + m] + dec_bias(d, m) : 0.f;
-          d.hd[(size_t)m * F + n] = av * v[0];
+          if (to_lds) s_h[k * MAXM + m] = av * v[0];
+          else d.hd[(size_t)m * F + n] = av * v[0];
         }
+      }
+    };
+    if (!PART) {
+      for (int k = wave; k < nu; k += NW) up_row(k, false);
+    } else {
+      // partial-row mode: every thread owns CPT consecutive columns of y; the
+      // down rows of a batch of entries are loaded (coalesced, 8 or 16 bytes
+      // per thread) in the same round as their up rows, then scaled by h and
+      // summed in entry order
+      constexpr int CPT = NW == 16 ? 4 : 8;             // 64 * NW * CPT = 4096 columns
+      constexpr int DB = MAXM == 1 ? 16 : (MAXM == 2 ? 8 : 4);
+      using DV = typename std::conditional<CPT == 4, uint2, uint4>::type;
+      const bool colt = (int)threadIdx.x * CPT < dm;
+      const uint16_t* wdn = reinterpret_cast<const uint16_t*>(d.w_down_nm) + (size_t)threadIdx.x * CPT;
+      float acc[MAXM][CPT];
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) acc[m][q] = 0.f;
+      for (int k0 = 0; k0 < nu; k0 += DB) {
+        DV dw[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i) {
+          const int k = k0 + i;
+          dw[i] = (k < nu && colt) ? *reinterpret_cast<const DV*>(wdn + (size_t)(n0 + s_urow[k]) * dm) : DV{};
+        }
+        for (int k = k0 + wave; k < min(nu, k0 + DB); k += NW) up_row(k, true);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < DB; ++i) {
+          const int k = k0 + i;
+          if (k < nu) {
+            float f[CPT];
+            const uint32_t* wv = reinterpret_cast<const uint32_t*>(&dw[i]);
+#pragma unroll
+            for (int q = 0; q < CPT / 2; ++q) {
+              f[2 * q] = __uint_as_float(wv[q] << 16);
+              f[2 * q + 1] = __uint_as_float(wv[q] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+              const float hv = s_h[k * MAXM + m];
+#pragma unroll
+              for (int q = 0; q < CPT; ++q) acc[m][q] = fmaf(hv, f[q], acc[m][q]);
+            }
+          }
+        }
+        __syncthreads();                                // s_h is rewritten by the next batch
+      }
+      if (nu > 0 && colt) {
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+          if (m < M) {
+            float* dst = d.part + ((size_t)sub * M + m) * dm + threadIdx.x * CPT;
+#pragma unroll
+            for (int q = 0; q < CPT; q += 4)
+              *reinterpret_cast<float4*>(dst + q) = float4{acc[m][q], acc[m][q + 1], acc[m][q + 2], acc[m][q + 3]};
+          }
       }
     }
   }
@@ -455,6 +518,78 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(const DecodeDesc d) {
   }
 }
 
+// ------------------------------------------------------------------ k_dec_reduce
+// y[m, slice] = sum over the non-empty sub-tiles (ascending) of their partial
+// rows. A workgroup owns a 128-byte slice (32 fp32 columns) of every token's
+// row: 8 threads read one partial row's slice (16 bytes each), 32 rows in
+// flight per pass; the 32 row sums per column are then added in row order.
+constexpr int kRedThreads = 256;
+
+template <int MAXM>
+__global__ __launch_bounds__(kRedThreads) void k_dec_reduce(const DecodeDesc d) {
+  constexpr int B = 16 / MAXM;                          // partial rows in flight per thread and token
+  __shared__ int s_list[kDecMaxSub];
+  __shared__ int s_scan[kRedThreads / 64];
+  __shared__ float s_red[MAXM][32][33];
+  const int nsl = d.d / 32;
+  if (d.route_pass && (int)blockIdx.x == nsl) {
+    route_pass(d.route);
+    return;
+  }
+  const int tid = threadIdx.x, q = tid & 7, r = tid >> 3;
+  const int sl = blockIdx.x, M = d.M, dm = d.d, nsub = d.F / d.R;
+  // ascending list of the sub-tiles that wrote a partial row
+  const int per = (nsub + kRedThreads - 1) / kRedThreads;
+  const int s0 = min(nsub, tid * per), s1 = min(nsub, s0 + per);
+  int loc = 0;
+  for (int s = s0; s < s1; ++s) loc += d.umask[s] != 0ull;
+  int ne;
+  int pos = block_excl_scan<kRedThreads>(loc, s_scan, &ne);
+  for (int s = s0; s < s1; ++s)
+    if (d.umask[s] != 0ull) s_list[pos++] = s;
+  __syncthreads();
+
+  float acc[MAXM][4];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[m][k] = 0.f;
+  const size_t col = (size_t)sl * 32 + q * 4;
+  for (int p0 = r; p0 < ne; p0 += 32 * B) {
+    float4 v[B][MAXM];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int p = p0 + 32 * i;
+      const int s = p < ne ? s_list[p] : 0;
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m)
+        v[i][m] = (p < ne && m < M) ? *reinterpret_cast<const float4*>(d.part + ((size_t)s * M + m) * dm + col)
+                                    : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) {
+        acc[m][0] += v[i][m].x;
+        acc[m][1] += v[i][m].y;
+        acc[m][2] += v[i][m].z;
+        acc[m][3] += v[i][m].w;
+      }
+  }
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s_red[m][q * 4 + k][r] = acc[m][k];
+  __syncthreads();
+  for (int o = tid; o < MAXM * 32; o += kRedThreads) {
+    const int m = o / 32, c = o % 32;
+    float sum = 0.f;
+#pragma unroll 8
+    for (int rr = 0; rr < 32; ++rr) sum += s_red[m][c][rr];
+    if (m < M) reinterpret_cast<uint16_t*>(d.y)[(size_t)m * dm + (size_t)sl * 32 + c] = (uint16_t)f2bf(sum);
+  }
+}
+
 // ------------------------------------------------------------------ launches
 static int pow2_pieces(int K) {
   int P = 1;
@@ -507,20 +642,21 @@ hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s) {
   }
 }
 
+template <int IPW, int MAXM, bool LOWRANK, bool PART>
+static hipError_t go_gate_k(const DecodeDesc& d, hipStream_t s) {
+  constexpr int NW = dec_gate_waves(MAXM);
+  const size_t lds = dec_gate_lds(d);
+  hipError_t e = lds_attr(k_dec_gate<NW, IPW, MAXM, LOWRANK, PART>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_dec_gate<NW, IPW, MAXM, LOWRANK, PART>), dim3(d.F / d.R), dim3(64 * NW), lds, s, d);
+  return hipGetLastError();
+}
+
 template <int IPW, int MAXM>
 static hipError_t go_gate(const DecodeDesc& d, hipStream_t s) {
-  const size_t lds = dec_gate_lds(d);
-  const dim3 grid(d.F / d.R), blk(64 * kDecWaves);
-  if (d.rank) {
-    hipError_t e = lds_attr(k_dec_gate<IPW, MAXM, true>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_dec_gate<IPW, MAXM, true>), grid, blk, lds, s, d);
-  } else {
-    hipError_t e = lds_attr(k_dec_gate<IPW, MAXM, false>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_dec_gate<IPW, MAXM, false>), grid, blk, lds, s, d);
-  }
-  return hipGetLastError();
+  const bool part = d.up && d.part_mode;
+  if (d.rank) return part ? go_gate_k<IPW, MAXM, true, true>(d, s) : go_gate_k<IPW, MAXM, true, false>(d, s);
+  return part ? go_gate_k<IPW, MAXM, false, true>(d, s) : go_gate_k<IPW, MAXM, false, false>(d, s);
 }
 
 template <int MAXM>
@@ -536,7 +672,7 @@ static hipError_t go_gate_m(const DecodeDesc& d, hipStream_t s) {
 hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s) {
   if (d.M < 1 || d.M > kDecMaxM) return hipErrorInvalidValue;
   const int P = pow2_pieces(d.K);
-  if (kDecWaves * d.ipw != d.R * P || d.R > 64 || d.R < 2 || d.T % d.R != 0 || d.F % d.R != 0 || d.T / d.R > 64)
+  if (dec_gate_waves(dec_maxm(d.M)) * d.ipw != d.R * P || d.R > 64 || d.R < 2 || d.T % d.R != 0 || d.F % d.R != 0 || d.T / d.R > 64)
     return hipErrorInvalidValue;
   switch (dec_maxm(d.M)) {
     case 1: return go_gate_m<1>(d, s);
@@ -544,6 +680,32 @@ hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s) {
     case 4: return go_gate_m<4>(d, s);
     default: return go_gate_m<8>(d, s);
   }
+}
+
+hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s) {
+  if (d.M < 1 || d.M > kDecMaxM || d.d % 32 != 0 || d.F / d.R > kDecMaxSub || !d.part) return hipErrorInvalidValue;
+  const dim3 grid(d.d / 32 + (d.route_pass ? 1 : 0)), blk(kRedThreads);
+  switch (dec_maxm(d.M)) {
+    case 1: hipLaunchKernelGGL((k_dec_reduce<1>), grid, blk, 0, s, d); break;
+    case 2: hipLaunchKernelGGL((k_dec_reduce<2>), grid, blk, 0, s, d); break;
+    case 4: hipLaunchKernelGGL((k_dec_reduce<4>), grid, blk, 0, s, d); break;
+    default: hipLaunchKernelGGL((k_dec_reduce<8>), grid, blk, 0, s, d); break;
+  }
+  return hipGetLastError();
+}
+
+int dec_rows_per_wg(int K, int T, int m, int* ipw_out) {
+  const int P = pow2_pieces(K);
+  if (P > 8 || m < 1 || m > kDecMaxM) return 0;
+  const int nw = dec_gate_waves(dec_maxm(m));
+  for (int ipw = 4; ipw >= 1; ipw >>= 1) {
+    const int R = nw * ipw / P;
+    if (R >= 2 && R <= 64 && T % R == 0 && T / R <= 64) {
+      if (ipw_out) *ipw_out = ipw;
+      return R;
+    }
+  }
+  return 0;
 }
 
 hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s) {

@@ -148,12 +148,18 @@ struct DecodeDesc {
   int ipw;                     // gate pieces (1 KB of a row) per wave: 1, 2 or 4
   int up;                      // 1: compute the hidden list (forward); 0: pack only
   uint64_t* umask;             // [F / R] neurons of each sub-tile active for any token
-  float* hd;                   // [M x F] h of those neurons (others not written)
+  float* hd;                   // [M x F] h of those neurons (column-chunk mode)
+  float* part;                 // [F / R x M x d] fp32 partial y rows (partial-row mode)
+  int part_mode;               // 1: the gate workgroup also sums its down rows into a
+                               // partial y row, k_dec_reduce adds them; 0: column-chunk
+                               // mode (hd + k_dec_down)
   int route_pass;              // k_dec_down: the last workgroup routes the pack
   RouteDesc route;
 };
 constexpr int kDecMaxM = 8;
-constexpr int kDecWaves = 16;      // waves of the gate workgroup
+// waves of the gate workgroup: 16 for one token; 8 (twice the registers per
+// thread) when the up / down accumulators hold several tokens
+constexpr int dec_gate_waves(int maxm) { return maxm == 1 ? 16 : 8; }
 constexpr int kDecVWaves = 4;      // waves of the low-rank first-stage workgroup
 // Dynamic LDS bytes of k_dec_gate / k_dec_lowrank for a descriptor.
 size_t dec_gate_lds(const DecodeDesc& d);
@@ -161,5 +167,9 @@ size_t dec_lowrank_lds(const DecodeDesc& d);
 hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s);
+hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s);
+// Gate rows per decode workgroup for a gate contraction length K, TwELL tile
+// width T and m tokens (0 when the decode shape does not apply).
+int dec_rows_per_wg(int K, int T, int m, int* ipw);
 
 }  // namespace ffn

@@ -25,14 +25,16 @@ def say(*a):
     sys.stdout.flush()
 
 
-# (workload, tokens, overrides): gate rows per workgroup R = 16 * IPW / P with
-# P = pieces of 512 per gate row; the comment gives (P, R, sub-tiles per TwELL tile)
+# (workload, tokens, overrides): gate rows per workgroup R = NW * IPW / P with
+# P = pieces of 512 per gate row, NW = 16 waves for one token and 8 otherwise;
+# the comment gives (P, R, sub-tiles per TwELL tile)
 DECODE = [
     ("c2", 1, dict(d=256, f=1024, T=128, E=16)),          # P1 R64 Q2
-    ("c2", 3, dict(d=512, f=2048, T=64, E=8)),            # P1 R64 Q1
-    ("c2", 8, dict(d=1024, f=2048, T=128, E=16)),         # P2 R32 Q4
-    ("c2", 2, dict(d=2048, f=4096, T=128, E=64)),         # P4 R16 Q8
-    ("c2", 4, dict(d=4096, f=2048, T=64, E=8)),           # P8 R8  Q8
+    ("c2", 3, dict(d=512, f=2048, T=64, E=8)),            # P1 R32 Q2
+    ("c2", 8, dict(d=1024, f=2048, T=128, E=16)),         # P2 R16 Q8
+    ("c2", 2, dict(d=2048, f=4096, T=128, E=64)),         # P4 R8  Q16
+    ("c2", 4, dict(d=4096, f=2048, T=64, E=8)),           # P8 R4  Q16
+    ("c2", 1, dict(d=4096, f=2048, T=64, E=8)),           # P8 R8  Q8
     ("c2", 4, dict(d=192, f=768, T=32, E=4)),             # P1 R32 Q1, partial piece
     ("c2", 7, dict(d=256, f=1024, T=16, E=16)),           # P1 R16 Q1
     ("c3", 1, dict(d=512, f=1792, rank=64, T=128, E=16)),
@@ -65,29 +67,37 @@ def test_decode_routed_tokens(E):
     run_full(wl, ref, E=E)
 
 
-def test_decode_and_general_agree():
-    """The decode sequence and the general one (forced through the tuning
-    switch) give the same pack and y within the parity tolerance."""
-    say("decode vs general")
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_decode_modes_and_general_agree(m):
+    """Both decode down-projection modes (partial rows + reduce, column
+    chunks) and the general sequence (all forced through the tuning switches)
+    give the same pack and y within the parity tolerance; each mode is
+    bitwise reproducible."""
+    say("decode modes vs general, m", m)
     import torch
-    wl = make_workload("c3", 4, 2, d=1024, f=2048, rank=128, T=128, E=16)
+    wl = make_workload("c3", m, 2, d=1024, f=2048, rank=128, T=128, E=16)
     ref = O.forward(wl)
     x = to_dev(wl, wl.x)
     outs = []
-    for force_general in (False, True):
-        if force_general:
-            os.environ["FFN_SPARSE_NO_DECODE"] = "1"
+    for env, path in (({}, "decode"), ({"FFN_SPARSE_DEC_CHUNK": "1"}, "decode"),
+                      ({"FFN_SPARSE_NO_DECODE": "1"}, "general")):
+        os.environ.update(env)
         try:
             ffn = make_ffn(wl)
         finally:
-            os.environ.pop("FFN_SPARSE_NO_DECODE", None)
-        assert ffn.forward_path(wl.m) == ("general" if force_general else "decode")
+            for k in env:
+                os.environ.pop(k, None)
+        assert ffn.forward_path(wl.m) == path
         y, pack = ffn.forward(x, **sel_args(wl))
         torch.cuda.synchronize()
         check_pack(wl, pack, ref)
         check_y(y_to_f64(wl, y)[: wl.m], ref["y"])
+        y_again, _ = ffn.forward(x, **sel_args(wl))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y_again), host(y))
         outs.append((host(pack.cnt).copy(), host(pack.idx).copy()))
-    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    for o in outs[1:]:
+        assert np.array_equal(outs[0][0], o[0]) and np.array_equal(outs[0][1], o[1])
 
 
 def test_decode_all_masked_and_single_token_repeat():
