@@ -13,7 +13,7 @@ DTYPES = {"f32": 0, "bf16": 1}
 ACTS = {"relu": 0, "silu": 1}
 SELS = {"bias": 0, "thresh": 1, "topk": 2}
 KERNEL_KINDS = {"gate": 0, "lowrank_v": 1, "topk": 2, "updown": 3, "reduce": 4, "fallback": 5, "dense": 6,
-                "route": 7}
+                "route": 7, "up": 8}
 
 EXPORTS = [
     "ffn_sparse_abi_version", "ffn_sparse_status_string", "ffn_sparse_check_config",

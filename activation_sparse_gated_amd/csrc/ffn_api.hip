@@ -66,6 +66,9 @@ struct Workspace {
   uint64_t* umask;       // [F / 2] decode sub-tiles: neurons active for any token
   float* hd;             // [kDecMaxM x F] decode hidden values (column-chunk mode)
   float* dec_part;       // [F / R x min(max_m, 8) x d] decode partial y rows
+  int32_t* ul_total;     // [1] decode split mode: union-list length
+  int32_t* ul_nrn;       // [F] decode split mode: union neurons
+  float* ul_h;           // [F x kDecMaxM] decode split mode: h per token
   size_t total;
 };
 
@@ -116,6 +119,9 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
     }
     w.dec_part = (float*)take(R ? (F / R) * std::min<size_t>(M, kDecMaxM) * d * sizeof(float) : 16);
   }
+  w.ul_total = (int32_t*)take(sizeof(int32_t));
+  w.ul_nrn = (int32_t*)take(F * sizeof(int32_t));
+  w.ul_h = (float*)take(F * kDecMaxM * sizeof(float));
   w.total = off;
   return w;
 }
@@ -143,11 +149,11 @@ int device_cus() {
 // environment: FFN_SPARSE_GATE_NT, FFN_SPARSE_GATE_WAVES, FFN_SPARSE_UD_SPLIT,
 // FFN_SPARSE_UD_GROUP, FFN_SPARSE_UD_WAVES, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
 // at decode sizes), FFN_SPARSE_NO_DECODE (1: the general kernels at 1..8 tokens
-// too), FFN_SPARSE_DEC_CHUNK (1: decode down projection in column-chunk mode for
-// one token as well). They change launch shapes and kernel choice only, never the result
+// too), FFN_SPARSE_DEC_MODE (1 + DecMode: force the decode down-projection
+// organisation). They change launch shapes and kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {
-  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_chunk = 0;
+  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0;
 };
 
 static int env_int(const char* name) {
@@ -576,8 +582,16 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.umask = h->ws.umask;
   d.hd = h->ws.hd;
   d.part = h->ws.dec_part;
-  // partial rows cost M x d x 4 bytes per sub-tile: they pay off for one token
-  d.part_mode = (m == 1 && !h->tune.dec_chunk) ? 1 : 0;
+  d.ad = h->ws.hd;
+  d.ul_total = h->ws.ul_total;
+  d.ul_nrn = h->ws.ul_nrn;
+  d.ul_h = h->ws.ul_h;
+  // partial rows cost M x d x 4 bytes per sub-tile: they pay off for one
+  // token; the column-chunk kernel's scattered loads grow with the union, so
+  // from 5 tokens the split sequence (balanced, coalesced) takes over
+  d.mode = m == 1 ? DEC_PART : (m <= 4 ? DEC_CHUNK : DEC_SPLIT);
+  if (h->tune.dec_mode >= 1 && h->tune.dec_mode <= 3) d.mode = h->tune.dec_mode - 1;
+  if (d.mode == DEC_SPLIT && dec_up_lds(d) + 25 * 1024 > (size_t)h->lds_max) d.mode = DEC_CHUNK;
   *out = d;
   return true;
 }
@@ -748,7 +762,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.no_gemv = env_int("FFN_SPARSE_NO_GEMV");
   h->tune.ud_waves = env_int("FFN_SPARSE_UD_WAVES");
   h->tune.no_decode = env_int("FFN_SPARSE_NO_DECODE");
-  h->tune.dec_chunk = env_int("FFN_SPARSE_DEC_CHUNK");
+  h->tune.dec_mode = env_int("FFN_SPARSE_DEC_MODE");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;
@@ -776,6 +790,9 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
                           (size_t)cfg->max_m * (cfg->d_ff / 16) * 2, s);
   if (err == hipSuccess)
     err = launch_fill_u32(reinterpret_cast<uint32_t*>(ws.dec_lb), 0u, (size_t)kDecMaxM * (cfg->d_ff / 2) * 2, s);
+  // the split-mode list is read past its length (masked): keep its ids valid
+  if (err == hipSuccess) err = launch_fill_u32(reinterpret_cast<uint32_t*>(ws.ul_nrn), 0u, cfg->d_ff, s);
+  if (err == hipSuccess) err = launch_fill_u32(reinterpret_cast<uint32_t*>(ws.ul_total), 0u, 1, s);
   if (err != hipSuccess) {
     delete h;
     return FFN_E_HIP;
@@ -844,8 +861,14 @@ ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, co
     dd.y = y;
     dd.route_pass = 1;
     dd.route = route_desc(h, m, pack);
+    if (dd.mode == DEC_SPLIT) {
+      Timed tu(h, FFN_K_UP, s);
+      if (launch_dec_up(dd, s) != hipSuccess) return FFN_E_HIP;
+    }
     Timed tm(h, FFN_K_UPDOWN, s);
-    return hip_status(dd.part_mode ? launch_dec_reduce(dd, s) : launch_dec_down(dd, s));
+    if (dd.mode == DEC_PART) return hip_status(launch_dec_reduce(dd, s));
+    if (dd.mode == DEC_SPLIT) return hip_status(launch_dec_down2(dd, s));
+    return hip_status(launch_dec_down(dd, s));
   }
   bool routed_by_topk = false;
   st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, nullptr, nullptr, s, &routed_by_topk);
@@ -882,7 +905,7 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle* h, const void* x, int32_t
 int32_t ffn_sparse_forward_path(const ffn_sparse_handle* h, int32_t m) {
   if (!h || m < 0 || m > h->cfg.max_m) return -1;
   DecodeDesc dd;
-  return plan_decode(h, m, &dd) ? 1 : 0;
+  return plan_decode(h, m, &dd) ? 1 + dd.mode : 0;
 }
 
 ffn_status ffn_sparse_timing_enable(ffn_sparse_handle* h, int32_t enable, int32_t capacity) {

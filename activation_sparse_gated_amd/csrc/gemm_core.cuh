@@ -487,7 +487,10 @@ static hipError_t go_gemv(const GemmDesc& g, const EpiDesc& e, dim3 grid, hipStr
   return hipErrorInvalidValue;
 }
 
-// Whether the decode GEMV handles this shape (host side).
+// Whether the decode GEMV handles this shape (host side). The tokens' inputs
+// live in NKC * MAXM * BW uint4 registers per lane: at most 8 of them in
+// 16-wave workgroups (128 VGPRs per lane), 32 in 4-wave ones; larger inputs
+// would spill, and the MFMA kernel takes those shapes.
 inline bool gemv_ok(const GemmDesc& g) {
   if (g.dtype != DT_BF16 || g.M > 8 || g.ks != 1 || g.nt > 128 || g.b_nsum != 1) return false;
   const int nkc = (g.K + 511) / 512;
@@ -496,7 +499,7 @@ inline bool gemv_ok(const GemmDesc& g) {
   const int mx = g.M <= 1 ? 1 : (g.M <= 4 ? 4 : 8);
   const int bw = g.bmode == B_F32_SPLIT ? 2 : 1;
   if (bw == 2 && nkc != 1) return false;
-  return kc * mx * bw <= 32;
+  return kc * mx * bw <= (g.nwaves == 16 ? 8 : 32);
 }
 
 // ------------------------------------------------------------------ fp32 VALU kernel

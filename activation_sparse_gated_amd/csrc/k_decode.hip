@@ -219,8 +219,9 @@ __device__ __forceinline__ int lb_count(const uint64_t* p, uint32_t epoch, uint6
   return (int)(uint32_t)w;
 }
 
-template <int NW, int IPW, int MAXM, bool LOWRANK, bool PART>
+template <int NW, int IPW, int MAXM, bool LOWRANK, int MODE>
 __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
+  constexpr bool PART = MODE == DEC_PART;
   extern __shared__ uint4 s_dyn[];
   __shared__ float s_part[NW * IPW * MAXM];
   __shared__ float s_g[64 * MAXM];
@@ -283,6 +284,16 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
     for (int m = 0; m < MAXM; ++m) uni |= s_bal[m];
     const int nu = __popcll(uni);
     if (threadIdx.x == 0) d.umask[sub] = uni;
+    if (MODE == DEC_SPLIT) {
+      // split mode: the activations of the union neurons for k_dec_up
+      for (int p = threadIdx.x; p < R * MAXM; p += NW * 64) {
+        const int r = p / MAXM, m = p % MAXM;
+        if (m < M && ((uni >> r) & 1ull)) {
+          const bool on = (s_bal[m] >> r) & 1ull;
+          d.ad[(size_t)m * F + n0 + r] = on ? s_g[r * MAXM + m] + dec_bias(d, m) : 0.f;
+        }
+      }
+    }
     if (wave == 0 && ((uni >> lane) & 1ull)) s_urow[__popcll(uni & lanemask_lt())] = lane;
     __syncthreads();
     const int pd = (dm + 511) / 512;
@@ -320,9 +331,9 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
         }
       }
     };
-    if (!PART) {
+    if (MODE == DEC_CHUNK) {
       for (int k = wave; k < nu; k += NW) up_row(k, false);
-    } else {
+    } else if (MODE == DEC_PART) {
       // partial-row mode: every thread owns CPT consecutive columns of y; the
       // down rows of a batch of entries are loaded (coalesced, 8 or 16 bytes
       // per thread) in the same round as their up rows, then scaled by h and
@@ -590,6 +601,204 @@ __global__ __launch_bounds__(kRedThreads) void k_dec_reduce(const DecodeDesc d) 
   }
 }
 
+// ------------------------------------------------------------------ k_dec_up (split mode)
+// The union neurons (set bits of the sub-tile masks, ascending) are dealt to a
+// fixed grid in equal contiguous ranges, one wave per neuron: u = <W_up[n,:],
+// x_t> for every token, h = a * u (a from the gate kernel). Writes the compact
+// list (neuron, h per token) in union order and its length.
+constexpr int kUpWaves = 8;
+constexpr int kUpGrid = 256;
+
+template <int MAXM>
+__global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
+  extern __shared__ uint4 s_dyn[];
+  __shared__ uint64_t s_mask[kDecMaxSub];
+  __shared__ int s_pre[kDecMaxSub + 1];
+  __shared__ int s_scan[kUpWaves];
+  uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn);       // [MAXM x d]
+  const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int M = d.M, dm = d.d, F = d.F, R = d.R, nsub = F / R;
+  constexpr int NT = 64 * kUpWaves;
+  const int per = (nsub + NT - 1) / NT;
+  const int s0 = min(nsub, tid * per), s1 = min(nsub, s0 + per);
+  int loc = 0;
+  for (int s = s0; s < s1; ++s) {
+    const uint64_t w = d.umask[s];
+    s_mask[s] = w;
+    loc += __popcll(w);
+  }
+  stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), M, dm / 8, dm / 8);
+  int total;
+  int run = block_excl_scan<NT>(loc, s_scan, &total);
+  for (int s = s0; s < s1; ++s) {
+    s_pre[s] = run;
+    run += __popcll(s_mask[s]);
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) *d.ul_total = total;
+  const int e0 = (int)((long long)total * blockIdx.x / gridDim.x);
+  const int e1 = (int)((long long)total * (blockIdx.x + 1) / gridDim.x);
+  const int pd = (dm + 511) / 512;
+  for (int e = e0 + wave; e < e1; e += kUpWaves) {
+    int lo = 0, hi = nsub - 1;                     // last sub-tile with s_pre <= e
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= e) lo = mid;
+      else hi = mid - 1;
+    }
+    const int n = lo * R + nth_set_bit(s_mask[lo], e - s_pre[lo]);
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)n * dm;
+    uint4 w[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int col = c * 512 + lane * 8;
+      w[c] = (c < pd && col < dm) ? ldg16(row + col) : uint4{0, 0, 0, 0};
+    }
+    float a[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) a[m] = m < M ? d.ad[(size_t)m * F + n] : 0.f;
+    float v[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int col = c * 512 + lane * 8;
+        if (c < pd && col < dm) s = dot8_bf(w[c], *reinterpret_cast<const uint4*>(s_x + (size_t)m * dm + col), s);
+      }
+      v[m] = s;
+    }
+    WaveTRed<MAXM, 32>::run(v, lane);
+    constexpr int SH = 6 - Log2<MAXM>::value;
+    if ((lane & ((1 << SH) - 1)) == 0) {
+      const int m = lane >> SH;
+      float am = a[0];
+#pragma unroll
+      for (int q = 1; q < MAXM; ++q)
+        if (q == m) am = a[q];
+      d.ul_h[(size_t)e * kDecMaxM + m] = m < M ? am * v[0] : 0.f;
+    }
+    if (lane == 0) d.ul_nrn[e] = n;
+  }
+}
+
+// ------------------------------------------------------------------ k_dec_down2 (split mode)
+// One workgroup per slice of LW 16-byte chunks of y's columns (LW = 4 or 8:
+// 64 or 128 bytes of every row). Its 1024 threads form 1024 / LW row lanes:
+// lane q of a row lane reads chunk q of the slice, so a wave reads 64 / LW
+// whole row slices per instruction. Row lane r takes list entries r, r + RL,
+// ...; the list length is read in the same round as the first entries (slots
+// past it hold stale but valid neuron ids and are masked). Sums over the row
+// lanes are reduced across the wave (WaveTRed over the row-lane bits) and then
+// across the waves in order; the extra last workgroup routes the pack.
+constexpr int kDown2Waves = 16;
+
+// Halving steps of WaveTRed restricted to the lane bits >= OMIN. With H the
+// number of halving steps (log2 V, at most 6 - log2 OMIN), each lane keeps
+// V >> H values with index base (lane >> (6 - H)) * (V >> H), summed over the
+// lanes that share lane % OMIN.
+template <int N, int O, int OMIN>
+struct WaveTRedHi {
+  template <int V>
+  __device__ __forceinline__ static void run(float (&v)[V], int lane) {
+    if constexpr (O >= OMIN) {
+      if constexpr (N > 1) {
+        const bool upper = (lane & O) != 0;
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+          const float lo = v[j], hi = v[j + N / 2];
+          const float keep = upper ? hi : lo;
+          const float send = upper ? lo : hi;
+          v[j] = keep + __shfl_xor(send, O, FFN_WAVE);
+        }
+        WaveTRedHi<N / 2, O / 2, OMIN>::run(v, lane);
+      } else {
+        v[0] += __shfl_xor(v[0], O, FFN_WAVE);
+        WaveTRedHi<1, O / 2, OMIN>::run(v, lane);
+      }
+    }
+  }
+};
+
+template <int MAXM, int LW>
+__global__ __launch_bounds__(64 * kDown2Waves) void k_dec_down2(const DecodeDesc d) {
+  constexpr int NT = 64 * kDown2Waves, RL = NT / LW;
+  constexpr int B = MAXM <= 2 ? 8 : 4;                  // entries in flight per thread
+  constexpr int V = 8 * MAXM;                           // sums per thread
+  constexpr int STEPS = 6 - Log2<LW>::value;            // row-lane bits of a wave
+  constexpr int H = Log2<V>::value < STEPS ? Log2<V>::value : STEPS;   // halving steps
+  constexpr int KEEP = V >> H;                          // sums each lane keeps
+  __shared__ float s_red[kDown2Waves][LW][V];
+  const int nsl = d.d / (8 * LW);
+  if (d.route_pass && (int)blockIdx.x == nsl) {
+    route_pass(d.route);
+    return;
+  }
+  const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int q = tid % LW, rl = tid / LW;
+  const int b = blockIdx.x;
+  const int sl = (nsl % 8 == 0) ? (b & 7) * (nsl >> 3) + (b >> 3) : b;   // neighbouring slices share an XCD
+  const int M = d.M, F = d.F;
+  const uint16_t* wd = reinterpret_cast<const uint16_t*>(d.w_down_nm) + (size_t)sl * 8 * LW + q * 8;
+  float acc[MAXM][8];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[m][k] = 0.f;
+  int total = F;
+  for (int e0 = rl; e0 < total; e0 += RL * B) {
+    int nrn[B];
+    float h[B][MAXM];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int e = e0 + i * RL;
+      nrn[i] = e < F ? d.ul_nrn[e] : 0;
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) h[i][m] = (e < F && m < M) ? d.ul_h[(size_t)e * kDecMaxM + m] : 0.f;
+    }
+    if (e0 == rl) total = *d.ul_total;
+    uint4 w[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int e = e0 + i * RL;
+      w[i] = e < total ? ldg16(wd + (size_t)nrn[i] * d.d) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int e = e0 + i * RL;
+      if (e < total) {
+        float f[8];
+        unpack8(w[i], f);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[m][k] = fmaf(h[i][m], f[k], acc[m][k]);
+      }
+    }
+  }
+  float v[V];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[m * 8 + k] = acc[m][k];
+  WaveTRedHi<V, 32, LW>::run(v, lane);
+  {
+    const int base = (lane >> (6 - H)) * KEEP;         // value indices this lane holds
+    if (base < V) {
+#pragma unroll
+      for (int j = 0; j < KEEP; ++j) s_red[wave][q][base + j] = v[j];
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < LW * V; o += NT) {
+    const int qq = o / V, j = o % V, m = j / 8, k = j % 8;
+    float s = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kDown2Waves; ++w2) s += s_red[w2][qq][j];
+    if (m < M) reinterpret_cast<uint16_t*>(d.y)[(size_t)m * d.d + (size_t)sl * 8 * LW + qq * 8 + k] = (uint16_t)f2bf(s);
+  }
+}
+
 // ------------------------------------------------------------------ launches
 static int pow2_pieces(int K) {
   int P = 1;
@@ -642,21 +851,28 @@ hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s) {
   }
 }
 
-template <int IPW, int MAXM, bool LOWRANK, bool PART>
+template <int IPW, int MAXM, bool LOWRANK, int MODE>
 static hipError_t go_gate_k(const DecodeDesc& d, hipStream_t s) {
   constexpr int NW = dec_gate_waves(MAXM);
   const size_t lds = dec_gate_lds(d);
-  hipError_t e = lds_attr(k_dec_gate<NW, IPW, MAXM, LOWRANK, PART>, lds);
+  hipError_t e = lds_attr(k_dec_gate<NW, IPW, MAXM, LOWRANK, MODE>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_gate<NW, IPW, MAXM, LOWRANK, PART>), dim3(d.F / d.R), dim3(64 * NW), lds, s, d);
+  hipLaunchKernelGGL((k_dec_gate<NW, IPW, MAXM, LOWRANK, MODE>), dim3(d.F / d.R), dim3(64 * NW), lds, s, d);
   return hipGetLastError();
+}
+
+template <int IPW, int MAXM, bool LOWRANK>
+static hipError_t go_gate_mode(const DecodeDesc& d, hipStream_t s) {
+  // a pack-only pass (no hidden values) uses the chunk-mode kernel with up = 0
+  const int mode = d.up ? d.mode : DEC_CHUNK;
+  if (mode == DEC_PART) return go_gate_k<IPW, MAXM, LOWRANK, DEC_PART>(d, s);
+  if (mode == DEC_SPLIT) return go_gate_k<IPW, MAXM, LOWRANK, DEC_SPLIT>(d, s);
+  return go_gate_k<IPW, MAXM, LOWRANK, DEC_CHUNK>(d, s);
 }
 
 template <int IPW, int MAXM>
 static hipError_t go_gate(const DecodeDesc& d, hipStream_t s) {
-  const bool part = d.up && d.part_mode;
-  if (d.rank) return part ? go_gate_k<IPW, MAXM, true, true>(d, s) : go_gate_k<IPW, MAXM, true, false>(d, s);
-  return part ? go_gate_k<IPW, MAXM, false, true>(d, s) : go_gate_k<IPW, MAXM, false, false>(d, s);
+  return d.rank ? go_gate_mode<IPW, MAXM, true>(d, s) : go_gate_mode<IPW, MAXM, false>(d, s);
 }
 
 template <int MAXM>
@@ -692,6 +908,50 @@ hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s) {
     default: hipLaunchKernelGGL((k_dec_reduce<8>), grid, blk, 0, s, d); break;
   }
   return hipGetLastError();
+}
+
+size_t dec_up_lds(const DecodeDesc& d) { return (size_t)dec_maxm(d.M) * d.d * 2; }
+
+template <int MAXM>
+static hipError_t go_up(const DecodeDesc& d, hipStream_t s) {
+  const size_t lds = dec_up_lds(d);
+  hipError_t e = lds_attr(k_dec_up<MAXM>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_dec_up<MAXM>), dim3(kUpGrid), dim3(64 * kUpWaves), lds, s, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_up(const DecodeDesc& d, hipStream_t s) {
+  if (d.M < 1 || d.M > kDecMaxM || d.F / d.R > kDecMaxSub || !d.ad || !d.ul_nrn || !d.ul_h || !d.ul_total)
+    return hipErrorInvalidValue;
+  switch (dec_maxm(d.M)) {
+    case 1: return go_up<1>(d, s);
+    case 2: return go_up<2>(d, s);
+    case 4: return go_up<4>(d, s);
+    default: return go_up<8>(d, s);
+  }
+}
+
+// slices of 64 bytes when that still leaves >= 64 workgroups, else 128 bytes
+template <int MAXM>
+static hipError_t go_down2(const DecodeDesc& d, hipStream_t s) {
+  const int extra = d.route_pass ? 1 : 0;
+  if (d.d / 32 >= 64) {
+    hipLaunchKernelGGL((k_dec_down2<MAXM, 4>), dim3(d.d / 32 + extra), dim3(64 * kDown2Waves), 0, s, d);
+  } else {
+    hipLaunchKernelGGL((k_dec_down2<MAXM, 8>), dim3(d.d / 64 + extra), dim3(64 * kDown2Waves), 0, s, d);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s) {
+  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || !d.ul_nrn || !d.ul_h || !d.ul_total) return hipErrorInvalidValue;
+  switch (dec_maxm(d.M)) {
+    case 1: return go_down2<1>(d, s);
+    case 2: return go_down2<2>(d, s);
+    case 4: return go_down2<4>(d, s);
+    default: return go_down2<8>(d, s);
+  }
 }
 
 int dec_rows_per_wg(int K, int T, int m, int* ipw_out) {

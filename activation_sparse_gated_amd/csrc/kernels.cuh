@@ -128,6 +128,15 @@ hipError_t launch_updown_reduce(const UpdownDesc& u, hipStream_t s);
 //   k_dec_down     one workgroup per 16-byte column chunk of y: y[:, chunk] =
 //                  sum over the hidden list of h * W_down^T[i, chunk], in a
 //                  fixed order; the extra last workgroup routes the pack
+// Down-projection organisation of the decode path.
+//   DEC_CHUNK  gate workgroups compute h of their active neurons into a dense
+//              array; k_dec_down: one workgroup per 16-byte column chunk
+//   DEC_PART   gate workgroups also sum their down rows into a partial y row;
+//              k_dec_reduce adds the partial rows
+//   DEC_SPLIT  gate workgroups publish masks and activations only; k_dec_up
+//              deals the union neurons evenly over the chip (compact h list);
+//              k_dec_down2 streams the list with coalesced row slices
+enum DecMode : int { DEC_CHUNK = 0, DEC_PART = 1, DEC_SPLIT = 2 };
 struct DecodeDesc {
   int M, d, F, T, E, K;        // K: gate contraction length (d, or rank)
   int rank;                    // 0: full gate
@@ -150,9 +159,11 @@ struct DecodeDesc {
   uint64_t* umask;             // [F / R] neurons of each sub-tile active for any token
   float* hd;                   // [M x F] h of those neurons (column-chunk mode)
   float* part;                 // [F / R x M x d] fp32 partial y rows (partial-row mode)
-  int part_mode;               // 1: the gate workgroup also sums its down rows into a
-                               // partial y row, k_dec_reduce adds them; 0: column-chunk
-                               // mode (hd + k_dec_down)
+  int mode;                    // DEC_CHUNK, DEC_PART or DEC_SPLIT (see DecMode)
+  float* ad;                   // [M x F] split mode: a = z (active) or 0 for union neurons
+  int32_t* ul_total;           // [1] split mode: union-list length
+  int32_t* ul_nrn;             // [F] split mode: union neurons, ascending (compact)
+  float* ul_h;                 // [F x 8] split mode: h per token of each list entry
   int route_pass;              // k_dec_down: the last workgroup routes the pack
   RouteDesc route;
 };
@@ -168,6 +179,9 @@ hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s);
+hipError_t launch_dec_up(const DecodeDesc& d, hipStream_t s);
+size_t dec_up_lds(const DecodeDesc& d);
+hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s);
 // Gate rows per decode workgroup for a gate contraction length K, TwELL tile
 // width T and m tokens (0 when the decode shape does not apply).
 int dec_rows_per_wg(int K, int T, int m, int* ipw);

@@ -136,11 +136,12 @@ class SparseFFN:
         return y
 
     def forward_path(self, m: int) -> str:
-        """Kernel sequence forward() runs for m tokens: 'decode' or 'general'."""
+        """Kernel sequence forward() runs for m tokens: 'general', or
+        'decode-chunk' / 'decode-part' / 'decode-split' (see the C header)."""
         r = self.lib.ffn_sparse_forward_path(self.handle, int(m))
         if r < 0:
             raise ValueError(f"invalid token count {m}")
-        return "decode" if r == 1 else "general"
+        return {0: "general", 1: "decode-chunk", 2: "decode-part", 3: "decode-split"}[r]
 
     # ------------------------------------------------------------------ timing
     def timing_enable(self, enable: bool = True, capacity: int = 4096) -> None:

@@ -202,7 +202,7 @@ def main():
         sparse_step(i)
     torch.cuda.synchronize()
     kernels = {}
-    for kind in ("lowrank_v", "gate", "topk", "updown", "reduce", "fallback"):
+    for kind in ("lowrank_v", "gate", "up", "topk", "updown", "reduce", "fallback"):
         n_tot, ms_tot = 0, 0.0
         for ffn, *_ in layers:
             n, ms = ffn.timing_read(kind)
@@ -214,13 +214,27 @@ def main():
         ffn.timing_enable(False)
 
     # algorithmic bytes per launch of each kernel
+    # algorithmic bytes per launch: each weight byte a kernel must read once,
+    # its inputs and its outputs (partial rows and lists are not counted)
+    path = ffn0.forward_path(m)
+    gate_alg = (F * r * 2 + m * r * 4 if r else F * d * 2 + m * d * 2) + pack_bytes + m * 9
+    urow = n_union * d * 2                       # up rows (or down rows) of the union neurons
     alg = {
         "lowrank_v": r * d * 2 + m * d * 2 + m * r * 4,
-        "gate": (F * r * 2 + m * r * 4 if r else F * d * 2 + m * d * 2) + pack_bytes + m * 9,
+        "gate": gate_alg,
         "updown": entries * row_bytes + m * d * 2 + m * d * 2 + pack_bytes,
         "topk": m * F * 8 + pack_bytes,
         "reduce": m * d * 2,
     }
+    if path == "decode-chunk":
+        alg["gate"] = gate_alg + urow
+        alg["updown"] = urow + m * d * 2
+    elif path == "decode-part":
+        alg["gate"] = gate_alg + 2 * urow
+        alg["updown"] = m * d * 2
+    elif path == "decode-split":
+        alg["up"] = urow + m * d * 2
+        alg["updown"] = urow + m * d * 2
     if wl.sel == "topk":
         alg["gate"] = 2 * F * d * 2 + m * d * 2 + 2 * m * F * 4
     dom = max((k for k in kernels if k in alg), key=lambda k: kernels[k]["avg_us"])
@@ -270,7 +284,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{WORKLOADS[cid]} m={m}", "d_model": d, "d_ff": F, "rank": r, "m": m,
                    "tile_w": T, "ell_w": E, "active_neurons": n_union, "layers_rotated": len(layers),
-                   "hip_graph": bool(args.graph)},
+                   "hip_graph": bool(args.graph), "kernel_path": path},
         "effective_hbm_GBps": round(touched / (ms_sparse * 1e-3) / 1e9, 1),
         "touched_bytes": int(touched),
         "dense_ms_per_step": round(ms_dense, 5),

@@ -182,9 +182,16 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t
                                     void *y, void *stream);
 
 /* Which kernel sequence ffn_sparse_forward runs for m tokens (host-only
- * query, no GPU work): 1 = the decode sequence (bf16, bias / threshold
- * selection, 1 <= m <= 8): low-rank first stage (rank > 0), the gate kernel
- * (pack + up products of the active neurons), the down kernel (y + routing);
+ * query, no GPU work). The decode sequences (bf16, bias / threshold
+ * selection, 1 <= m <= 8) run the low-rank first stage (rank > 0) and the gate
+ * kernel (selection + TwELL pack), then:
+ *   1 = column chunks: the gate kernel computes h of its active neurons, one
+ *       workgroup per 16-byte column chunk of y sums h * W_down rows;
+ *   2 = partial rows: the gate kernel also sums its active neurons' down rows
+ *       into a partial y row, a second kernel adds the partial rows;
+ *   3 = split: an up kernel deals the active neurons evenly over the chip and
+ *       writes a compact (neuron, h) list, a down kernel streams it in column
+ *       slices.
  * 0 = the general sequence (gate, sparse up + down, partial-row sum, dense
  * backup); -1 = invalid handle or m. */
 int32_t ffn_sparse_forward_path(const ffn_sparse_handle *h, int32_t m);
@@ -203,7 +210,8 @@ typedef enum {
   FFN_K_FALLBACK = 5,  /* dense backup kernels                                 */
   FFN_K_DENSE = 6,     /* dense baseline kernels                               */
   FFN_K_ROUTE = 7,     /* routing pass of a standalone gate_pack               */
-  FFN_K_COUNT = 8
+  FFN_K_UP = 8,        /* decode: up products of the union neurons (split mode) */
+  FFN_K_COUNT = 9
 } ffn_kernel_kind;
 ffn_status ffn_sparse_timing_enable(ffn_sparse_handle *h, int32_t enable, int32_t capacity);
 ffn_status ffn_sparse_timing_read(ffn_sparse_handle *h, int32_t kind, int32_t *launches,

@@ -49,7 +49,7 @@ def test_decode_parity(cid, m, kw):
     say("decode", cid, m, kw)
     wl = make_workload(cid, m, 0, **kw)
     ffn = make_ffn(wl)
-    assert ffn.forward_path(m) == "decode"
+    assert ffn.forward_path(m).startswith("decode")
     ref = O.forward(wl)
     run_full(wl, ref)
 
@@ -63,24 +63,32 @@ def test_decode_routed_tokens(E):
     ref = O.forward(wl, E=E)
     if E == 0:
         assert ref["n_dense"] == int((ref["mask"].sum(axis=1) > 0).sum())
-    assert make_ffn(wl, E=E).forward_path(6) == "decode"
+    assert make_ffn(wl, E=E).forward_path(6).startswith("decode")
     run_full(wl, ref, E=E)
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 8])
-def test_decode_modes_and_general_agree(m):
-    """Both decode down-projection modes (partial rows + reduce, column
-    chunks) and the general sequence (all forced through the tuning switches)
-    give the same pack and y within the parity tolerance; each mode is
-    bitwise reproducible."""
-    say("decode modes vs general, m", m)
+MODES = (({"FFN_SPARSE_DEC_MODE": "1"}, "decode-chunk"), ({"FFN_SPARSE_DEC_MODE": "2"}, "decode-part"),
+         ({"FFN_SPARSE_DEC_MODE": "3"}, "decode-split"), ({"FFN_SPARSE_NO_DECODE": "1"}, "general"))
+
+
+@pytest.mark.parametrize("cid,m,kw", [("c3", 1, dict(d=1024, f=2048, rank=128, T=128, E=16)),
+                                      ("c3", 2, dict(d=1024, f=2048, rank=128, T=128, E=16)),
+                                      ("c3", 4, dict(d=1024, f=2048, rank=128, T=128, E=16)),
+                                      ("c3", 8, dict(d=1024, f=2048, rank=128, T=128, E=16)),
+                                      ("c2", 3, dict(d=2048, f=4096, T=128, E=4)),
+                                      ("c2", 1, dict(d=192, f=768, T=32, E=4)),
+                                      ("c2", 4, dict(d=4096, f=1024, T=64, E=8))])
+def test_decode_modes_and_general_agree(cid, m, kw):
+    """The three decode down-projection organisations and the general
+    sequence (all forced through the tuning switches) give the same pack and y
+    within the parity tolerance; each is bitwise reproducible."""
+    say("decode modes vs general", cid, m, kw)
     import torch
-    wl = make_workload("c3", m, 2, d=1024, f=2048, rank=128, T=128, E=16)
+    wl = make_workload(cid, m, 2, **kw)
     ref = O.forward(wl)
     x = to_dev(wl, wl.x)
     outs = []
-    for env, path in (({}, "decode"), ({"FFN_SPARSE_DEC_CHUNK": "1"}, "decode"),
-                      ({"FFN_SPARSE_NO_DECODE": "1"}, "general")):
+    for env, path in MODES:
         os.environ.update(env)
         try:
             ffn = make_ffn(wl)
