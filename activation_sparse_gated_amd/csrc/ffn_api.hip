@@ -117,7 +117,10 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
       const int r1 = dec_rows_per_wg(K, c.tile_w, 1, nullptr), r2 = dec_rows_per_wg(K, c.tile_w, 2, nullptr);
       R = (r1 && r2) ? std::min(r1, r2) : (r1 ? r1 : r2);
     }
-    w.dec_part = (float*)take(R ? (F / R) * std::min<size_t>(M, kDecMaxM) * d * sizeof(float) : 16);
+    // partial rows of the gate sub-tiles (partial-row mode) or of the down
+    // kernel's entry groups (split mode), whichever is larger
+    const size_t mm = std::min<size_t>(M, kDecMaxM);
+    w.dec_part = (float*)take(R ? std::max<size_t>(F / R, 32) * mm * d * sizeof(float) : 16);
   }
   w.ul_total = (int32_t*)take(sizeof(int32_t));
   w.ul_nrn = (int32_t*)take(F * sizeof(int32_t));
@@ -150,10 +153,11 @@ int device_cus() {
 // FFN_SPARSE_UD_GROUP, FFN_SPARSE_UD_WAVES, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
 // at decode sizes), FFN_SPARSE_NO_DECODE (1: the general kernels at 1..8 tokens
 // too), FFN_SPARSE_DEC_MODE (1 + DecMode: force the decode down-projection
-// organisation). They change launch shapes and kernel choice only, never the result
+// organisation), FFN_SPARSE_NO_PREFILL_GEMM (1: the decode-shaped MFMA kernel
+// for 128+ tokens as well). They change launch shapes and kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {
-  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0;
+  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0;
 };
 
 static int env_int(const char* name) {
@@ -205,6 +209,7 @@ GemmDesc gemm_base(const ffn_sparse_handle* h) {
   g.nwaves = 4;
   g.ctrl = h->ws.ctrl;
   g.bmode = B_NATIVE;
+  g.no_pf = h->tune.no_pf;
   return g;
 }
 
@@ -586,6 +591,7 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.ul_total = h->ws.ul_total;
   d.ul_nrn = h->ws.ul_nrn;
   d.ul_h = h->ws.ul_h;
+  d.ngroups = dec_down2_groups(d.d);
   // partial rows cost M x d x 4 bytes per sub-tile: they pay off for one
   // token; the column-chunk kernel's scattered loads grow with the union, so
   // from 5 tokens the split sequence (balanced, coalesced) takes over
@@ -763,6 +769,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.ud_waves = env_int("FFN_SPARSE_UD_WAVES");
   h->tune.no_decode = env_int("FFN_SPARSE_NO_DECODE");
   h->tune.dec_mode = env_int("FFN_SPARSE_DEC_MODE");
+  h->tune.no_pf = env_int("FFN_SPARSE_NO_PREFILL_GEMM");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;

@@ -612,6 +612,10 @@ inline dim3 gemm_grid(const GemmDesc& g) {
   return dim3(tiles * g.ks, (g.M + g.mt - 1) / g.mt);
 }
 
+// prefill-shaped GEMM (k_prefill.hip): 128 x 128 LDS-staged MFMA tiles for M >= 128
+bool pf_ok(const GemmDesc& g, const EpiDesc& e);
+hipError_t launch_gemm_pf(const GemmDesc& g, const EpiDesc& e, hipStream_t s);
+
 // entry points per epilogue group (each in its own translation unit)
 hipError_t launch_gemm_pack(const GemmDesc& g, const EpiDesc& e, hipStream_t s);    // STORE_F32, TWELL
 hipError_t launch_gemm_dense(const GemmDesc& g, const EpiDesc& e, hipStream_t s);   // WINA, DENSE_H, Y

@@ -36,6 +36,7 @@
 //                  128-byte line go to the same XCD (workgroups are dealt to
 //                  the eight XCDs round-robin), so its L2 serves the line to
 //                  all of them. An extra workgroup routes the pack.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.cuh"
@@ -603,11 +604,43 @@ __global__ __launch_bounds__(kRedThreads) void k_dec_reduce(const DecodeDesc d) 
 
 // ------------------------------------------------------------------ k_dec_up (split mode)
 // The union neurons (set bits of the sub-tile masks, ascending) are dealt to a
-// fixed grid in equal contiguous ranges, one wave per neuron: u = <W_up[n,:],
-// x_t> for every token, h = a * u (a from the gate kernel). Writes the compact
-// list (neuron, h per token) in union order and its length.
+// fixed grid in equal contiguous ranges; a wave takes two neurons at a time
+// (16 row loads per lane in flight): u = <W_up[n,:], x_t> for every token,
+// h = a * u (a from the gate kernel). Writes the compact list (neuron, h per
+// token) in union order and its length.
 constexpr int kUpWaves = 8;
-constexpr int kUpGrid = 256;
+constexpr int kUpGrid = 512;
+
+template <int MAXM>
+__device__ __forceinline__ void up_dot_store(const DecodeDesc& d, const uint4 (&w)[8], int pd, const uint16_t* s_x,
+                                             int n, int e, int lane) {
+  const int M = d.M, dm = d.d;
+  float a[MAXM];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) a[m] = m < M ? d.ad[(size_t)m * d.F + n] : 0.f;
+  float v[MAXM];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int col = c * 512 + lane * 8;
+      if (c < pd && col < dm) s = dot8_bf(w[c], *reinterpret_cast<const uint4*>(s_x + (size_t)m * dm + col), s);
+    }
+    v[m] = s;
+  }
+  WaveTRed<MAXM, 32>::run(v, lane);
+  constexpr int SH = 6 - Log2<MAXM>::value;
+  if ((lane & ((1 << SH) - 1)) == 0) {
+    const int m = lane >> SH;
+    float am = a[0];
+#pragma unroll
+    for (int q = 1; q < MAXM; ++q)
+      if (q == m) am = a[q];
+    d.ul_h[(size_t)e * kDecMaxM + m] = m < M ? am * v[0] : 0.f;
+  }
+  if (lane == 0) d.ul_nrn[e] = n;
+}
 
 template <int MAXM>
 __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
@@ -639,46 +672,31 @@ __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
   const int e0 = (int)((long long)total * blockIdx.x / gridDim.x);
   const int e1 = (int)((long long)total * (blockIdx.x + 1) / gridDim.x);
   const int pd = (dm + 511) / 512;
-  for (int e = e0 + wave; e < e1; e += kUpWaves) {
+  auto neuron_of = [&](int e) {
     int lo = 0, hi = nsub - 1;                     // last sub-tile with s_pre <= e
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pre[mid] <= e) lo = mid;
       else hi = mid - 1;
     }
-    const int n = lo * R + nth_set_bit(s_mask[lo], e - s_pre[lo]);
-    const uint16_t* row = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)n * dm;
-    uint4 w[8];
+    return lo * R + nth_set_bit(s_mask[lo], e - s_pre[lo]);
+  };
+  for (int ea = e0 + wave; ea < e1; ea += 2 * kUpWaves) {
+    const int eb = ea + kUpWaves;
+    const bool hb = eb < e1;
+    const int na = neuron_of(ea), nb = hb ? neuron_of(eb) : 0;
+    const uint16_t* ra = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)na * dm;
+    const uint16_t* rb = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)nb * dm;
+    uint4 wa[8], wb[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int col = c * 512 + lane * 8;
-      w[c] = (c < pd && col < dm) ? ldg16(row + col) : uint4{0, 0, 0, 0};
+      const bool ok = c < pd && col < dm;
+      wa[c] = ok ? ldg16(ra + col) : uint4{0, 0, 0, 0};
+      wb[c] = (ok && hb) ? ldg16(rb + col) : uint4{0, 0, 0, 0};
     }
-    float a[MAXM];
-#pragma unroll
-    for (int m = 0; m < MAXM; ++m) a[m] = m < M ? d.ad[(size_t)m * F + n] : 0.f;
-    float v[MAXM];
-#pragma unroll
-    for (int m = 0; m < MAXM; ++m) {
-      float s = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int col = c * 512 + lane * 8;
-        if (c < pd && col < dm) s = dot8_bf(w[c], *reinterpret_cast<const uint4*>(s_x + (size_t)m * dm + col), s);
-      }
-      v[m] = s;
-    }
-    WaveTRed<MAXM, 32>::run(v, lane);
-    constexpr int SH = 6 - Log2<MAXM>::value;
-    if ((lane & ((1 << SH) - 1)) == 0) {
-      const int m = lane >> SH;
-      float am = a[0];
-#pragma unroll
-      for (int q = 1; q < MAXM; ++q)
-        if (q == m) am = a[q];
-      d.ul_h[(size_t)e * kDecMaxM + m] = m < M ? am * v[0] : 0.f;
-    }
-    if (lane == 0) d.ul_nrn[e] = n;
+    up_dot_store<MAXM>(d, wa, pd, s_x, na, ea, lane);
+    if (hb) up_dot_store<MAXM>(d, wb, pd, s_x, nb, eb, lane);
   }
 }
 
@@ -691,7 +709,7 @@ __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
 // past it hold stale but valid neuron ids and are masked). Sums over the row
 // lanes are reduced across the wave (WaveTRed over the row-lane bits) and then
 // across the waves in order; the extra last workgroup routes the pack.
-constexpr int kDown2Waves = 16;
+constexpr int kDown2Threads = 256;
 
 // Halving steps of WaveTRed restricted to the lane bits >= OMIN. With H the
 // number of halving steps (log2 V, at most 6 - log2 OMIN), each lane keeps
@@ -720,24 +738,20 @@ struct WaveTRedHi {
   }
 };
 
-template <int MAXM, int LW>
-__global__ __launch_bounds__(64 * kDown2Waves) void k_dec_down2(const DecodeDesc d) {
-  constexpr int NT = 64 * kDown2Waves, RL = NT / LW;
+template <int MAXM>
+__global__ __launch_bounds__(kDown2Threads) void k_dec_down2(const DecodeDesc d) {
+  constexpr int LW = 8;                                 // 16-byte chunks per slice (128 bytes)
+  constexpr int NW = kDown2Threads / 64, RL = kDown2Threads / LW;
   constexpr int B = MAXM <= 2 ? 8 : 4;                  // entries in flight per thread
   constexpr int V = 8 * MAXM;                           // sums per thread
   constexpr int STEPS = 6 - Log2<LW>::value;            // row-lane bits of a wave
   constexpr int H = Log2<V>::value < STEPS ? Log2<V>::value : STEPS;   // halving steps
   constexpr int KEEP = V >> H;                          // sums each lane keeps
-  __shared__ float s_red[kDown2Waves][LW][V];
-  const int nsl = d.d / (8 * LW);
-  if (d.route_pass && (int)blockIdx.x == nsl) {
-    route_pass(d.route);
-    return;
-  }
+  __shared__ float s_red[NW][LW][V];
+  const int nsl = d.d / (8 * LW), S = d.ngroups;
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int q = tid % LW, rl = tid / LW;
-  const int b = blockIdx.x;
-  const int sl = (nsl % 8 == 0) ? (b & 7) * (nsl >> 3) + (b >> 3) : b;   // neighbouring slices share an XCD
+  const int b = blockIdx.x, g = b % S, sl = b / S;     // the S groups of a slice are neighbours
   const int M = d.M, F = d.F;
   const uint16_t* wd = reinterpret_cast<const uint16_t*>(d.w_down_nm) + (size_t)sl * 8 * LW + q * 8;
   float acc[MAXM][8];
@@ -745,27 +759,29 @@ __global__ __launch_bounds__(64 * kDown2Waves) void k_dec_down2(const DecodeDesc
   for (int m = 0; m < MAXM; ++m)
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[m][k] = 0.f;
+  // entries g + S * (rl + RL * i): the list length is read in the same round
+  // as the first entries (slots past it hold stale but valid ids, masked)
   int total = F;
-  for (int e0 = rl; e0 < total; e0 += RL * B) {
+  for (int j0 = rl; g + S * j0 < total; j0 += RL * B) {
     int nrn[B];
     float h[B][MAXM];
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      const int e = e0 + i * RL;
+      const int e = g + S * (j0 + RL * i);
       nrn[i] = e < F ? d.ul_nrn[e] : 0;
 #pragma unroll
       for (int m = 0; m < MAXM; ++m) h[i][m] = (e < F && m < M) ? d.ul_h[(size_t)e * kDecMaxM + m] : 0.f;
     }
-    if (e0 == rl) total = *d.ul_total;
+    if (j0 == rl) total = *d.ul_total;
     uint4 w[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      const int e = e0 + i * RL;
+      const int e = g + S * (j0 + RL * i);
       w[i] = e < total ? ldg16(wd + (size_t)nrn[i] * d.d) : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      const int e = e0 + i * RL;
+      const int e = g + S * (j0 + RL * i);
       if (e < total) {
         float f[8];
         unpack8(w[i], f);
@@ -790,13 +806,35 @@ __global__ __launch_bounds__(64 * kDown2Waves) void k_dec_down2(const DecodeDesc
     }
   }
   __syncthreads();
-  for (int o = tid; o < LW * V; o += NT) {
+  for (int o = tid; o < LW * V; o += kDown2Threads) {
     const int qq = o / V, j = o % V, m = j / 8, k = j % 8;
     float s = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kDown2Waves; ++w2) s += s_red[w2][qq][j];
-    if (m < M) reinterpret_cast<uint16_t*>(d.y)[(size_t)m * d.d + (size_t)sl * 8 * LW + qq * 8 + k] = (uint16_t)f2bf(s);
+    for (int w2 = 0; w2 < NW; ++w2) s += s_red[w2][qq][j];
+    if (m < M) d.part[((size_t)g * M + m) * d.d + (size_t)sl * 8 * LW + qq * 8 + k] = s;
   }
+}
+
+// y = sum of the S group partials in group order; the extra last workgroup
+// routes the pack.
+__global__ __launch_bounds__(256) void k_dec_reduce2(const DecodeDesc d) {
+  const int n = d.M * d.d;
+  if (d.route_pass && (int)blockIdx.x == (n + 1023) / 1024) {
+    route_pass(d.route);
+    return;
+  }
+  const int i0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < d.ngroups; ++g) {
+    const float4 p = *reinterpret_cast<const float4*>(d.part + (size_t)g * n + i0);
+    acc.x += p.x;
+    acc.y += p.y;
+    acc.z += p.z;
+    acc.w += p.w;
+  }
+  uint16_t* y = reinterpret_cast<uint16_t*>(d.y) + i0;
+  *reinterpret_cast<uint2*>(y) = uint2{f2bf(acc.x) | (f2bf(acc.y) << 16), f2bf(acc.z) | (f2bf(acc.w) << 16)};
 }
 
 // ------------------------------------------------------------------ launches
@@ -932,26 +970,24 @@ hipError_t launch_dec_up(const DecodeDesc& d, hipStream_t s) {
   }
 }
 
-// slices of 64 bytes when that still leaves >= 64 workgroups, else 128 bytes
-template <int MAXM>
-static hipError_t go_down2(const DecodeDesc& d, hipStream_t s) {
-  const int extra = d.route_pass ? 1 : 0;
-  if (d.d / 32 >= 64) {
-    hipLaunchKernelGGL((k_dec_down2<MAXM, 4>), dim3(d.d / 32 + extra), dim3(64 * kDown2Waves), 0, s, d);
-  } else {
-    hipLaunchKernelGGL((k_dec_down2<MAXM, 8>), dim3(d.d / 64 + extra), dim3(64 * kDown2Waves), 0, s, d);
-  }
-  return hipGetLastError();
-}
+int dec_down2_groups(int d_model) { return std::max(1, std::min(32, 1024 / (d_model / 64))); }
 
 hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s) {
-  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || !d.ul_nrn || !d.ul_h || !d.ul_total) return hipErrorInvalidValue;
+  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || !d.ul_nrn || !d.ul_h || !d.ul_total || !d.part ||
+      d.ngroups != dec_down2_groups(d.d))
+    return hipErrorInvalidValue;
+  const dim3 grid(d.d / 64 * d.ngroups), blk(kDown2Threads);
   switch (dec_maxm(d.M)) {
-    case 1: return go_down2<1>(d, s);
-    case 2: return go_down2<2>(d, s);
-    case 4: return go_down2<4>(d, s);
-    default: return go_down2<8>(d, s);
+    case 1: hipLaunchKernelGGL((k_dec_down2<1>), grid, blk, 0, s, d); break;
+    case 2: hipLaunchKernelGGL((k_dec_down2<2>), grid, blk, 0, s, d); break;
+    case 4: hipLaunchKernelGGL((k_dec_down2<4>), grid, blk, 0, s, d); break;
+    default: hipLaunchKernelGGL((k_dec_down2<8>), grid, blk, 0, s, d); break;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = d.M * d.d;
+  hipLaunchKernelGGL(k_dec_reduce2, dim3((n + 1023) / 1024 + (d.route_pass ? 1 : 0)), dim3(256), 0, s, d);
+  return hipGetLastError();
 }
 
 int dec_rows_per_wg(int K, int T, int m, int* ipw_out) {

@@ -35,6 +35,7 @@ struct GemmDesc {
   int gemv;               // decode GEMV (VALU) instead of MFMA tiles (bf16, M <= 8)
   int ks;                 // workgroups splitting K; each writes its own output slab (>= 1)
   const uint32_t* ctrl;   // control block (epoch of the look-back words)
+  int no_pf;              // 1: never the prefill-shaped kernel (tuning switch)
 };
 
 struct EpiDesc {
@@ -164,6 +165,7 @@ struct DecodeDesc {
   int32_t* ul_total;           // [1] split mode: union-list length
   int32_t* ul_nrn;             // [F] split mode: union neurons, ascending (compact)
   float* ul_h;                 // [F x 8] split mode: h per token of each list entry
+  int ngroups;                 // split mode: entry groups of the down kernel (partials in part)
   int route_pass;              // k_dec_down: the last workgroup routes the pack
   RouteDesc route;
 };
@@ -181,7 +183,8 @@ hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_up(const DecodeDesc& d, hipStream_t s);
 size_t dec_up_lds(const DecodeDesc& d);
-hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s);
+hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s);   // + the group-partial sum
+int dec_down2_groups(int d_model);
 // Gate rows per decode workgroup for a gate contraction length K, TwELL tile
 // width T and m tokens (0 when the decode shape does not apply).
 int dec_rows_per_wg(int K, int T, int m, int* ipw);

@@ -289,3 +289,41 @@ def test_graph_replay_matches_eager():
         assert np.array_equal(host(y), eager)
         ffn.forward(x, pack=pack, y=y, **kw)      # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# prefill-shaped GEMMs (128+ tokens): several 128-token tiles, a ragged last
+# tile, the dense backup on a gathered token list, the dense baseline
+# ---------------------------------------------------------------------------
+
+PREFILL = [
+    ("c5", 300, dict(d=256, f=2048, T=256, E=32)),
+    ("c2", 200, dict(d=512, f=1024, T=128, E=16)),
+    ("c4", 160, dict(d=256, f=768, T=128, E=128)),
+]
+
+
+@pytest.mark.parametrize("cid,m,kw", PREFILL, ids=[f"{c}-m{m}" for c, m, _ in PREFILL])
+def test_prefill_shapes(cid, m, kw):
+    say("prefill", cid, m, kw)
+    import os
+    import torch
+    wl = make_workload(cid, m, 0, **kw)
+    ref = O.forward(wl)
+    run_full(wl, ref)
+    # the same pack and y (within tolerance) without the prefill-shaped kernel
+    os.environ["FFN_SPARSE_NO_PREFILL_GEMM"] = "1"
+    try:
+        ffn = make_ffn(wl)
+    finally:
+        os.environ.pop("FFN_SPARSE_NO_PREFILL_GEMM", None)
+    y2, pack2 = ffn.forward(to_dev(wl, wl.x), **sel_args(wl))
+    torch.cuda.synchronize()
+    check_pack(wl, pack2, ref)
+    check_y(y_to_f64(wl, y2)[: wl.m], ref["y"])
+    if wl.sel != "topk":
+        kw2 = sel_args(wl)
+        kw2.pop("k", None)
+        yd = make_ffn(wl).dense_forward(to_dev(wl, wl.x), **kw2)
+        torch.cuda.synchronize()
+        check_y(y_to_f64(wl, yd)[: wl.m], O.dense_forward(wl))
