@@ -61,16 +61,27 @@ __device__ __forceinline__ void epi_store_f32(const EpiDesc& e, const TileView& 
   }
 }
 
-// TwELL emission: one wave per token slot; the tile covers nt neurons
-// [n0, n0 + nt), sub-tile q of TwELL tile j (Q = T / nt). Active neurons are
-// compacted in ascending order with a ballot + prefix popcount.
+// TwELL emission: the tile covers nt neurons [n0, n0 + nt), sub-tile q of
+// TwELL tile j (Q = T / nt). Three block-wide phases, so that the look-back
+// costs one memory round for the whole tile rather than one per token:
+//   1. one wave per token slot counts the active neurons (ballot + popcount)
+//      and publishes the count (epoch-tagged word) when Q > 1;
+//   2. every (token, earlier sub-tile) pair is read by one thread, waiting
+//      for this pass's epoch, and added into the token's offset in LDS;
+//   3. one wave per token slot writes its entries in ascending order at that
+//      offset (ballot + prefix popcount), and the last sub-tile writes cnt and
+//      the padding.
+constexpr int kTwellMaxSlots = 128;
 __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, const uint32_t* ctrl) {
+  __shared__ int s_off[kTwellMaxSlots];
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int Q = e.T / v.nt, q = (v.n0 % e.T) / v.nt, j = v.n0 / e.T;
   const int ntiles = e.F / e.T, nsub = e.F / v.nt;
   // pass epoch of the look-back words (advanced by the routing pass after
   // every gate pass); only sub-tiled TwELL tiles need it
   const uint32_t epoch = Q > 1 ? __hip_atomic_load(&ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
+  for (int m = threadIdx.x; m < v.mcnt; m += blockDim.x) s_off[m] = 0;
+  // phase 1
   for (int m = wave; m < v.mcnt; m += nw) {
     const int tok = v.m0 + m;
     const float b = bias_of(e, tok), cut = cut_of(e, tok);
@@ -85,19 +96,26 @@ __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, c
       }
       c_local += __popcll(ballot64(act));
     }
-    int P = 0;
-    if (Q > 1) {
-      uint64_t* words = e.lb + (size_t)tok * nsub + (size_t)j * Q;
-      if (lane == 0) store64_relaxed(words + q, ((uint64_t)epoch << 32) | (uint32_t)c_local);
-      int pv = 0;
-      if (lane < q) {
-        uint64_t w;
-        while (((w = load64_relaxed(words + lane)) >> 32) != epoch) __builtin_amdgcn_s_sleep(1);
-        pv = (int)(uint32_t)w;
-      }
-      P = wave_sum_i(pv);
+    if (Q > 1 && lane == 0)
+      store64_relaxed(e.lb + (size_t)tok * nsub + (size_t)j * Q + q, ((uint64_t)epoch << 32) | (uint32_t)c_local);
+  }
+  __syncthreads();
+  // phase 2
+  if (Q > 1 && q > 0) {
+    for (int p = threadIdx.x; p < v.mcnt * q; p += blockDim.x) {
+      const int m = p / q, pp = p - m * q;
+      const uint64_t* wp = e.lb + (size_t)(v.m0 + m) * nsub + (size_t)j * Q + pp;
+      uint64_t w;
+      while (((w = load64_relaxed(wp)) >> 32) != epoch) __builtin_amdgcn_s_sleep(1);
+      atomicAdd(&s_off[m], (int)(uint32_t)w);
     }
-    int run = P;
+  }
+  __syncthreads();
+  // phase 3
+  for (int m = wave; m < v.mcnt; m += nw) {
+    const int tok = v.m0 + m;
+    const float b = bias_of(e, tok), cut = cut_of(e, tok);
+    int run = s_off[m];
     const size_t slot0 = ((size_t)tok * ntiles + j) * e.E;
     for (int c0 = 0; c0 < v.nt; c0 += 64) {
       const int r = c0 + lane;
@@ -123,6 +141,7 @@ __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, c
       }
     }
   }
+  __syncthreads();                                  // s_off is reused by the next call
 }
 
 // rows [0, rpm) of the tile are the gate, [rpm, 2 rpm) the up projection of
