@@ -15,6 +15,10 @@
 
 using namespace ffn;
 
+namespace ffn {
+thread_local LaunchEvents tl_launch_events = {nullptr, nullptr};
+}  // namespace ffn
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -181,20 +185,21 @@ struct ffn_sparse_handle {
 
 namespace {
 
+// Per-kernel timing: the next kernel launched in the scope records the pair
+// of events from its own dispatch (see ffn_launch); a scope that launched
+// nothing records nothing.
 struct Timed {
   ffn_sparse_handle* h;
   int kind;
-  hipStream_t s;
   bool on;
-  Timed(ffn_sparse_handle* hh, int k, hipStream_t st) : h(hh), kind(k), s(st) {
+  Timed(ffn_sparse_handle* hh, int k, hipStream_t) : h(hh), kind(k) {
     on = h->timing && h->used[kind] < h->cap;
-    if (on) (void)hipEventRecord(h->ev[kind][0][h->used[kind]], s);
+    if (on) tl_launch_events = LaunchEvents{h->ev[kind][0][h->used[kind]], h->ev[kind][1][h->used[kind]]};
   }
   ~Timed() {
-    if (on) {
-      (void)hipEventRecord(h->ev[kind][1][h->used[kind]], s);
-      h->used[kind]++;
-    }
+    if (!on) return;
+    if (tl_launch_events.start == nullptr) h->used[kind]++;   // a launch took the events
+    else tl_launch_events = LaunchEvents{nullptr, nullptr};
   }
 };
 

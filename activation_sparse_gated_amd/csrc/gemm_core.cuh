@@ -474,7 +474,7 @@ static hipError_t go_gemv_1(const GemmDesc& g, const EpiDesc& e, dim3 grid, hipS
   if constexpr (NKC * MAXM * (BF32 ? 2 : 1) > 32) {
     return hipErrorInvalidValue;
   } else {
-    hipLaunchKernelGGL((k_gemv_bf16<NW, MAXM, NKC, BF32, NMAT, EPI>), grid, dim3(64 * NW), 0, s, g, e);
+    ffn_launch((k_gemv_bf16<NW, MAXM, NKC, BF32, NMAT, EPI>), grid, dim3(64 * NW), 0, s, g, e);
     return hipGetLastError();
   }
 }
@@ -571,15 +571,15 @@ static hipError_t go_bf16(const GemmDesc& g, const EpiDesc& e, dim3 grid, hipStr
   const dim3 blk(64 * WN * WK);
   if (BM == B_F32_SPLIT) {
     switch (g.b_nsum) {
-      case 1: hipLaunchKernelGGL((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 1>), grid, blk, 0, s, g, e); break;
-      case 2: hipLaunchKernelGGL((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 2>), grid, blk, 0, s, g, e); break;
-      case 4: hipLaunchKernelGGL((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 4>), grid, blk, 0, s, g, e); break;
-      case 8: hipLaunchKernelGGL((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 8>), grid, blk, 0, s, g, e); break;
+      case 1: ffn_launch((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 1>), grid, blk, 0, s, g, e); break;
+      case 2: ffn_launch((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 2>), grid, blk, 0, s, g, e); break;
+      case 4: ffn_launch((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 4>), grid, blk, 0, s, g, e); break;
+      case 8: ffn_launch((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 8>), grid, blk, 0, s, g, e); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     if (g.b_nsum != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 1>), grid, blk, 0, s, g, e);
+    ffn_launch((k_gemm_bf16<RB, WN, WK, MB, BM, NMAT, EPI, 1>), grid, blk, 0, s, g, e);
   }
   return hipGetLastError();
 }
@@ -618,9 +618,9 @@ static hipError_t pick_shape(const GemmDesc& g, const EpiDesc& e, dim3 grid, hip
 template <int NMAT, int EPI>
 static hipError_t go_f32(const GemmDesc& g, const EpiDesc& e, dim3 grid, hipStream_t s) {
   switch (g.nt) {
-    case 16: if (NMAT == 1) { hipLaunchKernelGGL((k_gemm_f32<16, NMAT, EPI>), grid, dim3(256), 0, s, g, e); return hipGetLastError(); } break;
-    case 32: hipLaunchKernelGGL((k_gemm_f32<32, NMAT, EPI>), grid, dim3(256), 0, s, g, e); return hipGetLastError();
-    case 64: hipLaunchKernelGGL((k_gemm_f32<64, NMAT, EPI>), grid, dim3(256), 0, s, g, e); return hipGetLastError();
+    case 16: if (NMAT == 1) { ffn_launch((k_gemm_f32<16, NMAT, EPI>), grid, dim3(256), 0, s, g, e); return hipGetLastError(); } break;
+    case 32: ffn_launch((k_gemm_f32<32, NMAT, EPI>), grid, dim3(256), 0, s, g, e); return hipGetLastError();
+    case 64: ffn_launch((k_gemm_f32<64, NMAT, EPI>), grid, dim3(256), 0, s, g, e); return hipGetLastError();
   }
   return hipErrorInvalidValue;
 }

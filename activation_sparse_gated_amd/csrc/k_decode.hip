@@ -863,7 +863,7 @@ static hipError_t go_lowrank(const DecodeDesc& d, hipStream_t s) {
   const size_t lds = dec_lowrank_lds(d);
   hipError_t e = lds_attr(k_dec_lowrank<IPW, MAXM>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_lowrank<IPW, MAXM>), dim3((d.rank + R - 1) / R), dim3(64 * kDecVWaves), lds, s, d);
+  ffn_launch((k_dec_lowrank<IPW, MAXM>), dim3((d.rank + R - 1) / R), dim3(64 * kDecVWaves), lds, s, d);
   return hipGetLastError();
 }
 
@@ -895,7 +895,7 @@ static hipError_t go_gate_k(const DecodeDesc& d, hipStream_t s) {
   const size_t lds = dec_gate_lds(d);
   hipError_t e = lds_attr(k_dec_gate<NW, IPW, MAXM, LOWRANK, MODE>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_gate<NW, IPW, MAXM, LOWRANK, MODE>), dim3(d.F / d.R), dim3(64 * NW), lds, s, d);
+  ffn_launch((k_dec_gate<NW, IPW, MAXM, LOWRANK, MODE>), dim3(d.F / d.R), dim3(64 * NW), lds, s, d);
   return hipGetLastError();
 }
 
@@ -940,10 +940,10 @@ hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s) {
   if (d.M < 1 || d.M > kDecMaxM || d.d % 32 != 0 || d.F / d.R > kDecMaxSub || !d.part) return hipErrorInvalidValue;
   const dim3 grid(d.d / 32 + (d.route_pass ? 1 : 0)), blk(kRedThreads);
   switch (dec_maxm(d.M)) {
-    case 1: hipLaunchKernelGGL((k_dec_reduce<1>), grid, blk, 0, s, d); break;
-    case 2: hipLaunchKernelGGL((k_dec_reduce<2>), grid, blk, 0, s, d); break;
-    case 4: hipLaunchKernelGGL((k_dec_reduce<4>), grid, blk, 0, s, d); break;
-    default: hipLaunchKernelGGL((k_dec_reduce<8>), grid, blk, 0, s, d); break;
+    case 1: ffn_launch((k_dec_reduce<1>), grid, blk, 0, s, d); break;
+    case 2: ffn_launch((k_dec_reduce<2>), grid, blk, 0, s, d); break;
+    case 4: ffn_launch((k_dec_reduce<4>), grid, blk, 0, s, d); break;
+    default: ffn_launch((k_dec_reduce<8>), grid, blk, 0, s, d); break;
   }
   return hipGetLastError();
 }
@@ -955,7 +955,7 @@ static hipError_t go_up(const DecodeDesc& d, hipStream_t s) {
   const size_t lds = dec_up_lds(d);
   hipError_t e = lds_attr(k_dec_up<MAXM>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_up<MAXM>), dim3(kUpGrid), dim3(64 * kUpWaves), lds, s, d);
+  ffn_launch((k_dec_up<MAXM>), dim3(kUpGrid), dim3(64 * kUpWaves), lds, s, d);
   return hipGetLastError();
 }
 
@@ -978,15 +978,15 @@ hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 grid(d.d / 64 * d.ngroups), blk(kDown2Threads);
   switch (dec_maxm(d.M)) {
-    case 1: hipLaunchKernelGGL((k_dec_down2<1>), grid, blk, 0, s, d); break;
-    case 2: hipLaunchKernelGGL((k_dec_down2<2>), grid, blk, 0, s, d); break;
-    case 4: hipLaunchKernelGGL((k_dec_down2<4>), grid, blk, 0, s, d); break;
-    default: hipLaunchKernelGGL((k_dec_down2<8>), grid, blk, 0, s, d); break;
+    case 1: ffn_launch((k_dec_down2<1>), grid, blk, 0, s, d); break;
+    case 2: ffn_launch((k_dec_down2<2>), grid, blk, 0, s, d); break;
+    case 4: ffn_launch((k_dec_down2<4>), grid, blk, 0, s, d); break;
+    default: ffn_launch((k_dec_down2<8>), grid, blk, 0, s, d); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = d.M * d.d;
-  hipLaunchKernelGGL(k_dec_reduce2, dim3((n + 1023) / 1024 + (d.route_pass ? 1 : 0)), dim3(256), 0, s, d);
+  ffn_launch(k_dec_reduce2, dim3((n + 1023) / 1024 + (d.route_pass ? 1 : 0)), dim3(256), 0, s, d);
   return hipGetLastError();
 }
 
@@ -1008,10 +1008,10 @@ hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s) {
   if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || d.F / d.R > kDecMaxSub) return hipErrorInvalidValue;
   const dim3 grid(d.d / 8 + (d.route_pass ? 1 : 0)), blk(kDownThreads);
   switch (dec_maxm(d.M)) {
-    case 1: hipLaunchKernelGGL((k_dec_down<1>), grid, blk, 0, s, d); break;
-    case 2: hipLaunchKernelGGL((k_dec_down<2>), grid, blk, 0, s, d); break;
-    case 4: hipLaunchKernelGGL((k_dec_down<4>), grid, blk, 0, s, d); break;
-    default: hipLaunchKernelGGL((k_dec_down<8>), grid, blk, 0, s, d); break;
+    case 1: ffn_launch((k_dec_down<1>), grid, blk, 0, s, d); break;
+    case 2: ffn_launch((k_dec_down<2>), grid, blk, 0, s, d); break;
+    case 4: ffn_launch((k_dec_down<4>), grid, blk, 0, s, d); break;
+    default: ffn_launch((k_dec_down<8>), grid, blk, 0, s, d); break;
   }
   return hipGetLastError();
 }

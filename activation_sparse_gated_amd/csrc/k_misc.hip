@@ -25,9 +25,9 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T*
 hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int esize, hipStream_t s) {
   dim3 grid((cols + 63) / 64, (rows + 63) / 64);
   if (esize == 2)
-    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src, (uint16_t*)dst, rows, cols);
+    ffn_launch(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src, (uint16_t*)dst, rows, cols);
   else
-    hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s, (const float*)src, (float*)dst, rows, cols);
+    ffn_launch(k_transpose<float>, grid, dim3(256), 0, s, (const float*)src, (float*)dst, rows, cols);
   return hipGetLastError();
 }
 
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void k_rownorm(const void* __restrict__ w, flo
 }
 
 hipError_t launch_rownorm(const void* w, float* c, int F, int d, int dtype, hipStream_t s) {
-  hipLaunchKernelGGL(k_rownorm, dim3((F + 3) / 4), dim3(256), 0, s, w, c, F, d, dtype);
+  ffn_launch(k_rownorm, dim3((F + 3) / 4), dim3(256), 0, s, w, c, F, d, dtype);
   return hipGetLastError();
 }
 
@@ -69,7 +69,7 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   int blocks = (int)((n + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, s, p, v, n);
+  ffn_launch(k_fill_u32, dim3(blocks), dim3(256), 0, s, p, v, n);
   return hipGetLastError();
 }
 

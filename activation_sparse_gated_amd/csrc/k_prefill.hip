@@ -143,7 +143,7 @@ bool pf_ok(const GemmDesc& g, const EpiDesc& e) {
 template <int NMAT, int EPI>
 static hipError_t go_pf(const GemmDesc& g, const EpiDesc& e, hipStream_t s) {
   const dim3 grid(g.nrows * g.nmat / PF_BN, (g.M + PF_BM - 1) / PF_BM);
-  hipLaunchKernelGGL((k_gemm_pf<NMAT, EPI>), grid, dim3(PF_THREADS), 0, s, g, e);
+  ffn_launch((k_gemm_pf<NMAT, EPI>), grid, dim3(PF_THREADS), 0, s, g, e);
   return hipGetLastError();
 }
 

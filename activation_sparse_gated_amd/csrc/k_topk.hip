@@ -113,7 +113,7 @@ hipError_t launch_topk(const TopkDesc& d, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_topk, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
+  ffn_launch(k_topk, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ struct ElemTraits<DT_F32> {
 __global__ __launch_bounds__(256) void k_route(const RouteDesc r) { route_pass(r); }
 
 hipError_t launch_route(const RouteDesc& r, hipStream_t s) {
-  hipLaunchKernelGGL(k_route, dim3(1), dim3(256), 0, s, r);
+  ffn_launch(k_route, dim3(1), dim3(256), 0, s, r);
   return hipGetLastError();
 }
 
@@ -361,8 +361,8 @@ __global__ __launch_bounds__(64 * RED_GROUPS) void k_ud_reduce(const UpdownDesc 
 template <int DT>
 static hipError_t go_updown(const UpdownDesc& u, hipStream_t s) {
   dim3 grid(u.M * ud_groups(u) * u.slot_split + (u.route_pass ? 1 : 0));
-  if (u.nwaves == 8) hipLaunchKernelGGL((k_updown<DT, 8>), grid, dim3(512), 0, s, u);
-  else hipLaunchKernelGGL((k_updown<DT, 4>), grid, dim3(256), 0, s, u);
+  if (u.nwaves == 8) ffn_launch((k_updown<DT, 8>), grid, dim3(512), 0, s, u);
+  else ffn_launch((k_updown<DT, 4>), grid, dim3(256), 0, s, u);
   return hipGetLastError();
 }
 
@@ -377,8 +377,8 @@ hipError_t launch_updown(const UpdownDesc& u, hipStream_t s) {
 hipError_t launch_updown_reduce(const UpdownDesc& u, hipStream_t s) {
   if (u.M <= 0 || ud_groups(u) * u.slot_split == 1) return hipSuccess;
   dim3 grid((u.d + 63) / 64, u.M);
-  if (u.dtype == DT_BF16) hipLaunchKernelGGL(k_ud_reduce<DT_BF16>, grid, dim3(64 * RED_GROUPS), 0, s, u);
-  else hipLaunchKernelGGL(k_ud_reduce<DT_F32>, grid, dim3(64 * RED_GROUPS), 0, s, u);
+  if (u.dtype == DT_BF16) ffn_launch(k_ud_reduce<DT_BF16>, grid, dim3(64 * RED_GROUPS), 0, s, u);
+  else ffn_launch(k_ud_reduce<DT_F32>, grid, dim3(64 * RED_GROUPS), 0, s, u);
   return hipGetLastError();
 }
 

@@ -1,9 +1,26 @@
 // Internal interface between the C ABI layer and the kernel translation units.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace ffn {
+
+// Events the next kernel launched through ffn_launch on this host thread
+// records from its own dispatch (its start and end timestamps, as a profiler
+// sees them); cleared once used. Set by the per-kernel timing of the C ABI.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+extern thread_local LaunchEvents tl_launch_events;
+
+// Every kernel of the library is launched here.
+template <typename F, typename... Args>
+inline void ffn_launch(F kernel, const dim3& grid, const dim3& block, size_t lds, hipStream_t s, Args... args) {
+  const LaunchEvents ev = tl_launch_events;
+  tl_launch_events = LaunchEvents{nullptr, nullptr};
+  hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
+}
 
 enum Dtype : int { DT_F32 = 0, DT_BF16 = 1 };
 enum Act : int { ACT_RELU = 0, ACT_SILU = 1 };
