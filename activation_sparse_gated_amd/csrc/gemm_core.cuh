@@ -74,17 +74,24 @@ __device__ __forceinline__ void epi_store_f32(const EpiDesc& e, const TileView& 
 constexpr int kTwellMaxSlots = 128;
 __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, const uint32_t* ctrl) {
   __shared__ int s_off[kTwellMaxSlots];
+  __shared__ float s_bias[kTwellMaxSlots], s_cut[kTwellMaxSlots];
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int Q = e.T / v.nt, q = (v.n0 % e.T) / v.nt, j = v.n0 / e.T;
   const int ntiles = e.F / e.T, nsub = e.F / v.nt;
   // pass epoch of the look-back words (advanced by the routing pass after
   // every gate pass); only sub-tiled TwELL tiles need it
   const uint32_t epoch = Q > 1 ? __hip_atomic_load(&ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
-  for (int m = threadIdx.x; m < v.mcnt; m += blockDim.x) s_off[m] = 0;
+  // every token's bias and cut, read in one parallel round
+  for (int m = threadIdx.x; m < v.mcnt; m += blockDim.x) {
+    s_off[m] = 0;
+    s_bias[m] = bias_of(e, v.m0 + m);
+    s_cut[m] = cut_of(e, v.m0 + m);
+  }
+  __syncthreads();
   // phase 1
   for (int m = wave; m < v.mcnt; m += nw) {
     const int tok = v.m0 + m;
-    const float b = bias_of(e, tok), cut = cut_of(e, tok);
+    const float b = s_bias[m], cut = s_cut[m];
     int c_local = 0;
     for (int c0 = 0; c0 < v.nt; c0 += 64) {
       const int r = c0 + lane;
@@ -114,7 +121,7 @@ __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, c
   // phase 3
   for (int m = wave; m < v.mcnt; m += nw) {
     const int tok = v.m0 + m;
-    const float b = bias_of(e, tok), cut = cut_of(e, tok);
+    const float b = s_bias[m], cut = s_cut[m];
     int run = s_off[m];
     const size_t slot0 = ((size_t)tok * ntiles + j) * e.E;
     for (int c0 = 0; c0 < v.nt; c0 += 64) {
