@@ -283,7 +283,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{WORKLOADS[cid]} m={m}", "d_model": d, "d_ff": F, "rank": r, "m": m,
-                   "tile_w": T, "ell_w": E, "active_neurons": n_union, "layers_rotated": len(layers),
+                   "tile_w": T, "ell_w": E, "active_neurons": n_union, "routed_tokens": n_dense,
+                   "layers_rotated": len(layers),
                    "hip_graph": bool(args.graph), "kernel_path": path},
         "effective_hbm_GBps": round(touched / (ms_sparse * 1e-3) / 1e9, 1),
         "touched_bytes": int(touched),
