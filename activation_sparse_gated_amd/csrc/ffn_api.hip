@@ -72,7 +72,7 @@ struct Workspace {
   float* dec_part;       // [F / R x min(max_m, 8) x d] decode partial y rows
   int32_t* ul_total;     // [1] decode split mode: union-list length
   int32_t* ul_nrn;       // [F] decode split mode: union neurons
-  float* ul_h;           // [F x kDecMaxM] decode split mode: h per token
+  float* ul_h;           // decode split mode: hT, bf16 [kDecMaxM][F rounded up to 32]
   size_t total;
 };
 
@@ -128,7 +128,7 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
   }
   w.ul_total = (int32_t*)take(sizeof(int32_t));
   w.ul_nrn = (int32_t*)take(F * sizeof(int32_t));
-  w.ul_h = (float*)take(F * kDecMaxM * sizeof(float));
+  w.ul_h = (float*)take((size_t)kDecMaxM * ((F + 31) / 32 * 32) * sizeof(uint16_t));
   w.total = off;
   return w;
 }
@@ -596,13 +596,15 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.ul_total = h->ws.ul_total;
   d.ul_nrn = h->ws.ul_nrn;
   d.ul_h = h->ws.ul_h;
-  d.ngroups = dec_down2_groups(d.d);
+  d.ngroups = dec_down2_groups(d.d, d.F);
+  d.ldh = (d.F + 31) / 32 * 32;
   // partial rows cost M x d x 4 bytes per sub-tile: they pay off for one
-  // token; the column-chunk kernel's scattered loads grow with the union, so
-  // from 5 tokens the split sequence (balanced, coalesced) takes over
-  d.mode = m == 1 ? DEC_PART : (m <= 4 ? DEC_CHUNK : DEC_SPLIT);
+  // token; from two tokens the split sequence (union list dealt evenly over
+  // the chip, up and down products on matrix cores) is faster than the
+  // column-chunk kernel, whose scattered loads grow with the union
+  d.mode = m == 1 ? DEC_PART : DEC_SPLIT;
   if (h->tune.dec_mode >= 1 && h->tune.dec_mode <= 3) d.mode = h->tune.dec_mode - 1;
-  if (d.mode == DEC_SPLIT && dec_up_lds(d) + 25 * 1024 > (size_t)h->lds_max) d.mode = DEC_CHUNK;
+  if (d.mode == DEC_SPLIT && !dec_split_ok(d)) d.mode = DEC_CHUNK;
   *out = d;
   return true;
 }

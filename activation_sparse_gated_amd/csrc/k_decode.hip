@@ -603,56 +603,46 @@ __global__ __launch_bounds__(kRedThreads) void k_dec_reduce(const DecodeDesc d) 
 }
 
 // ------------------------------------------------------------------ k_dec_up (split mode)
-// The union neurons (set bits of the sub-tile masks, ascending) are dealt to a
-// fixed grid in equal contiguous ranges; a wave takes two neurons at a time
-// (16 row loads per lane in flight): u = <W_up[n,:], x_t> for every token,
-// h = a * u (a from the gate kernel). Writes the compact list (neuron, h per
-// token) in union order and its length.
+// The union neurons (set bits of the sub-tile masks, ascending) form the list;
+// workgroup b of the G in the grid takes the list entries [b U / G,
+// (b + 1) U / G) (U the list length), so every workgroup streams the same
+// number of W_up rows. Its entries form up to three groups of 16 rows whose
+// up products are a small dense contraction, 16 rows x d by d x M tokens, on
+// v_mfma_f32_16x16x32_bf16: wave w owns the contiguous eighth of d, step j of
+// it covering 32 elements. Operand lane l holds row l % 16 at the 16-byte
+// chunk 4 j + l / 16, so one load instruction reads 64 contiguous bytes of each
+// of the 16 rows and two consecutive steps a whole 128-byte line; all loads of
+// the workgroup's groups are issued before the first product. The tokens' x
+// (B operand) sits in LDS, one row per token padded by 16 bytes so that the
+// eight tokens of a read fall in distinct banks. The eight waves' partial
+// 16 x 16 tiles are summed in LDS in wave order; h = a * u is stored as bf16 in
+// token-major rows hT[token][entry], the neuron ids in the list. The last
+// workgroup zeroes the entries from U up to the next multiple of 32, which the
+// down kernel reads whole.
 constexpr int kUpWaves = 8;
-constexpr int kUpGrid = 512;
+constexpr int kUpGrid = 256;
+constexpr int kUpMaxSteps = 16;                        // 32-element steps per wave (d <= 4096)
+constexpr int kUpNB = 3;                               // groups of 16 entries in flight
+constexpr int kUpMaxEnt = 128;                         // entries per workgroup (F <= 128 * kUpGrid)
 
-template <int MAXM>
-__device__ __forceinline__ void up_dot_store(const DecodeDesc& d, const uint4 (&w)[8], int pd, const uint16_t* s_x,
-                                             int n, int e, int lane) {
-  const int M = d.M, dm = d.d;
-  float a[MAXM];
-#pragma unroll
-  for (int m = 0; m < MAXM; ++m) a[m] = m < M ? d.ad[(size_t)m * d.F + n] : 0.f;
-  float v[MAXM];
-#pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int col = c * 512 + lane * 8;
-      if (c < pd && col < dm) s = dot8_bf(w[c], *reinterpret_cast<const uint4*>(s_x + (size_t)m * dm + col), s);
-    }
-    v[m] = s;
-  }
-  WaveTRed<MAXM, 32>::run(v, lane);
-  constexpr int SH = 6 - Log2<MAXM>::value;
-  if ((lane & ((1 << SH) - 1)) == 0) {
-    const int m = lane >> SH;
-    float am = a[0];
-#pragma unroll
-    for (int q = 1; q < MAXM; ++q)
-      if (q == m) am = a[q];
-    d.ul_h[(size_t)e * kDecMaxM + m] = m < M ? am * v[0] : 0.f;
-  }
-  if (lane == 0) d.ul_nrn[e] = n;
-}
-
-template <int MAXM>
 __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
-  extern __shared__ uint4 s_dyn[];
+  extern __shared__ uint4 s_dyn[];                     // x: M rows of d + 8 bf16
   __shared__ uint64_t s_mask[kDecMaxSub];
-  __shared__ int s_pre[kDecMaxSub + 1];
+  __shared__ int s_pre[kDecMaxSub];
   __shared__ int s_scan[kUpWaves];
-  uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn);       // [MAXM x d]
+  __shared__ int s_nrn[kUpMaxEnt];
+  __shared__ f32x4_t s_acc[kUpWaves][kUpNB][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int M = d.M, dm = d.d, F = d.F, R = d.R, nsub = F / R;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int steps = dm / (32 * kUpWaves);              // per wave
+  const int q = lane >> 4, r16 = lane & 15;
+  const int k0 = wave * steps * 32;                    // first element of the wave's K range
+  const int ldx = dm + 8;                              // LDS row stride of x (elements)
   constexpr int NT = 64 * kUpWaves;
-  const int per = (nsub + NT - 1) / NT;
+
+  // masks and their prefix; x into LDS
+  const int per = (nsub + NT - 1) / NT;                 // sub-tiles per thread (<= 4)
   const int s0 = min(nsub, tid * per), s1 = min(nsub, s0 + per);
   int loc = 0;
   for (int s = s0; s < s1; ++s) {
@@ -660,7 +650,15 @@ __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
     s_mask[s] = w;
     loc += __popcll(w);
   }
-  stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), M, dm / 8, dm / 8);
+  {
+    uint16_t* sx = reinterpret_cast<uint16_t*>(s_dyn);
+    const int c16 = dm / 8;
+    for (int p = tid; p < M * c16; p += NT) {
+      const int m = p / c16, c = p - m * c16;
+      *reinterpret_cast<uint4*>(sx + (size_t)m * ldx + c * 8) =
+          ldg16(reinterpret_cast<const uint16_t*>(d.x) + (size_t)m * dm + c * 8);
+    }
+  }
   int total;
   int run = block_excl_scan<NT>(loc, s_scan, &total);
   for (int s = s0; s < s1; ++s) {
@@ -668,150 +666,209 @@ __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
     run += __popcll(s_mask[s]);
   }
   __syncthreads();
-  if (blockIdx.x == 0 && tid == 0) *d.ul_total = total;
-  const int e0 = (int)((long long)total * blockIdx.x / gridDim.x);
-  const int e1 = (int)((long long)total * (blockIdx.x + 1) / gridDim.x);
-  const int pd = (dm + 511) / 512;
-  auto neuron_of = [&](int e) {
-    int lo = 0, hi = nsub - 1;                     // last sub-tile with s_pre <= e
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pre[mid] <= e) lo = mid;
-      else hi = mid - 1;
+  if (b == 0 && tid == 0) *d.ul_total = total;
+  const int e0 = (int)((long long)total * b / G), e1 = (int)((long long)total * (b + 1) / G);
+  const int ne = e1 - e0;
+  for (int i = tid; i < kUpMaxEnt; i += NT) {
+    int n = -1;
+    if (i < ne) {
+      const int e = e0 + i;
+      int lo = 0, hi = nsub - 1;                         // last sub-tile with s_pre <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= e) lo = mid;
+        else hi = mid - 1;
+      }
+      n = lo * R + nth_set_bit(s_mask[lo], e - s_pre[lo]);
     }
-    return lo * R + nth_set_bit(s_mask[lo], e - s_pre[lo]);
-  };
-  for (int ea = e0 + wave; ea < e1; ea += 2 * kUpWaves) {
-    const int eb = ea + kUpWaves;
-    const bool hb = eb < e1;
-    const int na = neuron_of(ea), nb = hb ? neuron_of(eb) : 0;
-    const uint16_t* ra = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)na * dm;
-    const uint16_t* rb = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)nb * dm;
-    uint4 wa[8], wb[8];
+    s_nrn[i] = n;
+  }
+  // the pad entries [total, total rounded up to 32)
+  if (b == G - 1) {
+    const int pad = (total + 31) / 32 * 32;
+    uint16_t* hT = reinterpret_cast<uint16_t*>(d.ul_h);
+    for (int p = tid; p < (pad - total) * M; p += NT) {
+      const int m = p / (pad - total), e = total + p % (pad - total);
+      hT[(size_t)m * d.ldh + e] = 0;
+      if (m == 0) d.ul_nrn[e] = 0;
+    }
+  }
+  __syncthreads();
+
+  const uint16_t* sx = reinterpret_cast<const uint16_t*>(s_dyn);
+  uint16_t* hT = reinterpret_cast<uint16_t*>(d.ul_h);
+  for (int g0 = 0; g0 * 16 < ne; g0 += kUpNB) {
+    uint4 aw[kUpNB][kUpMaxSteps];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int col = c * 512 + lane * 8;
-      const bool ok = c < pd && col < dm;
-      wa[c] = ok ? ldg16(ra + col) : uint4{0, 0, 0, 0};
-      wb[c] = (ok && hb) ? ldg16(rb + col) : uint4{0, 0, 0, 0};
+    for (int g = 0; g < kUpNB; ++g) {
+      const int nrn = s_nrn[(g0 + g) * 16 + r16];
+#pragma unroll
+      for (int j = 0; j < kUpMaxSteps; ++j) aw[g][j] = uint4{0, 0, 0, 0};
+      if (nrn >= 0) {
+        const uint16_t* wr = reinterpret_cast<const uint16_t*>(d.w_up) + (size_t)nrn * dm + k0 + q * 8;
+#pragma unroll
+        for (int j = 0; j < kUpMaxSteps; ++j)
+          if (j < steps) aw[g][j] = ldg16(wr + j * 32);
+      }
     }
-    up_dot_store<MAXM>(d, wa, pd, s_x, na, ea, lane);
-    if (hb) up_dot_store<MAXM>(d, wb, pd, s_x, nb, eb, lane);
+    // activations a[token][neuron] of the entries wave g reduces
+    float av[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave < kUpNB && r16 < M) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int n = s_nrn[(g0 + wave) * 16 + 4 * q + v];
+        if (n >= 0) av[v] = d.ad[(size_t)r16 * F + n];
+      }
+    }
+    f32x4_t acc[kUpNB];
+#pragma unroll
+    for (int g = 0; g < kUpNB; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* xr = sx + (size_t)min(r16, M - 1) * ldx + k0 + q * 8;
+#pragma unroll
+    for (int j = 0; j < kUpMaxSteps; ++j) {
+      if (j < steps) {
+        uint4 bx = *reinterpret_cast<const uint4*>(xr + j * 32);
+        if (r16 >= M) bx = uint4{0, 0, 0, 0};
+#pragma unroll
+        for (int g = 0; g < kUpNB; ++g)
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw[g][j]), as_bf16x8(bx), acc[g], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kUpNB; ++g) s_acc[wave][g][lane] = acc[g];
+    __syncthreads();
+    if (wave < kUpNB && (g0 + wave) * 16 < ne) {
+      const int g = wave;
+      f32x4_t u = s_acc[0][g][lane];
+#pragma unroll
+      for (int w = 1; w < kUpWaves; ++w) {
+        const f32x4_t t = s_acc[w][g][lane];
+        u[0] += t[0];
+        u[1] += t[1];
+        u[2] += t[2];
+        u[3] += t[3];
+      }
+      // lane l: local entries 16 (g0 + g) + 4 (l / 16) + v, token l % 16
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = (g0 + g) * 16 + 4 * q + v;
+        if (i < ne) {
+          if (r16 < M) hT[(size_t)r16 * d.ldh + e0 + i] = (uint16_t)f2bf(av[v] * u[v]);
+          if (r16 == 0) d.ul_nrn[e0 + i] = s_nrn[i];
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ k_dec_down2 (split mode)
-// One workgroup per slice of LW 16-byte chunks of y's columns (LW = 4 or 8:
-// 64 or 128 bytes of every row). Its 1024 threads form 1024 / LW row lanes:
-// lane q of a row lane reads chunk q of the slice, so a wave reads 64 / LW
-// whole row slices per instruction. Row lane r takes list entries r, r + RL,
-// ...; the list length is read in the same round as the first entries (slots
-// past it hold stale but valid neuron ids and are masked). Sums over the row
-// lanes are reduced across the wave (WaveTRed over the row-lane bits) and then
-// across the waves in order; the extra last workgroup routes the pack.
+// y[token, :] = sum over the list of h[token, e] W_down[:, n_e], as MFMA tiles
+// D[column][token] += W_down^T[column][e] hT[token][e] over 32 entries a step.
+// A workgroup owns a 64-column slice of y and one of S contiguous ranges of
+// 32-entry blocks; its four waves take the blocks in turn. A wave gathers the
+// block's 32 row slices (128 bytes each: eight lanes per row, whole lines)
+// into its own LDS tile and reads them back transposed as the A operand
+// (lane l: column l % 16 of a 16-column block, entries 8 (l / 16) .. + 7) with
+// ds_read_b64_tr_b16: in each 16-lane group, output lane j receives element
+// j % 4 of the 8 bytes source lane 4 v + j / 4 addressed, as its value v. So
+// source lane 4 v + u of group q points at row 8 q + 4 h + v, columns
+// c0 + 4 u .. + 3, and two reads (h = 0, 1) give a lane its column's 8 rows.
+// The 16-byte chunks of a row are stored XOR-swizzled by 2 (row % 4), which
+// spreads the 16 rows one read touches evenly over the banks. The B operand
+// is read straight from hT (16 bytes a lane). The four
+// waves' tiles are summed in LDS in wave order and written as the group's
+// partial rows; k_dec_reduce2 adds the S groups in group order.
 constexpr int kDown2Threads = 256;
+constexpr int kDown2MaxIds = 2048;                     // list entries per workgroup
 
-// Halving steps of WaveTRed restricted to the lane bits >= OMIN. With H the
-// number of halving steps (log2 V, at most 6 - log2 OMIN), each lane keeps
-// V >> H values with index base (lane >> (6 - H)) * (V >> H), summed over the
-// lanes that share lane % OMIN.
-template <int N, int O, int OMIN>
-struct WaveTRedHi {
-  template <int V>
-  __device__ __forceinline__ static void run(float (&v)[V], int lane) {
-    if constexpr (O >= OMIN) {
-      if constexpr (N > 1) {
-        const bool upper = (lane & O) != 0;
-#pragma unroll
-        for (int j = 0; j < N / 2; ++j) {
-          const float lo = v[j], hi = v[j + N / 2];
-          const float keep = upper ? hi : lo;
-          const float send = upper ? lo : hi;
-          v[j] = keep + __shfl_xor(send, O, FFN_WAVE);
-        }
-        WaveTRedHi<N / 2, O / 2, OMIN>::run(v, lane);
-      } else {
-        v[0] += __shfl_xor(v[0], O, FFN_WAVE);
-        WaveTRedHi<1, O / 2, OMIN>::run(v, lane);
-      }
-    }
-  }
-};
+__device__ __forceinline__ int dn_slot(int row, int c) { return row * 8 + (c ^ ((row & 3) << 1)); }
+typedef short dn_v4s __attribute__((ext_vector_type(4)));
 
-template <int MAXM>
 __global__ __launch_bounds__(kDown2Threads) void k_dec_down2(const DecodeDesc d) {
-  constexpr int LW = 8;                                 // 16-byte chunks per slice (128 bytes)
-  constexpr int NW = kDown2Threads / 64, RL = kDown2Threads / LW;
-  constexpr int B = MAXM <= 2 ? 8 : 4;                  // entries in flight per thread
-  constexpr int V = 8 * MAXM;                           // sums per thread
-  constexpr int STEPS = 6 - Log2<LW>::value;            // row-lane bits of a wave
-  constexpr int H = Log2<V>::value < STEPS ? Log2<V>::value : STEPS;   // halving steps
-  constexpr int KEEP = V >> H;                          // sums each lane keeps
-  __shared__ float s_red[NW][LW][V];
-  const int nsl = d.d / (8 * LW), S = d.ngroups;
+  constexpr int NW = kDown2Threads / 64;
+  __shared__ uint4 s_w[NW][2][32 * 8];                 // per wave: two blocks of 32 rows x 128 bytes
+  __shared__ int s_ids[kDown2MaxIds];
+  __shared__ f32x4_t s_acc[NW][4][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
-  const int q = tid % LW, rl = tid / LW;
-  const int b = blockIdx.x, g = b % S, sl = b / S;     // the S groups of a slice are neighbours
-  const int M = d.M, F = d.F;
-  const uint16_t* wd = reinterpret_cast<const uint16_t*>(d.w_down_nm) + (size_t)sl * 8 * LW + q * 8;
-  float acc[MAXM][8];
+  const int S = d.ngroups, nsl = d.d / 64;
+  const int sl = blockIdx.x % nsl, g = blockIdx.x / nsl;
+  const int M = d.M, dm = d.d, ldh = d.ldh;
+  const int total = *d.ul_total;
+  const int nkb = (total + 31) / 32;
+  const int kb0 = (int)((long long)nkb * g / S), kb1 = (int)((long long)nkb * (g + 1) / S);
+  for (int i = tid; i < (kb1 - kb0) * 32; i += kDown2Threads) s_ids[i] = d.ul_nrn[kb0 * 32 + i];
+  __syncthreads();
+  const int q = lane >> 4, r16 = lane & 15;
+  const int lrow = lane >> 3, lch = lane & 7;          // gather: row lrow + 8 i, chunk lch
+  const uint16_t* wd = reinterpret_cast<const uint16_t*>(d.w_down_nm) + (size_t)sl * 64 + lch * 8;
+  const uint16_t* hT = reinterpret_cast<const uint16_t*>(d.ul_h);
+  f32x4_t acc[4];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m)
+  for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // transposed-read source of this lane: row 8 q + 4 h + r16 / 4, columns 4 (r16 % 4) .. + 3
+  const int trow = 8 * q + (r16 >> 2), tcol = 4 * (r16 & 3);
+  for (int kb = kb0 + wave; kb < kb1; kb += 2 * NW) {
+    const int kbb = kb + NW;
+    const bool two = kbb < kb1;
+    uint4 w[2][4];
+    uint4 hb[2];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[m][k] = 0.f;
-  // entries g + S * (rl + RL * i): the list length is read in the same round
-  // as the first entries (slots past it hold stale but valid ids, masked)
-  int total = F;
-  for (int j0 = rl; g + S * j0 < total; j0 += RL * B) {
-    int nrn[B];
-    float h[B][MAXM];
+    for (int u = 0; u < 2; ++u) {
+      const int kk = u ? kbb : kb;
+      const bool on = u == 0 || two;
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const int e = g + S * (j0 + RL * i);
-      nrn[i] = e < F ? d.ul_nrn[e] : 0;
-#pragma unroll
-      for (int m = 0; m < MAXM; ++m) h[i][m] = (e < F && m < M) ? d.ul_h[(size_t)e * kDecMaxM + m] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int n = on ? s_ids[(kk - kb0) * 32 + lrow + 8 * i] : 0;
+        w[u][i] = on ? ldg16(wd + (size_t)n * dm) : uint4{0, 0, 0, 0};
+      }
+      hb[u] = (on && r16 < M) ? ldg16(hT + (size_t)r16 * ldh + kk * 32 + q * 8) : uint4{0, 0, 0, 0};
     }
-    if (j0 == rl) total = *d.ul_total;
-    uint4 w[B];
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const int e = g + S * (j0 + RL * i);
-      w[i] = e < total ? ldg16(wd + (size_t)nrn[i] * d.d) : uint4{0, 0, 0, 0};
-    }
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const int e = g + S * (j0 + RL * i);
-      if (e < total) {
-        float f[8];
-        unpack8(w[i], f);
+      for (int i = 0; i < 4; ++i) s_w[wave][u][dn_slot(lrow + 8 * i, lch)] = w[u][i];
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m)
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      const uint16_t* tb = reinterpret_cast<const uint16_t*>(&s_w[wave][u][0]);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc[m][k] = fmaf(h[i][m], f[k], acc[m][k]);
+      for (int c = 0; c < 4; ++c) {
+        // columns 16 c + tcol .. + 3 lie in chunk 2 c + tcol / 8 at element tcol % 8
+        const int ch = 2 * c + (tcol >> 3), el = tcol & 7;
+        const dn_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) dn_v4s*)(tb + dn_slot(trow, ch) * 8 + el));
+        const dn_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) dn_v4s*)(tb + dn_slot(trow + 4, ch) * 8 + el));
+        const uint4 a = uint4{(uint32_t)(uint16_t)lo.x | ((uint32_t)(uint16_t)lo.y << 16),
+                              (uint32_t)(uint16_t)lo.z | ((uint32_t)(uint16_t)lo.w << 16),
+                              (uint32_t)(uint16_t)hi.x | ((uint32_t)(uint16_t)hi.y << 16),
+                              (uint32_t)(uint16_t)hi.z | ((uint32_t)(uint16_t)hi.w << 16)};
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(hb[u]), acc[c], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
-  float v[V];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[m * 8 + k] = acc[m][k];
-  WaveTRedHi<V, 32, LW>::run(v, lane);
-  {
-    const int base = (lane >> (6 - H)) * KEEP;         // value indices this lane holds
-    if (base < V) {
-#pragma unroll
-      for (int j = 0; j < KEEP; ++j) s_red[wave][q][base + j] = v[j];
-    }
-  }
+  for (int c = 0; c < 4; ++c) s_acc[wave][c][lane] = acc[c];
   __syncthreads();
-  for (int o = tid; o < LW * V; o += kDown2Threads) {
-    const int qq = o / V, j = o % V, m = j / 8, k = j % 8;
-    float s = 0.f;
+  {
+    const int c = tid >> 6, l = tid & 63;              // 256 threads: 4 column blocks x 64 lanes
+    f32x4_t s = s_acc[0][c][l];
 #pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) s += s_red[w2][qq][j];
-    if (m < M) d.part[((size_t)g * M + m) * d.d + (size_t)sl * 8 * LW + qq * 8 + k] = s;
+    for (int w2 = 1; w2 < NW; ++w2) {
+      const f32x4_t t = s_acc[w2][c][l];
+      s[0] += t[0];
+      s[1] += t[1];
+      s[2] += t[2];
+      s[3] += t[3];
+    }
+    // lane l: columns 16 c + 4 (l / 16) + v, token l % 16
+    const int tok = l & 15;
+    if (tok < M)
+      *reinterpret_cast<float4*>(d.part + ((size_t)g * M + tok) * dm + sl * 64 + 16 * c + 4 * (l >> 4)) =
+          float4{s[0], s[1], s[2], s[3]};
   }
 }
 
@@ -948,41 +1005,42 @@ hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t dec_up_lds(const DecodeDesc& d) { return (size_t)dec_maxm(d.M) * d.d * 2; }
+size_t dec_up_lds(const DecodeDesc& d) { return (size_t)d.M * (d.d + 8) * 2; }
 
-template <int MAXM>
-static hipError_t go_up(const DecodeDesc& d, hipStream_t s) {
-  const size_t lds = dec_up_lds(d);
-  hipError_t e = lds_attr(k_dec_up<MAXM>, lds);
-  if (e != hipSuccess) return e;
-  ffn_launch((k_dec_up<MAXM>), dim3(kUpGrid), dim3(64 * kUpWaves), lds, s, d);
-  return hipGetLastError();
+// Shapes the split sequence handles: d a multiple of 256 and at most 4096
+// (a wave's eighth of d in registers), the padded list within the up grid's
+// groups and each down workgroup's entries within its id buffer.
+bool dec_split_ok(const DecodeDesc& d) {
+  const int nkb = (d.F + 31) / 32;
+  return d.d % 256 == 0 && d.d <= 32 * kUpWaves * kUpMaxSteps && (d.F + kUpGrid - 1) / kUpGrid <= kUpMaxEnt &&
+         dec_up_lds(d) <= 80 * 1024 &&
+         d.F / d.R <= kDecMaxSub && d.ngroups >= 1 && d.ngroups <= 32 && (nkb + d.ngroups - 1) / d.ngroups * 32 <= kDown2MaxIds &&
+         d.ldh >= nkb * 32;
 }
 
 hipError_t launch_dec_up(const DecodeDesc& d, hipStream_t s) {
-  if (d.M < 1 || d.M > kDecMaxM || d.F / d.R > kDecMaxSub || !d.ad || !d.ul_nrn || !d.ul_h || !d.ul_total)
+  if (d.M < 1 || d.M > kDecMaxM || !dec_split_ok(d) || !d.ad || !d.ul_nrn || !d.ul_h || !d.ul_total)
     return hipErrorInvalidValue;
-  switch (dec_maxm(d.M)) {
-    case 1: return go_up<1>(d, s);
-    case 2: return go_up<2>(d, s);
-    case 4: return go_up<4>(d, s);
-    default: return go_up<8>(d, s);
-  }
+  const size_t lds = dec_up_lds(d);
+  hipError_t e = lds_attr(k_dec_up, lds);
+  if (e != hipSuccess) return e;
+  ffn_launch(k_dec_up, dim3(kUpGrid), dim3(64 * kUpWaves), lds, s, d);
+  return hipGetLastError();
 }
 
-int dec_down2_groups(int d_model) { return std::max(1, std::min(32, 1024 / (d_model / 64))); }
+// Entry groups of the split down kernel: about 512 workgroups in all, and
+// enough groups that each holds at most kDown2MaxIds list entries.
+int dec_down2_groups(int d_model, int d_ff) {
+  const int nsl = std::max(1, d_model / 64), nkb = (d_ff + 31) / 32;
+  const int need = (nkb * 32 + kDown2MaxIds - 1) / kDown2MaxIds;
+  return std::max(need, std::max(1, std::min(32, 512 / nsl)));
+}
 
 hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s) {
-  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || !d.ul_nrn || !d.ul_h || !d.ul_total || !d.part ||
-      d.ngroups != dec_down2_groups(d.d))
+  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || !dec_split_ok(d) || !d.ul_nrn || !d.ul_h || !d.ul_total ||
+      !d.part)
     return hipErrorInvalidValue;
-  const dim3 grid(d.d / 64 * d.ngroups), blk(kDown2Threads);
-  switch (dec_maxm(d.M)) {
-    case 1: ffn_launch((k_dec_down2<1>), grid, blk, 0, s, d); break;
-    case 2: ffn_launch((k_dec_down2<2>), grid, blk, 0, s, d); break;
-    case 4: ffn_launch((k_dec_down2<4>), grid, blk, 0, s, d); break;
-    default: ffn_launch((k_dec_down2<8>), grid, blk, 0, s, d); break;
-  }
+  ffn_launch(k_dec_down2, dim3(d.d / 64 * d.ngroups), dim3(kDown2Threads), 0, s, d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = d.M * d.d;

@@ -152,8 +152,9 @@ hipError_t launch_updown_reduce(const UpdownDesc& u, hipStream_t s);
 //   DEC_PART   gate workgroups also sum their down rows into a partial y row;
 //              k_dec_reduce adds the partial rows
 //   DEC_SPLIT  gate workgroups publish masks and activations only; k_dec_up
-//              deals the union neurons evenly over the chip (compact h list);
-//              k_dec_down2 streams the list with coalesced row slices
+//              computes h of the union neurons, 16 at a time, on matrix cores
+//              (compact list); k_dec_down2 contracts the list's row slices
+//              with h on matrix cores
 enum DecMode : int { DEC_CHUNK = 0, DEC_PART = 1, DEC_SPLIT = 2 };
 struct DecodeDesc {
   int M, d, F, T, E, K;        // K: gate contraction length (d, or rank)
@@ -181,7 +182,8 @@ struct DecodeDesc {
   float* ad;                   // [M x F] split mode: a = z (active) or 0 for union neurons
   int32_t* ul_total;           // [1] split mode: union-list length
   int32_t* ul_nrn;             // [F] split mode: union neurons, ascending (compact)
-  float* ul_h;                 // [F x 8] split mode: h per token of each list entry
+  float* ul_h;                 // split mode: hT, bf16 [M][ldh], h per token of each list entry
+  int ldh;                     // split mode: row stride of hT (list entries, >= F rounded up to 32)
   int ngroups;                 // split mode: entry groups of the down kernel (partials in part)
   int route_pass;              // k_dec_down: the last workgroup routes the pack
   RouteDesc route;
@@ -199,9 +201,9 @@ hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s);
 hipError_t launch_dec_up(const DecodeDesc& d, hipStream_t s);
-size_t dec_up_lds(const DecodeDesc& d);
+bool dec_split_ok(const DecodeDesc& d);
 hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s);   // + the group-partial sum
-int dec_down2_groups(int d_model);
+int dec_down2_groups(int d_model, int d_ff);
 // Gate rows per decode workgroup for a gate contraction length K, TwELL tile
 // width T and m tokens (0 when the decode shape does not apply).
 int dec_rows_per_wg(int K, int T, int m, int* ipw);

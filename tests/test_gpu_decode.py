@@ -95,6 +95,8 @@ def test_decode_modes_and_general_agree(cid, m, kw):
         finally:
             for k in env:
                 os.environ.pop(k, None)
+        if path == "decode-split" and (wl.d % 256 or wl.d > 4096):
+            path = "decode-chunk"        # the split sequence needs d a multiple of 256, at most 4096
         assert ffn.forward_path(wl.m) == path
         y, pack = ffn.forward(x, **sel_args(wl))
         torch.cuda.synchronize()
