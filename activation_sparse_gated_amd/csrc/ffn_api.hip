@@ -124,7 +124,9 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
     // partial rows of the gate sub-tiles (partial-row mode) or of the down
     // kernel's entry groups (split mode), whichever is larger
     const size_t mm = std::min<size_t>(M, kDecMaxM);
-    w.dec_part = (float*)take(R ? std::max<size_t>(F / R, 32) * mm * d * sizeof(float) : 16);
+    // (top-k selection: the list-driven down kernel's groups for one token)
+    const size_t parts = R ? std::max<size_t>(F / R, 32) : (c.dtype == FFN_BF16 ? 32 : 0);
+    w.dec_part = (float*)take(parts ? parts * mm * d * sizeof(float) : 16);
   }
   w.ul_total = (int32_t*)take(sizeof(int32_t));
   w.ul_nrn = (int32_t*)take(F * sizeof(int32_t));
@@ -158,10 +160,13 @@ int device_cus() {
 // at decode sizes), FFN_SPARSE_NO_DECODE (1: the general kernels at 1..8 tokens
 // too), FFN_SPARSE_DEC_MODE (1 + DecMode: force the decode down-projection
 // organisation), FFN_SPARSE_NO_PREFILL_GEMM (1: the decode-shaped MFMA kernel
-// for 128+ tokens as well). They change launch shapes and kernel choice only, never the result
+// for 128+ tokens as well), FFN_SPARSE_NO_TOPK_DOWN (1: top-k selection's down
+// product through the per-token TwELL kernel). They change launch shapes and
+// kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {
-  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0;
+  int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0,
+      no_topk_down = 0;
 };
 
 static int env_int(const char* name) {
@@ -486,9 +491,12 @@ RouteDesc route_desc(const ffn_sparse_handle* h, int m, const ffn_twell_pack* p)
 }
 
 // Gate pass writing cnt / idx / val (no routing; see run_route / updown).
+// topk_out (top-k selection only): 0 the pack alone; 1 also the kept neurons
+// as the one-token list of the list-driven down kernel; 2 also the masked h
+// rows in hbuf for a dense down product.
 ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const float* bias, float bias_scalar,
                           const float* tau, int k, ffn_twell_pack* pack, float* g_debug, float* s_debug,
-                          hipStream_t s, bool* routed_by_topk) {
+                          hipStream_t s, bool* routed_by_topk, int topk_out = 0) {
   const auto& c = h->cfg;
   *routed_by_topk = false;
   EpiDesc e = epi_base(h, bias, bias_scalar, tau);
@@ -534,6 +542,14 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
     td.route = pack->route;
     td.dense_list = pack->dense_list;
     td.n_dense = pack->n_dense;
+    if (topk_out == 1) {
+      td.ul_nrn = h->ws.ul_nrn;
+      td.ul_hT = reinterpret_cast<uint16_t*>(h->ws.ul_h);
+      td.ul_total = h->ws.ul_total;
+    } else if (topk_out == 2) {
+      td.hmask = h->ws.hbuf;
+      td.ldhm = c.d_ff;
+    }
     *routed_by_topk = true;
     Timed tm(h, FFN_K_TOPK, s);
     return hip_status(launch_topk(td, s));
@@ -777,6 +793,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.no_decode = env_int("FFN_SPARSE_NO_DECODE");
   h->tune.dec_mode = env_int("FFN_SPARSE_DEC_MODE");
   h->tune.no_pf = env_int("FFN_SPARSE_NO_PREFILL_GEMM");
+  h->tune.no_topk_down = env_int("FFN_SPARSE_NO_TOPK_DOWN");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;
@@ -860,6 +877,40 @@ ffn_status ffn_sparse_dense_fallback(ffn_sparse_handle* h, const void* x, int32_
   return hip_status(run_dense_down(h, m, pack->dense_list, pack->n_dense, y, FFN_K_FALLBACK, s));
 }
 
+// Descriptor of the list-driven down kernel for one token's top-k list
+// (written by the top-k kernel); false when the shape does not fit it.
+static bool topk_list_desc(const ffn_sparse_handle* h, void* y, DecodeDesc* out) {
+  const auto& c = h->cfg;
+  DecodeDesc d{};
+  d.M = 1;
+  d.d = c.d_model;
+  d.F = c.d_ff;
+  d.T = c.tile_w;
+  d.R = 64;
+  d.w_down_nm = h->w_down_nm;
+  d.ul_total = h->ws.ul_total;
+  d.ul_nrn = h->ws.ul_nrn;
+  d.ul_h = h->ws.ul_h;
+  d.ldh = (d.F + 31) / 32 * 32;
+  d.ngroups = dec_down2_groups(d.d, d.F);
+  d.part = h->ws.dec_part;
+  d.y = y;
+  d.route_pass = 0;                    // the top-k kernel has routed the pack
+  if (!dec_split_ok(d)) return false;
+  *out = d;
+  return true;
+}
+
+// Down-product organisation of top-k selection's forward pass: 0 the
+// per-token TwELL kernel (fp32, or forced by the tuning switch), 1 the
+// one-token list kernel, 2 the dense product of masked h rows.
+static int topk_down_kind(const ffn_sparse_handle* h, int m) {
+  const auto& c = h->cfg;
+  if (c.sel != FFN_SEL_TOPK_WINA || c.dtype != FFN_BF16 || h->tune.no_topk_down || m < 1) return 0;
+  DecodeDesc ld;
+  return (m == 1 && topk_list_desc(h, nullptr, &ld)) ? 1 : 2;
+}
+
 ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
                               float bias_scalar, const float* tau, int32_t k, ffn_twell_pack* pack,
                               void* y, void* stream) {
@@ -884,10 +935,22 @@ ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, co
     if (dd.mode == DEC_SPLIT) return hip_status(launch_dec_down2(dd, s));
     return hip_status(launch_dec_down(dd, s));
   }
-  bool routed_by_topk = false;
-  st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, nullptr, nullptr, s, &routed_by_topk);
-  if (st != FFN_OK) return st;
   const auto& c = h->cfg;
+  // top-k selection keeps a fixed share of every token's neurons: one token's
+  // kept rows go to the list-driven down kernel; from two tokens the union of
+  // the kept sets covers most of W_down, so the masked h rows go to a dense
+  // down product
+  const int topk_out = topk_down_kind(h, m);
+  DecodeDesc ld{};
+  if (topk_out == 1 && !topk_list_desc(h, y, &ld)) return FFN_E_UNSUPPORTED;
+  bool routed_by_topk = false;
+  st = gate_pack_core(h, x, m, bias, bias_scalar, tau, k, pack, nullptr, nullptr, s, &routed_by_topk, topk_out);
+  if (st != FFN_OK) return st;
+  if (topk_out == 1) {
+    Timed tm(h, FFN_K_UPDOWN, s);
+    return hip_status(launch_dec_down2(ld, s));
+  }
+  if (topk_out == 2) return hip_status(run_dense_down(h, m, nullptr, nullptr, y, FFN_K_UPDOWN, s));
   const bool can_route = c.sel != FFN_SEL_TOPK_WINA && c.ell_w < c.tile_w;
   const bool decode = m <= kDecodeMaxM;
   UpdownDesc u = updown_desc(h, x, m, pack, y, decode && can_route);
@@ -919,7 +982,10 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle* h, const void* x, int32_t
 int32_t ffn_sparse_forward_path(const ffn_sparse_handle* h, int32_t m) {
   if (!h || m < 0 || m > h->cfg.max_m) return -1;
   DecodeDesc dd;
-  return plan_decode(h, m, &dd) ? 1 + dd.mode : 0;
+  if (plan_decode(h, m, &dd)) return 1 + dd.mode;
+  if (topk_down_kind(h, m) == 1) return 4;
+  if (topk_down_kind(h, m) == 2) return 5;
+  return 0;
 }
 
 ffn_status ffn_sparse_timing_enable(ffn_sparse_handle* h, int32_t enable, int32_t capacity) {

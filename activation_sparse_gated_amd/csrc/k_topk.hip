@@ -4,8 +4,13 @@
 // non-negative, so their fp32 bit patterns order like the values. A three-pass
 // radix select (11 + 11 + 10 bits, histograms in LDS) finds the exact key of
 // the k-th largest score; every key above it is kept, and among keys equal to
-// it the lowest indices are kept (prefix count over index order). The kept
-// neurons are then written per tile in ascending order with their h values.
+// it the lowest indices are kept (prefix count over index order). Each thread
+// owns a contiguous run of neurons, so two block-wide scans give every kept
+// neuron its rank in index order; the kept count before each tile start then
+// gives its TwELL slot, and the pack is written in one pass. Optionally the
+// kernel also writes the kept neurons as a neuron-ordered list with bf16 h (the
+// input of the list-driven down kernel) or h rows with the other neurons
+// zeroed (the input of a dense down product).
 #include "common.cuh"
 #include "kernels.cuh"
 
@@ -16,13 +21,12 @@ constexpr int TOPK_THREADS = 1024;
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   extern __shared__ uint32_t s_keys[];           // F score bit patterns
   __shared__ uint32_t s_hist[2048];
-  __shared__ uint32_t s_selbits[1024];           // F / 32 selection bits (F <= 32768)
+  __shared__ int s_tstart[1024 + 1];             // kept count before each tile (F / T <= 1024)
   __shared__ int s_scan[16];
   __shared__ uint32_t s_digit, s_above;
   const int tok = blockIdx.x, F = d.F, tid = threadIdx.x;
   const float* srow = d.s_buf + (size_t)tok * F;
   for (int i = tid; i < F; i += TOPK_THREADS) s_keys[i] = __float_as_uint(srow[i]);
-  for (int i = tid; i < (F + 31) / 32; i += TOPK_THREADS) s_selbits[i] = 0u;
   __syncthreads();
 
   const int k = min(max(d.k, 0), F);
@@ -54,49 +58,84 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
       __syncthreads();
     }
   }
-  // selection bits: key > tau, or key == tau among the first `need` in index order
+  // selection: thread t owns the contiguous chunk [t C, t C + C). A key above
+  // tau is kept; among keys equal to tau the first `need` in index order are.
+  // One scan ranks the equal keys, a second gives each kept neuron its rank
+  // among the kept ones (its position in the neuron-ordered list).
   const uint32_t tau = prefix;
-  int base = 0;
-  for (int c0 = 0; c0 < F; c0 += TOPK_THREADS) {
-    const int i = c0 + tid;
-    const uint32_t key = i < F ? s_keys[i] : 0u;
-    const int eq = (i < F && k > 0 && k < F && key == tau) ? 1 : 0;
-    int tot;
-    const int r = block_excl_scan<TOPK_THREADS>(eq, s_scan, &tot);
+  const int C = (F + TOPK_THREADS - 1) / TOPK_THREADS;    // <= 32
+  const int i0 = min(F, tid * C), i1 = min(F, i0 + C);
+  const bool partial = k > 0 && k < F;
+  int neq = 0;
+  for (int i = i0; i < i1; ++i) neq += (partial && s_keys[i] == tau) ? 1 : 0;
+  int tot;
+  int er = block_excl_scan<TOPK_THREADS>(neq, s_scan, &tot);
+  uint32_t cm = 0u;                                // kept elements of the chunk, bit i - i0
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = s_keys[i];
     bool sel;
     if (k == 0) sel = false;
-    else if (k >= F) sel = i < F;
-    else sel = i < F && (key > tau || (eq && base + r < need));
-    if (sel) atomicOr(&s_selbits[i >> 5], 1u << (i & 31));
-    base += tot;
+    else if (k >= F) sel = true;
+    else {
+      sel = key > tau;
+      if (key == tau) {
+        sel = er < need;
+        ++er;
+      }
+    }
+    if (sel) cm |= 1u << (i - i0);
+  }
+  int nsel_tot;
+  const int pb = block_excl_scan<TOPK_THREADS>(__popc(cm), s_scan, &nsel_tot);
+  // kept count before each tile start that falls in this chunk; each thread
+  // then overwrites its own keys with the kept neurons' ranks (or ~0)
+  const int T = d.T, ntiles = F / T;
+  for (int j = (i0 + T - 1) / T; j * T < i1; ++j) s_tstart[j] = pb + __popc(cm & ((1u << (j * T - i0)) - 1u));
+  if (tid == 0) s_tstart[ntiles] = nsel_tot;
+  {
+    int p = pb;
+    for (int i = i0; i < i1; ++i) s_keys[i] = ((cm >> (i - i0)) & 1u) ? (uint32_t)p++ : ~0u;
   }
   __syncthreads();
 
-  // pack: one wave per tile, 64 columns per ballot
-  const int ntiles = F / d.T, lane = tid & 63, wave = tid >> 6;
+  // pack (slot = rank within the tile) and, when asked, the neuron-ordered
+  // list or the masked h rows, in neuron order across the threads
   const float* hrow = d.h_buf + (size_t)tok * F;
-  for (int j = wave; j < ntiles; j += TOPK_THREADS / 64) {
-    const size_t slot0 = ((size_t)tok * ntiles + j) * d.T;  // E == T
-    int run = 0;
-    for (int c = 0; c < d.T; c += 64) {
-      const int r = c + lane;
-      const int i = j * d.T + r;
-      const bool sel = r < d.T && ((s_selbits[i >> 5] >> (i & 31)) & 1u);
-      const uint64_t bal = ballot64(sel);
-      const int pos = run + __popcll(bal & lanemask_lt());
-      if (sel) {
-        d.idx[slot0 + pos] = (uint16_t)r;
-        if (d.dtype == DT_F32) reinterpret_cast<float*>(d.val)[slot0 + pos] = hrow[i];
-        else reinterpret_cast<uint16_t*>(d.val)[slot0 + pos] = (uint16_t)f2bf(hrow[i]);
+  uint16_t* hm = d.hmask ? reinterpret_cast<uint16_t*>(d.hmask) + (size_t)tok * d.ldhm : nullptr;
+  for (int i = tid; i < F; i += TOPK_THREADS) {
+    const uint32_t rk = s_keys[i];
+    const int j = i / T;
+    const float hv = hrow[i];
+    if (rk != ~0u) {
+      const size_t slot = ((size_t)tok * ntiles + j) * T + ((int)rk - s_tstart[j]);   // E == T
+      d.idx[slot] = (uint16_t)(i - j * T);
+      if (d.dtype == DT_F32) reinterpret_cast<float*>(d.val)[slot] = hv;
+      else reinterpret_cast<uint16_t*>(d.val)[slot] = (uint16_t)f2bf(hv);
+      if (d.ul_nrn) {
+        d.ul_nrn[rk] = i;
+        d.ul_hT[rk] = (uint16_t)f2bf(hv);
       }
-      run += __popcll(bal);
     }
-    if (lane == 0) d.cnt[(size_t)tok * ntiles + j] = run;
-    for (int s = run + lane; s < d.T; s += 64) {
-      d.idx[slot0 + s] = 0xFFFF;
-      if (d.dtype == DT_F32) reinterpret_cast<float*>(d.val)[slot0 + s] = 0.f;
-      else reinterpret_cast<uint16_t*>(d.val)[slot0 + s] = 0;
+    if (hm) hm[i] = rk != ~0u ? (uint16_t)f2bf(hv) : (uint16_t)0;
+  }
+  for (int j = tid; j < ntiles; j += TOPK_THREADS) d.cnt[(size_t)tok * ntiles + j] = s_tstart[j + 1] - s_tstart[j];
+  for (int sidx = tid; sidx < F; sidx += TOPK_THREADS) {
+    const int j = sidx / T, sl = sidx - j * T;
+    if (sl >= s_tstart[j + 1] - s_tstart[j]) {
+      const size_t slot = (size_t)tok * F + sidx;
+      d.idx[slot] = 0xFFFF;
+      if (d.dtype == DT_F32) reinterpret_cast<float*>(d.val)[slot] = 0.f;
+      else reinterpret_cast<uint16_t*>(d.val)[slot] = 0;
     }
+  }
+  if (d.ul_nrn) {
+    // list length and the zero pad up to the next multiple of 32
+    const int pad = (nsel_tot + 31) / 32 * 32;
+    for (int e = nsel_tot + tid; e < pad; e += TOPK_THREADS) {
+      d.ul_nrn[e] = 0;
+      d.ul_hT[e] = 0;
+    }
+    if (tid == 0) *d.ul_total = nsel_tot;
   }
   // routing: with E == T no tile can overflow; every token holds exactly k entries
   if (tid == 0) {
@@ -107,6 +146,9 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
 
 hipError_t launch_topk(const TopkDesc& d, hipStream_t s) {
   if (d.M <= 0) return hipSuccess;
+  if (d.F > 32 * TOPK_THREADS || d.T <= 0 || d.F % d.T != 0 || d.F / d.T > 1024 || (d.ul_nrn && d.M != 1) ||
+      (d.hmask && d.ldhm < d.F))
+    return hipErrorInvalidValue;
   const size_t lds = (size_t)d.F * sizeof(uint32_t);
   if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk),

@@ -94,6 +94,9 @@ struct TopkDesc {
   const float* s_buf; const float* h_buf;
   int32_t* cnt; uint16_t* idx; void* val;
   uint8_t* route; int32_t* dense_list; int32_t* n_dense;
+  // optional outputs (null: not written)
+  int32_t* ul_nrn; uint16_t* ul_hT; int32_t* ul_total;   // one token: kept neurons ascending, bf16 h, count
+  void* hmask; int ldhm;                                  // bf16 h rows, unselected neurons zero
 };
 hipError_t launch_topk(const TopkDesc& d, hipStream_t s);
 

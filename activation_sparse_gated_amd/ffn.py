@@ -136,12 +136,14 @@ class SparseFFN:
         return y
 
     def forward_path(self, m: int) -> str:
-        """Kernel sequence forward() runs for m tokens: 'general', or
-        'decode-chunk' / 'decode-part' / 'decode-split' (see the C header)."""
+        """Kernel sequence forward() runs for m tokens: 'general',
+        'decode-chunk' / 'decode-part' / 'decode-split', or (top-k selection)
+        'topk-list' / 'topk-masked-dense' (see the C header)."""
         r = self.lib.ffn_sparse_forward_path(self.handle, int(m))
         if r < 0:
             raise ValueError(f"invalid token count {m}")
-        return {0: "general", 1: "decode-chunk", 2: "decode-part", 3: "decode-split"}[r]
+        return {0: "general", 1: "decode-chunk", 2: "decode-part", 3: "decode-split",
+                4: "topk-list", 5: "topk-masked-dense"}[r]
 
     # ------------------------------------------------------------------ timing
     def timing_enable(self, enable: bool = True, capacity: int = 4096) -> None:

@@ -235,6 +235,8 @@ def main():
     elif path == "decode-split":
         alg["up"] = urow + m * d * 2
         alg["updown"] = urow + m * d * 2
+    elif path == "topk-masked-dense":
+        alg["updown"] = F * d * 2 + m * F * 2 + m * d * 2      # all of W_down, the masked h rows, y
     if wl.sel == "topk":
         alg["gate"] = 2 * F * d * 2 + m * d * 2 + 2 * m * F * 4
     dom = max((k for k in kernels if k in alg), key=lambda k: kernels[k]["avg_us"])

@@ -189,11 +189,20 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t
  *       workgroup per 16-byte column chunk of y sums h * W_down rows;
  *   2 = partial rows: the gate kernel also sums its active neurons' down rows
  *       into a partial y row, a second kernel adds the partial rows;
- *   3 = split: an up kernel deals the active neurons evenly over the chip and
- *       writes a compact (neuron, h) list, a down kernel streams it in column
- *       slices.
- * 0 = the general sequence (gate, sparse up + down, partial-row sum, dense
- * backup); -1 = invalid handle or m. */
+ *   3 = split: an up kernel deals the union of the tokens' active neurons
+ *       evenly over the chip and writes a compact (neuron, h) list, a down
+ *       kernel contracts it in column slices (both on matrix cores).
+ * WINA top-k selection (bf16) runs the gate + up GEMM with the score epilogue
+ * and the top-k kernel, then:
+ *   4 = one token: the top-k kernel also writes its kept neurons as a
+ *       compact (neuron, h) list, which the split sequence's down kernel
+ *       contracts;
+ *   5 = several tokens (or a shape the list kernel does not take): the top-k
+ *       kernel writes h rows with the other neurons zeroed, and a dense down
+ *       GEMM multiplies them (the union of the tokens' kept sets covers most of
+ *       W_down).
+ * 0 = the general sequence (gate, sparse up + down over the TwELL pack,
+ * partial-row sum, dense backup); -1 = invalid handle or m. */
 int32_t ffn_sparse_forward_path(const ffn_sparse_handle *h, int32_t m);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around each

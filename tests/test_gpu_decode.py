@@ -134,3 +134,37 @@ def test_decode_all_masked_and_single_token_repeat():
         y, pack = ffn.forward(x, bias=f32_dev(bias))
         torch.cuda.synchronize()
         assert np.array_equal(host(y), first)
+
+
+@pytest.mark.parametrize("m,kw", [(1, dict(d=512, f=1024, T=128, E=128)),
+                                  (1, dict(d=1024, f=2816, T=128, E=128)),
+                                  (3, dict(d=512, f=1024, T=128, E=128)),
+                                  (1, dict(d=192, f=768, T=64, E=64))])
+def test_topk_down_organisations(m, kw):
+    """Top-k selection's down product through the one-token list kernel (one
+    token), the dense product of the masked h rows (several tokens, or a shape
+    the list kernel does not take) and the per-token TwELL kernel (forced by
+    the tuning switch) all match the oracle, pack and y, reproducibly."""
+    say("topk down", m, kw)
+    import torch
+    wl = make_workload("c4", m, 3, **kw)
+    ref = O.forward(wl)
+    x = to_dev(wl, wl.x)
+    ys = []
+    for env in ({}, {"FFN_SPARSE_NO_TOPK_DOWN": "1"}):
+        os.environ.update(env)
+        try:
+            ffn = make_ffn(wl)
+        finally:
+            for k in env:
+                os.environ.pop(k, None)
+        want = "general" if env else ("topk-list" if m == 1 and wl.d % 256 == 0 else "topk-masked-dense")
+        assert ffn.forward_path(wl.m) == want
+        y, pack = ffn.forward(x, **sel_args(wl))
+        torch.cuda.synchronize()
+        check_pack(wl, pack, ref)
+        check_y(y_to_f64(wl, y)[: wl.m], ref["y"])
+        y2, _ = ffn.forward(x, **sel_args(wl))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y2), host(y))
+        ys.append(host(y)[: wl.m].copy())

@@ -43,7 +43,7 @@ def run_full(wl, ref, *, E=None, check_band=True):
     torch.cuda.synchronize()
     worst = check_y(y_to_f64(wl, y)[: wl.m], ref["y"])
     # the one-call forward: same pack. On the general path non-routed rows are
-    # bit-identical (same sparse kernel); the decode path (1..8 tokens) sums in
+    # bit-identical (same sparse kernel); the decode and top-k sequences sum in
     # another order, so there only the oracle comparison applies
     y2, pack2 = ffn.forward(x, **kw)
     torch.cuda.synchronize()
