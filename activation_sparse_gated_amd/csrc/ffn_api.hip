@@ -70,6 +70,8 @@ struct Workspace {
   uint64_t* umask;       // [F / 2] decode sub-tiles: neurons active for any token
   float* hd;             // [kDecMaxM x F] decode hidden values (column-chunk mode)
   float* dec_part;       // [F / R x min(max_m, 8) x d] decode partial y rows
+  float* xh;             // [M x F / T x E] prefill: h per pack slot (XCD-sliced up / down)
+  float* kpart;          // [kPfSplitK x M x d] prefill dense backup: split-K partials (or null)
   int32_t* ul_total;     // [1] decode split mode: union-list length
   int32_t* ul_nrn;       // [F] decode split mode: union neurons
   float* ul_h;           // decode split mode: hT, bf16 [kDecMaxM][F rounded up to 32]
@@ -128,6 +130,12 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
     const size_t parts = R ? std::max<size_t>(F / R, 32) : (c.dtype == FFN_BF16 ? 32 : 0);
     w.dec_part = (float*)take(parts ? parts * mm * d * sizeof(float) : 16);
   }
+  // split-K partials of the dense backup's down product at prefill sizes
+  const bool can_route = !topk && c.ell_w < c.tile_w;
+  w.kpart = (float*)(M >= 128 && can_route && c.dtype == FFN_BF16 ? take((size_t)kPfSplitK * M * d * sizeof(float))
+                                                                    : nullptr);
+  // h per pack slot of the XCD-sliced prefill up / down pair
+  w.xh = (float*)take(M >= 128 && !topk ? M * (F / c.tile_w) * std::max(1, c.ell_w) * sizeof(float) : 16);
   w.ul_total = (int32_t*)take(sizeof(int32_t));
   w.ul_nrn = (int32_t*)take(F * sizeof(int32_t));
   w.ul_h = (float*)take((size_t)kDecMaxM * ((F + 31) / 32 * 32) * sizeof(uint16_t));
@@ -161,12 +169,13 @@ int device_cus() {
 // too), FFN_SPARSE_DEC_MODE (1 + DecMode: force the decode down-projection
 // organisation), FFN_SPARSE_NO_PREFILL_GEMM (1: the decode-shaped MFMA kernel
 // for 128+ tokens as well), FFN_SPARSE_NO_TOPK_DOWN (1: top-k selection's down
-// product through the per-token TwELL kernel). They change launch shapes and
+// product through the per-token TwELL kernel), FFN_SPARSE_NO_XCD (1: the
+// per-token sparse kernel at prefill token counts too). They change launch shapes and
 // kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {
   int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0,
-      no_topk_down = 0;
+      no_topk_down = 0, no_xcd = 0;
 };
 
 static int env_int(const char* name) {
@@ -473,6 +482,24 @@ hipError_t run_dense_down(ffn_sparse_handle* h, int m, const int32_t* list, cons
   e.y = y;
   e.ldy = c.d_model;
   e.yrows = list;
+  // dense backup at prefill sizes: few routed tokens (a device-side count)
+  // leave most 128 x 128 tiles empty, so K is split kPfSplitK ways and the
+  // slices are summed in order by a second kernel
+  if (list && m_dev && h->ws.kpart && !h->tune.no_pf) {
+    GemmDesc gp = g;
+    gp.ks = kPfSplitK;
+    gp.kpart = h->ws.kpart;
+    gp.kpart_m = c.max_m;
+    if (pf_ok(gp, e)) {
+      {
+        Timed tm(h, kind, s);
+        hipError_t err = launch_gemm_pf(gp, e, s);
+        if (err != hipSuccess) return err;
+      }
+      Timed tm(h, kind, s);
+      return launch_pf_ksum(gp, e, s);
+    }
+  }
   Timed tm(h, kind, s);
   return launch_gemm(g, e, s);
 }
@@ -698,7 +725,44 @@ UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const f
   return u;
 }
 
+// The XCD-sliced pair at prefill token counts (bf16 ReLU packs, routed tokens
+// left to the dense backup); false when it does not apply.
+static bool xcd_desc(const ffn_sparse_handle* h, const UpdownDesc& u, XcdDesc* out) {
+  if (u.M < 128 || u.include_routed || u.down_only || u.dtype != DT_BF16 || h->tune.no_xcd || u.M > h->cfg.max_m)
+    return false;
+  XcdDesc x{};
+  x.M = u.M;
+  x.d = u.d;
+  x.T = u.T;
+  x.E = u.E;
+  x.ntiles = u.F / u.T;
+  x.lg_e = 0;
+  while ((1 << x.lg_e) < u.E) ++x.lg_e;
+  x.x = u.x;
+  x.w_up = u.w_up;
+  x.w_down_nm = u.w_down_nm;
+  x.cnt = u.cnt;
+  x.idx = u.idx;
+  x.val = u.val;
+  x.hp = h->ws.xh;
+  x.y = u.y;
+  x.route_pass = u.route_pass;
+  x.route = u.route;
+  if (!xcd_ok(x)) return false;
+  *out = x;
+  return true;
+}
+
 ffn_status run_updown(ffn_sparse_handle* h, UpdownDesc& u, hipStream_t s) {
+  XcdDesc xd;
+  if (xcd_desc(h, u, &xd)) {
+    {
+      Timed tm(h, FFN_K_UP, s);
+      if (launch_xcd_up(xd, s) != hipSuccess) return FFN_E_HIP;
+    }
+    Timed tm(h, FFN_K_UPDOWN, s);
+    return hip_status(launch_xcd_down(xd, s));
+  }
   const long long nparts = (long long)ud_groups(u) * u.slot_split;
   if (nparts > 1 && (size_t)(u.M * nparts) > h->ws.ud_rows) return FFN_E_UNSUPPORTED;
   hipError_t err;
@@ -794,6 +858,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.dec_mode = env_int("FFN_SPARSE_DEC_MODE");
   h->tune.no_pf = env_int("FFN_SPARSE_NO_PREFILL_GEMM");
   h->tune.no_topk_down = env_int("FFN_SPARSE_NO_TOPK_DOWN");
+  h->tune.no_xcd = env_int("FFN_SPARSE_NO_XCD");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;

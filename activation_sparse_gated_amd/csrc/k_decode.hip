@@ -42,69 +42,9 @@
 #include "common.cuh"
 #include "kernels.cuh"
 #include "route.cuh"
+#include "wave.cuh"
 
 namespace ffn {
-
-// ------------------------------------------------------------------ wave transpose reduction
-// Reduces N values per lane across the 64 lanes of a wave. Each halving step
-// keeps one half of the values and swaps the other half with the partner lane,
-// so N - 1 + (6 - log2 N) shuffles replace N full butterflies. Afterwards
-// v[0] of lane L holds the wave total of value index L >> (6 - log2 N).
-template <int N, int O>
-struct WaveTRed {
-  template <int V>
-  __device__ __forceinline__ static void run(float (&v)[V], int lane) {
-    const bool upper = (lane & O) != 0;
-#pragma unroll
-    for (int j = 0; j < N / 2; ++j) {
-      const float lo = v[j], hi = v[j + N / 2];
-      const float keep = upper ? hi : lo;
-      const float send = upper ? lo : hi;
-      v[j] = keep + __shfl_xor(send, O, FFN_WAVE);
-    }
-    WaveTRed<N / 2, O / 2>::run(v, lane);
-  }
-};
-template <int O>
-struct WaveTRed<1, O> {
-  template <int V>
-  __device__ __forceinline__ static void run(float (&v)[V], int lane) {
-    v[0] += __shfl_xor(v[0], O, FFN_WAVE);
-    WaveTRed<1, O / 2>::run(v, lane);
-  }
-};
-template <>
-struct WaveTRed<1, 0> {
-  template <int V>
-  __device__ __forceinline__ static void run(float (&)[V], int) {}
-};
-template <int N>
-struct Log2 {
-  static constexpr int value = N <= 1 ? 0 : 1 + Log2<N / 2>::value;
-};
-template <>
-struct Log2<1> {
-  static constexpr int value = 0;
-};
-
-// dot of 8 bf16 weights with 8 bf16 inputs (fp32 products, fixed order)
-__device__ __forceinline__ float dot8_bf(const uint4 a, const uint4 b, float acc) {
-  float fa[8], fb[8];
-  unpack8(a, fa);
-  unpack8(b, fb);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc = fmaf(fa[k], fb[k], acc);
-  return acc;
-}
-__device__ __forceinline__ float dot8_f32(const uint4 a, const float4 b0, const float4 b1, float acc) {
-  float fa[8];
-  unpack8(a, fa);
-  acc = fmaf(fa[0], b0.x, acc); acc = fmaf(fa[1], b0.y, acc);
-  acc = fmaf(fa[2], b0.z, acc); acc = fmaf(fa[3], b0.w, acc);
-  acc = fmaf(fa[4], b1.x, acc); acc = fmaf(fa[5], b1.y, acc);
-  acc = fmaf(fa[6], b1.z, acc); acc = fmaf(fa[7], b1.w, acc);
-  return acc;
-}
 
 // ------------------------------------------------------------------ shared GEMV
 // Dot products of rows [row0, row0 + R) of A (nrows x K bf16, row-major) with

@@ -81,12 +81,14 @@ __global__ __launch_bounds__(PF_THREADS) void k_gemm_pf(const GemmDesc g, const 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = g.K / PF_BK;
-  fetch(0);
+  // K steps of this workgroup: all of them, or slice blockIdx.z of g.ks
+  const int KTA = g.K / PF_BK;
+  const int kt0 = (int)((long long)KTA * blockIdx.z / g.ks), KT = (int)((long long)KTA * (blockIdx.z + 1) / g.ks);
+  fetch(kt0);
   stash(0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
+  for (int kt = kt0; kt < KT; ++kt) {
+    const int st = (kt - kt0) & 1;
     if (kt + 1 < KT) fetch(kt + 1);
     const uint4* sa = smem + st * (2 * PF_BN * 8);
     const uint4* sb = sa + PF_BN * 8;
@@ -106,6 +108,20 @@ __global__ __launch_bounds__(PF_THREADS) void k_gemm_pf(const GemmDesc g, const 
     }
     if (kt + 1 < KT) stash(st ^ 1);
     __syncthreads();
+  }
+
+  if (g.ks > 1) {
+    // split K: this slice's fp32 partial tile, four consecutive rows a lane
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = wm * 64 + j * 16 + (lane & 15), r = wn * 64 + i * 16 + 4 * (lane >> 4);
+        if (m < mcnt)
+          *reinterpret_cast<float4*>(g.kpart + ((size_t)blockIdx.z * g.kpart_m + m0 + m) * g.nrows + n0 + r) =
+              float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      }
+    return;
   }
 
   // epilogue, one 64-token half at a time through an fp32 LDS tile
@@ -132,7 +148,10 @@ __global__ __launch_bounds__(PF_THREADS) void k_gemm_pf(const GemmDesc g, const 
 
 // Whether the prefill kernel handles this GEMM (host side).
 bool pf_ok(const GemmDesc& g, const EpiDesc& e) {
-  if (g.dtype != DT_BF16 || g.bmode != B_NATIVE || g.b_nsum != 1 || g.ks != 1 || g.gemv) return false;
+  if (g.dtype != DT_BF16 || g.bmode != B_NATIVE || g.b_nsum != 1 || g.gemv) return false;
+  if (g.ks != 1 && (g.ks < 1 || g.nmat != 1 || e.kind != EPI_Y || !g.kpart || !g.m_dev || g.kpart_m < g.M ||
+                    g.K / PF_BK < g.ks))
+    return false;
   if (g.M < PF_BM || g.K % PF_BK != 0 || (g.nrows * g.nmat) % PF_BN != 0) return false;
   if (g.nmat == 2 && g.nrows % (PF_BN / 2) != 0) return false;
   if (e.kind == EPI_TWELL && (e.T % PF_BN != 0 || e.t_out)) return false;
@@ -142,8 +161,39 @@ bool pf_ok(const GemmDesc& g, const EpiDesc& e) {
 
 template <int NMAT, int EPI>
 static hipError_t go_pf(const GemmDesc& g, const EpiDesc& e, hipStream_t s) {
-  const dim3 grid(g.nrows * g.nmat / PF_BN, (g.M + PF_BM - 1) / PF_BM);
+  const dim3 grid(g.nrows * g.nmat / PF_BN, (g.M + PF_BM - 1) / PF_BM, g.ks);
   ffn_launch((k_gemm_pf<NMAT, EPI>), grid, dim3(PF_THREADS), 0, s, g, e);
+  return hipGetLastError();
+}
+
+// y rows of a split-K product: the sum of the g.ks partial slices in slice
+// order, for the first m_dev token slots (output row yrows[m]).
+__global__ __launch_bounds__(256) void k_pf_ksum(const GemmDesc g, const EpiDesc e) {
+  const int Mtot = min(g.M, *g.m_dev);
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= g.nrows) return;
+  for (int m = blockIdx.y; m < Mtot; m += gridDim.y) {
+    float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < g.ks; ++z) {
+      const float4 p = *reinterpret_cast<const float4*>(g.kpart + ((size_t)z * g.kpart_m + m) * g.nrows + n);
+      acc.x += p.x;
+      acc.y += p.y;
+      acc.z += p.z;
+      acc.w += p.w;
+    }
+    const size_t row = (size_t)(e.yrows ? e.yrows[m] : m) * e.ldy + n;
+    if (e.out_f32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(e.y) + row) = acc;
+    } else {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(e.y) + row) =
+          uint2{f2bf(acc.x) | (f2bf(acc.y) << 16), f2bf(acc.z) | (f2bf(acc.w) << 16)};
+    }
+  }
+}
+
+hipError_t launch_pf_ksum(const GemmDesc& g, const EpiDesc& e, hipStream_t s) {
+  if (g.ks <= 1 || !g.kpart || !g.m_dev || g.nrows % 4 != 0) return hipErrorInvalidValue;
+  ffn_launch(k_pf_ksum, dim3((g.nrows / 4 + 255) / 256, 256), dim3(256), 0, s, g, e);
   return hipGetLastError();
 }
 

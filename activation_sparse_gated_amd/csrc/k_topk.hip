@@ -4,10 +4,12 @@
 // non-negative, so their fp32 bit patterns order like the values. A three-pass
 // radix select (11 + 11 + 10 bits, histograms in LDS) finds the exact key of
 // the k-th largest score; every key above it is kept, and among keys equal to
-// it the lowest indices are kept (prefix count over index order). Each thread
-// owns a contiguous run of neurons, so two block-wide scans give every kept
-// neuron its rank in index order; the kept count before each tile start then
-// gives its TwELL slot, and the pack is written in one pass. Optionally the
+// it the lowest indices are kept (prefix count over index order). Thread t
+// holds the contiguous run of keys [t C, t C + C) in registers (C <= CW), so
+// two block-wide scans give every kept neuron its rank in index order: one
+// ranks the keys equal to the cut, one the kept neurons. The ranks go to LDS,
+// and one wave per TwELL tile writes the tile's slots from them (slot = rank
+// minus the kept count before the tile) with coalesced stores. Optionally the
 // kernel also writes the kept neurons as a neuron-ordered list with bf16 h (the
 // input of the list-driven down kernel) or h rows with the other neurons
 // zeroed (the input of a dense down product).
@@ -18,8 +20,9 @@ namespace ffn {
 
 constexpr int TOPK_THREADS = 1024;
 
+template <int CW>
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
-  extern __shared__ uint32_t s_keys[];           // F score bit patterns
+  extern __shared__ uint32_t s_keys[];           // F score bit patterns, then the kept ranks
   __shared__ uint32_t s_hist[2048];
   __shared__ int s_tstart[1024 + 1];             // kept count before each tile (F / T <= 1024)
   __shared__ int s_scan[16];
@@ -28,6 +31,11 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   const float* srow = d.s_buf + (size_t)tok * F;
   for (int i = tid; i < F; i += TOPK_THREADS) s_keys[i] = __float_as_uint(srow[i]);
   __syncthreads();
+  const int C = (F + TOPK_THREADS - 1) / TOPK_THREADS;    // <= CW
+  const int i0 = min(F, tid * C), n = min(F, i0 + C) - i0;
+  uint32_t key[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) key[c] = c < n ? s_keys[i0 + c] : 0u;
 
   const int k = min(max(d.k, 0), F);
   uint32_t prefix = 0, pmask = 0;
@@ -38,10 +46,9 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
       const int sh = shifts[pass], nb = 1 << widths[pass];
       for (int i = tid; i < 2048; i += TOPK_THREADS) s_hist[i] = 0u;
       __syncthreads();
-      for (int i = tid; i < F; i += TOPK_THREADS) {
-        const uint32_t key = s_keys[i];
-        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1u);
-      }
+#pragma unroll
+      for (int c = 0; c < CW; ++c)
+        if (c < n && (key[c] & pmask) == prefix) atomicAdd(&s_hist[(key[c] >> sh) & (nb - 1)], 1u);
       __syncthreads();
       // cumulative counts from the largest digit down: thread t owns digits
       // nb-1-2t and nb-2-2t
@@ -58,74 +65,76 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
       __syncthreads();
     }
   }
-  // selection: thread t owns the contiguous chunk [t C, t C + C). A key above
-  // tau is kept; among keys equal to tau the first `need` in index order are.
-  // One scan ranks the equal keys, a second gives each kept neuron its rank
-  // among the kept ones (its position in the neuron-ordered list).
+
+  // selection: a key above tau is kept; among keys equal to tau the first
+  // `need` in index order are
   const uint32_t tau = prefix;
-  const int C = (F + TOPK_THREADS - 1) / TOPK_THREADS;    // <= 32
-  const int i0 = min(F, tid * C), i1 = min(F, i0 + C);
   const bool partial = k > 0 && k < F;
   int neq = 0;
-  for (int i = i0; i < i1; ++i) neq += (partial && s_keys[i] == tau) ? 1 : 0;
+#pragma unroll
+  for (int c = 0; c < CW; ++c) neq += (c < n && partial && key[c] == tau) ? 1 : 0;
   int tot;
   int er = block_excl_scan<TOPK_THREADS>(neq, s_scan, &tot);
-  uint32_t cm = 0u;                                // kept elements of the chunk, bit i - i0
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = s_keys[i];
+  uint32_t cm = 0u;                                // kept elements of the run, bit c
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
     bool sel;
     if (k == 0) sel = false;
     else if (k >= F) sel = true;
     else {
-      sel = key > tau;
-      if (key == tau) {
+      sel = key[c] > tau;
+      if (key[c] == tau) {
         sel = er < need;
         ++er;
       }
     }
-    if (sel) cm |= 1u << (i - i0);
+    if (c < n && sel) cm |= 1u << c;
   }
   int nsel_tot;
   const int pb = block_excl_scan<TOPK_THREADS>(__popc(cm), s_scan, &nsel_tot);
-  // kept count before each tile start that falls in this chunk; each thread
+  // kept count before each tile start that falls in this run; each thread
   // then overwrites its own keys with the kept neurons' ranks (or ~0)
   const int T = d.T, ntiles = F / T;
-  for (int j = (i0 + T - 1) / T; j * T < i1; ++j) s_tstart[j] = pb + __popc(cm & ((1u << (j * T - i0)) - 1u));
+  for (int j = (i0 + T - 1) / T; j * T < i0 + n; ++j) s_tstart[j] = pb + __popc(cm & ((1u << (j * T - i0)) - 1u));
   if (tid == 0) s_tstart[ntiles] = nsel_tot;
   {
     int p = pb;
-    for (int i = i0; i < i1; ++i) s_keys[i] = ((cm >> (i - i0)) & 1u) ? (uint32_t)p++ : ~0u;
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+      if (c < n) s_keys[i0 + c] = ((cm >> c) & 1u) ? (uint32_t)p++ : ~0u;
   }
   __syncthreads();
 
-  // pack (slot = rank within the tile) and, when asked, the neuron-ordered
-  // list or the masked h rows, in neuron order across the threads
+  // one wave per tile: its slots (rank within the tile), the list entries and
+  // the masked h row, from the ranks in LDS
+  const int lane = tid & 63, wave = tid >> 6;
   const float* hrow = d.h_buf + (size_t)tok * F;
   uint16_t* hm = d.hmask ? reinterpret_cast<uint16_t*>(d.hmask) + (size_t)tok * d.ldhm : nullptr;
-  for (int i = tid; i < F; i += TOPK_THREADS) {
-    const uint32_t rk = s_keys[i];
-    const int j = i / T;
-    const float hv = hrow[i];
-    if (rk != ~0u) {
-      const size_t slot = ((size_t)tok * ntiles + j) * T + ((int)rk - s_tstart[j]);   // E == T
-      d.idx[slot] = (uint16_t)(i - j * T);
-      if (d.dtype == DT_F32) reinterpret_cast<float*>(d.val)[slot] = hv;
-      else reinterpret_cast<uint16_t*>(d.val)[slot] = (uint16_t)f2bf(hv);
-      if (d.ul_nrn) {
-        d.ul_nrn[rk] = i;
-        d.ul_hT[rk] = (uint16_t)f2bf(hv);
+  for (int j = wave; j < ntiles; j += TOPK_THREADS / 64) {
+    const int base = s_tstart[j], cntj = s_tstart[j + 1] - base;
+    const size_t slot0 = ((size_t)tok * ntiles + j) * T;   // E == T
+    if (lane == 0) d.cnt[(size_t)tok * ntiles + j] = cntj;
+#pragma unroll 4
+    for (int r = lane; r < T; r += 64) {
+      const int i = j * T + r;
+      const uint32_t rk = s_keys[i];
+      const float hv = hrow[i];
+      if (rk != ~0u) {
+        const size_t slot = slot0 + ((int)rk - base);
+        d.idx[slot] = (uint16_t)r;
+        if (d.dtype == DT_F32) reinterpret_cast<float*>(d.val)[slot] = hv;
+        else reinterpret_cast<uint16_t*>(d.val)[slot] = (uint16_t)f2bf(hv);
+        if (d.ul_nrn) {
+          d.ul_nrn[rk] = i;
+          d.ul_hT[rk] = (uint16_t)f2bf(hv);
+        }
       }
-    }
-    if (hm) hm[i] = rk != ~0u ? (uint16_t)f2bf(hv) : (uint16_t)0;
-  }
-  for (int j = tid; j < ntiles; j += TOPK_THREADS) d.cnt[(size_t)tok * ntiles + j] = s_tstart[j + 1] - s_tstart[j];
-  for (int sidx = tid; sidx < F; sidx += TOPK_THREADS) {
-    const int j = sidx / T, sl = sidx - j * T;
-    if (sl >= s_tstart[j + 1] - s_tstart[j]) {
-      const size_t slot = (size_t)tok * F + sidx;
-      d.idx[slot] = 0xFFFF;
-      if (d.dtype == DT_F32) reinterpret_cast<float*>(d.val)[slot] = 0.f;
-      else reinterpret_cast<uint16_t*>(d.val)[slot] = 0;
+      if (hm) hm[i] = rk != ~0u ? (uint16_t)f2bf(hv) : (uint16_t)0;
+      if (r >= cntj) {                             // unused slots of the tile
+        d.idx[slot0 + r] = 0xFFFF;
+        if (d.dtype == DT_F32) reinterpret_cast<float*>(d.val)[slot0 + r] = 0.f;
+        else reinterpret_cast<uint16_t*>(d.val)[slot0 + r] = 0;
+      }
     }
   }
   if (d.ul_nrn) {
@@ -150,12 +159,14 @@ hipError_t launch_topk(const TopkDesc& d, hipStream_t s) {
       (d.hmask && d.ldhm < d.F))
     return hipErrorInvalidValue;
   const size_t lds = (size_t)d.F * sizeof(uint32_t);
+  const bool wide = d.F > 16 * TOPK_THREADS;
+  const void* kern = wide ? reinterpret_cast<const void*>(k_topk<32>) : reinterpret_cast<const void*>(k_topk<16>);
   if (lds > 48 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  ffn_launch(k_topk, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
+  if (wide) ffn_launch(k_topk<32>, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
+  else ffn_launch(k_topk<16>, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
   return hipGetLastError();
 }
 

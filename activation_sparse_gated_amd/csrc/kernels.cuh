@@ -53,6 +53,10 @@ struct GemmDesc {
   int ks;                 // workgroups splitting K; each writes its own output slab (>= 1)
   const uint32_t* ctrl;   // control block (epoch of the look-back words)
   int no_pf;              // 1: never the prefill-shaped kernel (tuning switch)
+  // prefill-shaped kernel with ks > 1 (output rows y, device-side token count):
+  // slice z of K writes fp32 partials kpart[(z * kpart_m + m) * nrows + n]
+  float* kpart;
+  int kpart_m;
 };
 
 struct EpiDesc {
@@ -130,6 +134,27 @@ struct UpdownDesc {
   int rank;
   const float* bias; float bias_scalar; const float* tau; int sel;
 };
+// Sparse up / down over the pack at prefill token counts, one eighth of the
+// weights per XCD (k_xcd_up: tiles j = r mod 8; k_xcd_down: y column slice r).
+struct XcdDesc {
+  int M, d, T, E, ntiles, lg_e;   // lg_e = log2 E
+  const void* x; const void* w_up; const void* w_down_nm;
+  const int32_t* cnt; const uint16_t* idx; const void* val;   // val: bf16 activations a
+  float* hp;                      // [M x ntiles x E] h per pack slot
+  void* y;
+  int route_pass;                 // the extra last workgroup routes the pack
+  RouteDesc route;
+};
+bool xcd_ok(const XcdDesc& u);
+// Prefill-shaped MFMA GEMM (128+ tokens): whether it takes a product, the
+// launch, and the slice sum of its split-K mode.
+bool pf_ok(const GemmDesc& g, const EpiDesc& e);
+hipError_t launch_gemm_pf(const GemmDesc& g, const EpiDesc& e, hipStream_t s);
+hipError_t launch_pf_ksum(const GemmDesc& g, const EpiDesc& e, hipStream_t s);
+constexpr int kPfSplitK = 8;       // K slices of the dense backup's down product
+hipError_t launch_xcd_up(const XcdDesc& u, hipStream_t s);     // + the routing pass
+hipError_t launch_xcd_down(const XcdDesc& u, hipStream_t s);
+
 // Entries one sparse workgroup holds in LDS (tiles per group * max entries per tile).
 constexpr int kUpdownCap = 2048;
 __host__ __device__ inline int ud_groups(const UpdownDesc& u) { return (u.F / u.T + u.tiles_per_group - 1) / u.tiles_per_group; }

@@ -235,6 +235,9 @@ def main():
     elif path == "decode-split":
         alg["up"] = urow + m * d * 2
         alg["updown"] = urow + m * d * 2
+    elif path == "general" and "up" in kernels:                 # prefill: XCD-sliced up, then down
+        alg["up"] = entries * d * 2 + m * d * 2
+        alg["updown"] = entries * d * 2 + m * d * 2
     elif path == "topk-masked-dense":
         alg["updown"] = F * d * 2 + m * F * 2 + m * d * 2      # all of W_down, the masked h rows, y
     if wl.sel == "topk":

@@ -300,6 +300,9 @@ PREFILL = [
     ("c5", 300, dict(d=256, f=2048, T=256, E=32)),
     ("c2", 200, dict(d=512, f=1024, T=128, E=16)),
     ("c4", 160, dict(d=256, f=768, T=128, E=128)),
+    ("c5", 261, dict(d=1024, f=2048, T=256, E=32)),
+    ("c2", 300, dict(d=512, f=4096, T=64, E=8)),
+    ("c3", 150, dict(d=512, f=1024, rank=64, T=128, E=16)),
 ]
 
 
@@ -327,3 +330,33 @@ def test_prefill_shapes(cid, m, kw):
         yd = make_ffn(wl).dense_forward(to_dev(wl, wl.x), **kw2)
         torch.cuda.synchronize()
         check_y(y_to_f64(wl, yd)[: wl.m], O.dense_forward(wl))
+
+
+@pytest.mark.parametrize("cid,m,kw", [("c5", 261, dict(d=1024, f=2048, T=256, E=32)),
+                                      ("c2", 300, dict(d=512, f=4096, T=64, E=8))])
+def test_prefill_xcd_pair_vs_per_token_kernel(cid, m, kw):
+    """The XCD-sliced up / down pair and the per-token sparse kernel (forced by
+    the tuning switch) give the same pack and y within the parity tolerance
+    against the oracle; the pair is bitwise reproducible."""
+    say("prefill xcd vs per-token", cid, m, kw)
+    import os
+    import torch
+    wl = make_workload(cid, m, 1, **kw)
+    ref = O.forward(wl)
+    x = to_dev(wl, wl.x)
+    outs = []
+    for env in ({}, {"FFN_SPARSE_NO_XCD": "1"}):
+        os.environ.update(env)
+        try:
+            ffn = make_ffn(wl)
+        finally:
+            for k in env:
+                os.environ.pop(k, None)
+        y, pack = ffn.forward(x, **sel_args(wl))
+        torch.cuda.synchronize()
+        check_pack(wl, pack, ref)
+        check_y(y_to_f64(wl, y)[: wl.m], ref["y"])
+        y2, _ = ffn.forward(x, **sel_args(wl))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y2), host(y))
+        outs.append(host(y)[: wl.m].copy())
