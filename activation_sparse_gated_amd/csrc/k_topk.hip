@@ -6,8 +6,8 @@
 // the k-th largest score; every key above it is kept, and among keys equal to
 // it the lowest indices are kept (prefix count over index order). Thread t
 // holds the contiguous run of keys [t C, t C + C) in registers (C <= CW), so
-// two block-wide scans give every kept neuron its rank in index order: one
-// ranks the keys equal to the cut, one the kept neurons. The ranks go to LDS,
+// one block-wide scan (of the counts above and equal to the cut, packed in one
+// word) gives every kept neuron its rank in index order. The ranks go to LDS,
 // and one wave per TwELL tile writes the tile's slots from them (slot = rank
 // minus the kept count before the tile) with coalesced stores. Optionally the
 // kernel also writes the kept neurons as a neuron-ordered list with bf16 h (the
@@ -20,16 +20,21 @@ namespace ffn {
 
 constexpr int TOPK_THREADS = 1024;
 
-template <int CW>
+template <int CW, bool HLDS>
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
-  extern __shared__ uint32_t s_keys[];           // F score bit patterns, then the kept ranks
+  extern __shared__ uint32_t s_keys[];           // F score bit patterns, then the kept ranks; h (HLDS)
   __shared__ uint32_t s_hist[2048];
   __shared__ int s_tstart[1024 + 1];             // kept count before each tile (F / T <= 1024)
   __shared__ int s_scan[16];
   __shared__ uint32_t s_digit, s_above;
   const int tok = blockIdx.x, F = d.F, tid = threadIdx.x;
   const float* srow = d.s_buf + (size_t)tok * F;
-  for (int i = tid; i < F; i += TOPK_THREADS) s_keys[i] = __float_as_uint(srow[i]);
+  float* s_hv = reinterpret_cast<float*>(s_keys + F);
+  const float* hrow = d.h_buf + (size_t)tok * F;
+  for (int i = tid; i < F; i += TOPK_THREADS) {
+    s_keys[i] = __float_as_uint(srow[i]);
+    if (HLDS) s_hv[i] = hrow[i];                 // h too, in the same round of loads
+  }
   __syncthreads();
   const int C = (F + TOPK_THREADS - 1) / TOPK_THREADS;    // <= CW
   const int i0 = min(F, tid * C), n = min(F, i0 + C) - i0;
@@ -70,11 +75,21 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   // `need` in index order are
   const uint32_t tau = prefix;
   const bool partial = k > 0 && k < F;
-  int neq = 0;
+  // one scan of the packed pair (keys above tau) << 16 | (keys equal to tau)
+  // per run gives both prefixes: the kept count before a run is the keys above
+  // tau before it plus min(need, equal keys before it) (both fields < 2^15)
+  int ngt = 0, neq = 0;
 #pragma unroll
-  for (int c = 0; c < CW; ++c) neq += (c < n && partial && key[c] == tau) ? 1 : 0;
+  for (int c = 0; c < CW; ++c) {
+    if (c < n && partial) {
+      ngt += key[c] > tau ? 1 : 0;
+      neq += key[c] == tau ? 1 : 0;
+    }
+  }
   int tot;
-  int er = block_excl_scan<TOPK_THREADS>(neq, s_scan, &tot);
+  const int pre2 = block_excl_scan<TOPK_THREADS>((ngt << 16) | neq, s_scan, &tot);
+  const int eqb = pre2 & 0xFFFF, gtb = pre2 >> 16;
+  int er = eqb;
   uint32_t cm = 0u;                                // kept elements of the run, bit c
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
@@ -90,8 +105,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
     }
     if (c < n && sel) cm |= 1u << c;
   }
-  int nsel_tot;
-  const int pb = block_excl_scan<TOPK_THREADS>(__popc(cm), s_scan, &nsel_tot);
+  const int pb = k == 0 ? 0 : (k >= F ? i0 : gtb + min(need, eqb));
+  const int nsel_tot = k == 0 ? 0 : (k >= F ? F : (tot >> 16) + min(need, tot & 0xFFFF));
   // kept count before each tile start that falls in this run; each thread
   // then overwrites its own keys with the kept neurons' ranks (or ~0)
   const int T = d.T, ntiles = F / T;
@@ -108,7 +123,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   // one wave per tile: its slots (rank within the tile), the list entries and
   // the masked h row, from the ranks in LDS
   const int lane = tid & 63, wave = tid >> 6;
-  const float* hrow = d.h_buf + (size_t)tok * F;
   uint16_t* hm = d.hmask ? reinterpret_cast<uint16_t*>(d.hmask) + (size_t)tok * d.ldhm : nullptr;
   for (int j = wave; j < ntiles; j += TOPK_THREADS / 64) {
     const int base = s_tstart[j], cntj = s_tstart[j + 1] - base;
@@ -118,7 +132,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
     for (int r = lane; r < T; r += 64) {
       const int i = j * T + r;
       const uint32_t rk = s_keys[i];
-      const float hv = hrow[i];
+      const float hv = HLDS ? s_hv[i] : hrow[i];
       if (rk != ~0u) {
         const size_t slot = slot0 + ((int)rk - base);
         d.idx[slot] = (uint16_t)r;
@@ -158,15 +172,17 @@ hipError_t launch_topk(const TopkDesc& d, hipStream_t s) {
   if (d.F > 32 * TOPK_THREADS || d.T <= 0 || d.F % d.T != 0 || d.F / d.T > 1024 || (d.ul_nrn && d.M != 1) ||
       (d.hmask && d.ldhm < d.F))
     return hipErrorInvalidValue;
-  const size_t lds = (size_t)d.F * sizeof(uint32_t);
+  // up to 16 keys per thread: h is staged in LDS beside the keys (8 F bytes)
   const bool wide = d.F > 16 * TOPK_THREADS;
-  const void* kern = wide ? reinterpret_cast<const void*>(k_topk<32>) : reinterpret_cast<const void*>(k_topk<16>);
+  const size_t lds = (size_t)d.F * sizeof(uint32_t) * (wide ? 1 : 2);
+  const void* kern = wide ? reinterpret_cast<const void*>(k_topk<32, false>)
+                          : reinterpret_cast<const void*>(k_topk<16, true>);
   if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if (wide) ffn_launch(k_topk<32>, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
-  else ffn_launch(k_topk<16>, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
+  if (wide) ffn_launch(k_topk<32, false>, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
+  else ffn_launch(k_topk<16, true>, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
   return hipGetLastError();
 }
 
