@@ -12,8 +12,9 @@
 // chunks of 16 bytes stored at chunk c ^ (row % 8), so the 16 rows one MFMA
 // operand read touches fall in distinct banks.
 //
-// The fp32 result is written to LDS one 64-token half at a time and handed to
-// the same epilogues as the decode-shaped kernels (gemm_core.cuh): activation,
+// The fp32 result tile (128 x 128, padded rows) is written to LDS, reusing the
+// staging buffers, and handed to the same epilogues as the decode-shaped
+// kernels (gemm_core.cuh) in one pass: activation,
 // selection and TwELL pack for the gate [Sparser/Faster/Lighter page,
 // "TwELL 減掉轉換開銷"], dense hidden values, output rows, WINA scores.
 #include "gemm_core.cuh"
@@ -27,8 +28,11 @@ __device__ __forceinline__ int pf_slot(int row, int c) { return row * 8 + (c ^ (
 template <int NMAT, int EPI>
 __global__ __launch_bounds__(PF_THREADS) void k_gemm_pf(const GemmDesc g, const EpiDesc e) {
   constexpr int RPM = PF_BN / NMAT;
-  constexpr int LDT = 65;                               // C tile: 128 rows x 64 tokens (+1 pad)
-  __shared__ uint4 smem[2 * 2 * PF_BN * 8];             // 2 stages x (A, B) x 128 rows x 8 chunks = 64 KB
+  constexpr int LDT = PF_BM + 1;                        // C tile: 128 rows x 128 tokens (+1 pad)
+  // 2 stages x (A, B) x 128 rows x 8 chunks = 64 KB for the K loop, then the
+  // fp32 C tile (66 KB) for the epilogue
+  constexpr int SMEM16 = (PF_BN * LDT * 4 + 15) / 16 > 2 * 2 * PF_BN * 8 ? (PF_BN * LDT * 4 + 15) / 16 : 2 * 2 * PF_BN * 8;
+  __shared__ uint4 smem[SMEM16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int tile_id = blockIdx.x, n0 = tile_id * RPM;
@@ -124,26 +128,19 @@ __global__ __launch_bounds__(PF_THREADS) void k_gemm_pf(const GemmDesc g, const 
     return;
   }
 
-  // epilogue, one 64-token half at a time through an fp32 LDS tile
+  // epilogue on the whole 128 x 128 tile through fp32 LDS: one pass (one
+  // look-back round for the TwELL pack) per workgroup
   float* tile = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int hm0 = m0 + hf * 64, hcnt = min(64, mcnt - hf * 64);
-    if (hcnt <= 0) break;
-    if (wm == hf) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            tile[(wn * 64 + i * 16 + 4 * (lane >> 4) + v) * LDT + j * 16 + (lane & 15)] = acc[i][j][v];
-    }
-    __syncthreads();
-    const TileView tv{tile, LDT, PF_BN, n0, hm0, hcnt, RPM};
-    run_epilogue<NMAT, EPI>(e, tv, g.ctrl, 0);
-    __syncthreads();
-  }
+      for (int v = 0; v < 4; ++v)
+        tile[(wn * 64 + i * 16 + 4 * (lane >> 4) + v) * LDT + wm * 64 + j * 16 + (lane & 15)] = acc[i][j][v];
+  __syncthreads();
+  const TileView tv{tile, LDT, PF_BN, n0, m0, mcnt, RPM};
+  run_epilogue<NMAT, EPI>(e, tv, g.ctrl, 0);
 }
 
 // Whether the prefill kernel handles this GEMM (host side).
