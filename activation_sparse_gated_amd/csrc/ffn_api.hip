@@ -640,6 +640,8 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.ul_nrn = h->ws.ul_nrn;
   d.ul_h = h->ws.ul_h;
   d.ngroups = dec_down2_groups(d.d, d.F);
+  d.nslab = c.rank ? dec_lowrank_slabs(m, c.d_model, c.rank) : 0;
+  d.tslab = h->ws.lr_slabs;
   d.ldh = (d.F + 31) / 32 * 32;
   // partial rows cost M x d x 4 bytes per sub-tile: they pay off for one
   // token; from two tokens the split sequence (union list dealt evenly over

@@ -8,7 +8,8 @@
 //
 //   k_dec_lowrank  t = V x (low-rank gate only; LoPA page, "How LoPA Gating
 //                  Restructures FFN Computation"): 1 KB pieces of V's rows,
-//                  several per wave, reduced in LDS.
+//                  several per wave, reduced in LDS; from two tokens
+//                  k_dec_lowrank_mf, the same product on matrix cores.
 //   k_dec_gate     one workgroup per sub-tile of R gate rows (R divides the
 //                  TwELL tile width T). The gate rows are streamed and dotted
 //                  with every token; the epilogue applies the selection and
@@ -143,6 +144,68 @@ __global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank(const DecodeDes
   }
 }
 
+// ------------------------------------------------------------------ k_dec_lowrank_mf
+// t = V x for 2..8 tokens on matrix cores (bf16 inputs, exact products): a
+// small dense contraction, 16 rows of V x d x the tokens per row group. The
+// grid is (rank / 16 row groups) x (nslab slices of d); the 4 waves of a
+// workgroup split its slice, step j of a wave being one
+// v_mfma_f32_16x16x32_bf16 with operand lane l holding row l % 16 (A: V, B:
+// token l % 16, zero from M on) at the 16-byte chunk 4 j + l / 16. The four
+// partial tiles are summed in LDS in wave order and written as slab z,
+// fp32 [M x rank]; the gate kernel adds the nslab slabs in slab order.
+constexpr int kLrWaves = 4;
+constexpr int kLrMaxSteps = 4;                        // 32-element steps per wave
+
+__global__ __launch_bounds__(64 * kLrWaves) void k_dec_lowrank_mf(const DecodeDesc d) {
+  __shared__ f32x4_t s_acc[kLrWaves][64];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15, M = d.M, dm = d.d, z = blockIdx.y;
+  const int steps = dm / (32 * kLrWaves * d.nslab);
+  const int k0 = (z * kLrWaves + wave) * steps * 32;
+  const int row = blockIdx.x * 16 + r16;
+  const uint16_t* vr = reinterpret_cast<const uint16_t*>(d.v) + (size_t)row * dm + k0 + q * 8;
+  const uint16_t* xr = reinterpret_cast<const uint16_t*>(d.x) + (size_t)min(r16, M - 1) * dm + k0 + q * 8;
+  uint4 a[kLrMaxSteps], b[kLrMaxSteps];
+#pragma unroll
+  for (int j = 0; j < kLrMaxSteps; ++j) {
+    a[j] = uint4{0, 0, 0, 0};
+    b[j] = uint4{0, 0, 0, 0};
+    if (j < steps) {                                   // uniform; B rows clamped, then masked
+      a[j] = ldg16(vr + j * 32);
+      const uint4 xv = ldg16(xr + j * 32);
+      b[j] = r16 < M ? xv : uint4{0, 0, 0, 0};
+    }
+  }
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kLrMaxSteps; ++j)
+    if (j < steps) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(b[j]), acc, 0, 0, 0);
+  s_acc[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t t = s_acc[0][lane];
+#pragma unroll
+    for (int w = 1; w < kLrWaves; ++w) {
+      const f32x4_t u = s_acc[w][lane];
+      t[0] += u[0];
+      t[1] += u[1];
+      t[2] += u[2];
+      t[3] += u[3];
+    }
+    // lane l: rows 16 b + 4 (l / 16) + v, token l % 16
+    if (r16 < M)
+      *reinterpret_cast<float4*>(d.tslab + ((size_t)z * M + r16) * d.rank + blockIdx.x * 16 + 4 * q) =
+          float4{t[0], t[1], t[2], t[3]};
+  }
+}
+
+// Slices of d for the matrix-core first stage (0: not applicable).
+int dec_lowrank_slabs(int m, int d_model, int rank) {
+  if (m < 2 || m > kDecMaxM || rank % 16 != 0 || d_model % 512 != 0) return 0;
+  const int S = std::min(8, d_model / 512);
+  return d_model / (32 * kLrWaves * S) <= kLrMaxSteps ? S : 0;
+}
+
 // ------------------------------------------------------------------ k_dec_gate
 __device__ __forceinline__ float dec_bias(const DecodeDesc& d, int t) { return d.bias ? d.bias[t] : d.bias_scalar; }
 __device__ __forceinline__ float dec_cut(const DecodeDesc& d, int t) {
@@ -183,8 +246,31 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   uint4 a[IPW];
   dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
   stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), M, dm / 8, dm / 8);
-  if (LOWRANK)
-    stage_rows<MAXM>(reinterpret_cast<uint4*>(s_t), reinterpret_cast<const uint4*>(d.t), M, d.rank / 4, d.rank / 4);
+  if (LOWRANK) {
+    if (d.nslab > 0) {
+      // t = the first stage's slabs, added in slab order
+      const int c4 = d.rank / 4;
+      for (int p = threadIdx.x; p < MAXM * c4; p += blockDim.x) {
+        const int m = p / c4, c = p - m * c4;
+        float4 v[8];                                   // all slab loads in flight together
+#pragma unroll
+        for (int z = 0; z < 8; ++z)
+          v[z] = (m < M && z < d.nslab) ? *reinterpret_cast<const float4*>(d.tslab + ((size_t)z * M + m) * d.rank + c * 4)
+                                         : float4{0.f, 0.f, 0.f, 0.f};
+        float4 acc = v[0];
+#pragma unroll
+        for (int z = 1; z < 8; ++z) {
+          acc.x += v[z].x;
+          acc.y += v[z].y;
+          acc.z += v[z].z;
+          acc.w += v[z].w;
+        }
+        reinterpret_cast<float4*>(s_t)[p] = acc;
+      }
+    } else {
+      stage_rows<MAXM>(reinterpret_cast<uint4*>(s_t), reinterpret_cast<const uint4*>(d.t), M, d.rank / 4, d.rank / 4);
+    }
+  }
   const uint32_t epoch = __hip_atomic_load(&d.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   __syncthreads();
   dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
@@ -875,6 +961,12 @@ static hipError_t go_lowrank_m(const DecodeDesc& d, hipStream_t s) {
 
 hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s) {
   if (d.M < 1 || d.M > kDecMaxM || d.rank <= 0) return hipErrorInvalidValue;
+  // several tokens: the matrix-core kernel, writing nslab slabs
+  if (d.nslab > 0) {
+    if (d.nslab != dec_lowrank_slabs(d.M, d.d, d.rank) || !d.tslab) return hipErrorInvalidValue;
+    ffn_launch(k_dec_lowrank_mf, dim3(d.rank / 16, d.nslab), dim3(64 * kLrWaves), 0, s, d);
+    return hipGetLastError();
+  }
   DecodeDesc e = d;
   e.ipw = pow2_pieces(d.d);
   if (e.ipw > 8) return hipErrorInvalidValue;

@@ -214,6 +214,8 @@ struct DecodeDesc {
   int ldh;                     // split mode: row stride of hT (list entries, >= F rounded up to 32)
   int ngroups;                 // split mode: entry groups of the down kernel (partials in part)
   int route_pass;              // k_dec_down: the last workgroup routes the pack
+  int nslab;                   // low rank, 2..8 tokens: t as nslab fp32 slabs [nslab][M][rank] (0: t)
+  float* tslab;
   RouteDesc route;
 };
 constexpr int kDecMaxM = 8;
@@ -235,5 +237,7 @@ int dec_down2_groups(int d_model, int d_ff);
 // Gate rows per decode workgroup for a gate contraction length K, TwELL tile
 // width T and m tokens (0 when the decode shape does not apply).
 int dec_rows_per_wg(int K, int T, int m, int* ipw);
+// Slices of d of the matrix-core first stage for m tokens (0: the VALU kernel).
+int dec_lowrank_slabs(int m, int d_model, int rank);
 
 }  // namespace ffn
