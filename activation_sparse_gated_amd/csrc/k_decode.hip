@@ -113,6 +113,71 @@ __device__ __forceinline__ void dec_gemv_finish(const uint4 (&a)[IPW], int K, in
   __syncthreads();
 }
 
+// Low-rank gate of 5..8 tokens on matrix cores: G[r, m] = U[n0 + r, :] t_m
+// for the R = 16 * NG rows of a sub-tile. t is fp32 and is not rounded: it is
+// split into bf16 hi + lo parts (t - hi rounded again), so each step is two
+// exact-product v_mfma_f32_16x16x32_bf16 accumulating in fp32. Waves
+// [g NW / NG, (g + 1) NW / NG) own row group g, each a contiguous range of
+// DS = K / 32 / (NW / NG) steps; operand lane l holds row l % 16 (A) or token
+// l % 16 (B, zero from M on) at the 16-byte chunk 4 j + l / 16.
+template <int NW, int NG, int DS>
+__device__ __forceinline__ void dec_mfma_issue(const uint16_t* __restrict__ A, int K, int row0, uint4 (&a)[DS]) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  constexpr int WPG = NW / NG;
+  const int g = wave / WPG, j0 = (wave % WPG) * DS;
+  const uint16_t* ar = A + (size_t)(row0 + g * 16 + (lane & 15)) * K + (lane >> 4) * 8;
+#pragma unroll
+  for (int j = 0; j < DS; ++j) a[j] = ldg16(ar + (j0 + j) * 32);
+}
+
+template <int NW, int NG, int DS, int MAXM>
+__device__ __forceinline__ void dec_mfma_finish(const uint4 (&a)[DS], int K, const float* s_t, int M,
+                                                f32x4_t* s_acc, float* s_g) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  constexpr int WPG = NW / NG;
+  const int g = wave / WPG, j0 = (wave % WPG) * DS;
+  const int q = lane >> 4, r16 = lane & 15;
+  const float* tr = s_t + (size_t)min(r16, M - 1) * K + q * 8;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < DS; ++j) {
+    const float4 t0 = *reinterpret_cast<const float4*>(tr + (j0 + j) * 32);
+    const float4 t1 = *reinterpret_cast<const float4*>(tr + (j0 + j) * 32 + 4);
+    const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t h0 = r16 < M ? f2bf(tv[2 * e]) : 0u, h1 = r16 < M ? f2bf(tv[2 * e + 1]) : 0u;
+      const uint32_t l0 = r16 < M ? f2bf(tv[2 * e] - bf2f(h0)) : 0u;
+      const uint32_t l1 = r16 < M ? f2bf(tv[2 * e + 1] - bf2f(h1)) : 0u;
+      hi[e] = h0 | (h1 << 16);
+      lo[e] = l0 | (l1 << 16);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(uint4{hi[0], hi[1], hi[2], hi[3]}), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(uint4{lo[0], lo[1], lo[2], lo[3]}), acc, 0, 0, 0);
+  }
+  s_acc[wave * 64 + lane] = acc;
+  __syncthreads();
+  // row group g's WPG tiles summed in wave order; lane l of the group's first
+  // wave holds rows 4 (l / 16) + v, token l % 16
+  if (wave % WPG == 0) {
+    f32x4_t s = s_acc[wave * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < WPG; ++w) {
+      const f32x4_t u = s_acc[(wave + w) * 64 + lane];
+      s[0] += u[0];
+      s[1] += u[1];
+      s[2] += u[2];
+      s[3] += u[3];
+    }
+    if (r16 < MAXM) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_g[(g * 16 + 4 * q + v) * MAXM + r16] = r16 < M ? s[v] : 0.f;
+    }
+  }
+  __syncthreads();
+}
+
 // Stages `rows` rows of `cols16` 16-byte chunks (row stride ld16 chunks in
 // global memory) into LDS, zero-filling rows [rows, MAXM).
 template <int MAXM>
@@ -232,6 +297,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   __shared__ uint64_t s_bal[MAXM];
   __shared__ int s_urow[64];
   __shared__ float s_h[PART ? 64 * MAXM : 1];
+  __shared__ f32x4_t s_acc[LOWRANK && MAXM == 8 && NW == 8 ? NW * 64 : 1];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int M = d.M, dm = d.d, F = d.F;
   const int K = d.K;
@@ -243,8 +309,20 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   float* s_t = reinterpret_cast<float*>(reinterpret_cast<char*>(s_dyn) + (size_t)MAXM * dm * 2);  // [MAXM x rank]
 
   // ---- gate row loads first; the token inputs are staged while they fly
+  // 5..8 tokens, low rank, 32-row sub-tiles over a K of 512: the gate on
+  // matrix cores (t split into bf16 hi + lo); otherwise the VALU GEMV (at 2..4
+  // tokens it is as fast, with fewer barriers)
+  constexpr bool MF = LOWRANK && MAXM == 8 && NW == 8;
+  constexpr int MF_DS = 4;                              // steps per wave: K = 512, two row groups
+  const bool use_mf = MF && R == 32 && K == 512;
   uint4 a[IPW];
-  dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
+  uint4 am[MF ? MF_DS : 1];
+  if constexpr (MF) {
+    if (use_mf) dec_mfma_issue<8, 2, MF_DS>(reinterpret_cast<const uint16_t*>(d.a_gate), K, n0, am);
+    else dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
+  } else {
+    dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
+  }
   stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), M, dm / 8, dm / 8);
   if (LOWRANK) {
     if (d.nslab > 0) {
@@ -273,7 +351,12 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   }
   const uint32_t epoch = __hip_atomic_load(&d.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   __syncthreads();
-  dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
+  if constexpr (MF) {
+    if (use_mf) dec_mfma_finish<8, 2, MF_DS, MAXM>(am, K, s_t, M, s_acc, s_g);
+    else dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
+  } else {
+    dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
+  }
 
   // ---- selection: one wave per token; the sub-tile's mask is one ballot (R <= 64)
   const int T = d.T, Q = T / R, q = (n0 % T) / R, j = n0 / T;
