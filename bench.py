@@ -192,6 +192,8 @@ def main():
     pack_bytes = m * ntiles * (4 + E * 4)
     touched = gate_bytes + n_union * row_bytes + 2 * m * d * 2 + 2 * pack_bytes
     n_dense = int(route.sum())
+    # the own dense FFN reads every weight once: gate (or U and V), W_up, W_down, x, y
+    dense_bytes = (F * r + r * d) * 2 + 2 * F * d * 2 + 2 * m * d * 2 if r else 3 * F * d * 2 + 2 * m * d * 2
     if n_dense:
         touched += 3 * F * d * 2
 
@@ -294,6 +296,7 @@ def main():
         "effective_hbm_GBps": round(touched / (ms_sparse * 1e-3) / 1e9, 1),
         "touched_bytes": int(touched),
         "dense_ms_per_step": round(ms_dense, 5),
+        "dense_effective_hbm_GBps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
         "speedup_vs_dense": round(ms_dense / ms_sparse, 3),
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
         "roofline": roofline,

@@ -41,6 +41,8 @@ DECODE = [
     ("c3", 6, dict(d=1024, f=2048, rank=128, T=128, E=8)),
     ("c3", 8, dict(d=2048, f=2048, rank=256, T=64, E=4)),
     ("c3", 2, dict(d=4096, f=1024, rank=512, T=128, E=64)),
+    ("c3", 5, dict(d=1024, f=2048, rank=512, T=128, E=16)),  # matrix-core gate (R32, K512), ragged M
+    ("c3", 7, dict(d=512, f=4096, rank=512, T=64, E=8)),     # matrix-core gate, two sub-tiles per tile
 ]
 
 
