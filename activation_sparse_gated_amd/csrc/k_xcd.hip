@@ -42,7 +42,7 @@ constexpr int kXList = 1024;                           // list entries a wave ho
 // transpose reduction, and lane group r writes h of row r.
 template <int CPL>
 __global__ __launch_bounds__(64 * kXWaves) void k_xcd_up(const XcdDesc u) {
-  constexpr int RPG = 32 / CPL;                        // rows per group
+  constexpr int RPG = 16 / CPL > 0 ? 16 / CPL : 1;      // rows per group
   const int nchunks = (u.M + kXTok - 1) / kXTok;
   if ((int)blockIdx.x == 8 * nchunks) {
     if (u.route_pass) route_pass(u.route);
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * kXWaves) void k_xcd_up(const XcdDesc u) {
 template <int LPE>
 __global__ __launch_bounds__(64 * kXWaves) void k_xcd_down(const XcdDesc u) {
   constexpr int EPI = 64 / LPE;                        // rows per load instruction
-  constexpr int U = 8;                                 // load instructions in flight
+  constexpr int U = 16;                                // load instructions in flight
   __shared__ int s_n[kXWaves][kXList];
   __shared__ float s_h[kXWaves][kXList];
   __shared__ int s_ne[kXWaves];
