@@ -533,6 +533,7 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
   e.idx = pack->idx;
   e.val = pack->val;
   e.lb = h->ws.lb;
+  e.lb_ld = h->cfg.max_m;
   GemmDesc g = gemm_base(h);
   g.M = m;
   if (c.sel == FFN_SEL_TOPK_WINA) {

@@ -67,7 +67,8 @@ __device__ __forceinline__ void epi_store_f32(const EpiDesc& e, const TileView& 
 //   1. one wave per token slot counts the active neurons (ballot + popcount)
 //      and publishes the count (epoch-tagged word) when Q > 1;
 //   2. every (token, earlier sub-tile) pair is read by one thread, waiting
-//      for this pass's epoch, and added into the token's offset in LDS;
+//      for this pass's epoch, and added into the token's offset in LDS (the
+//      words are sub-tile-major, so a wave reads 64 consecutive tokens' words);
 //   3. one wave per token slot writes its entries in ascending order at that
 //      offset (ballot + prefix popcount), and the last sub-tile writes cnt and
 //      the padding.
@@ -77,7 +78,7 @@ __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, c
   __shared__ float s_bias[kTwellMaxSlots], s_cut[kTwellMaxSlots];
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int Q = e.T / v.nt, q = (v.n0 % e.T) / v.nt, j = v.n0 / e.T;
-  const int ntiles = e.F / e.T, nsub = e.F / v.nt;
+  const int ntiles = e.F / e.T;
   // pass epoch of the look-back words (advanced by the routing pass after
   // every gate pass); only sub-tiled TwELL tiles need it
   const uint32_t epoch = Q > 1 ? __hip_atomic_load(&ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
@@ -104,14 +105,14 @@ __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, c
       c_local += __popcll(ballot64(act));
     }
     if (Q > 1 && lane == 0)
-      store64_relaxed(e.lb + (size_t)tok * nsub + (size_t)j * Q + q, ((uint64_t)epoch << 32) | (uint32_t)c_local);
+      store64_relaxed(e.lb + ((size_t)j * Q + q) * e.lb_ld + tok, ((uint64_t)epoch << 32) | (uint32_t)c_local);
   }
   __syncthreads();
   // phase 2
   if (Q > 1 && q > 0) {
     for (int p = threadIdx.x; p < v.mcnt * q; p += blockDim.x) {
-      const int m = p / q, pp = p - m * q;
-      const uint64_t* wp = e.lb + (size_t)(v.m0 + m) * nsub + (size_t)j * Q + pp;
+      const int pp = p / v.mcnt, m = p - pp * v.mcnt;   // consecutive threads: consecutive tokens
+      const uint64_t* wp = e.lb + ((size_t)j * Q + pp) * e.lb_ld + v.m0 + m;
       uint64_t w;
       while (((w = load64_relaxed(wp)) >> 32) != epoch) __builtin_amdgcn_s_sleep(1);
       atomicAdd(&s_off[m], (int)(uint32_t)w);

@@ -76,7 +76,8 @@ struct EpiDesc {
   // EPI_TWELL
   int T, E;
   int32_t* cnt; uint16_t* idx; void* val;
-  uint64_t* lb;           // look-back words [M x F / nt] (sub-tiled TwELL tiles)
+  uint64_t* lb;           // look-back words [F / nt sub-tiles x lb_ld tokens] (sub-tiled TwELL tiles)
+  int lb_ld;              // token stride of lb (>= the token count)
   // EPI_WINA
   const float* colnorm; float* s_buf; float* h_buf;
   // EPI_DENSE_H
