@@ -389,6 +389,15 @@ int run_lowrank_v(ffn_sparse_handle* h, const void* x, int m, const int32_t* gat
   return ks;
 }
 
+// Sums the first stage's slabs into slab 0 once (in slab order), so that the
+// gate GEMM reads t as one slab; returns the slab count left (1).
+int collapse_slabs(ffn_sparse_handle* h, int m, int nslabs, hipStream_t s, hipError_t* err) {
+  if (nslabs <= 1) return nslabs;
+  Timed tm(h, FFN_K_LOWRANK_V, s);
+  *err = launch_slab_sum(h->ws.lr_slabs, nslabs, (size_t)h->cfg.max_m * h->cfg.rank, (size_t)m * h->cfg.rank, s);
+  return 1;
+}
+
 // Points a GEMM's B operand at the first-stage slabs (summed on load).
 void b_from_slabs(GemmDesc& g, const ffn_sparse_handle* h, int nslabs) {
   g.B = h->ws.lr_slabs;
@@ -429,7 +438,9 @@ hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const in
   }
   // low-rank gate: t = V x (slabs), g = U t (fp32 into g_ext), then the up GEMM
   hipError_t err = hipSuccess;
-  const int nslabs = run_lowrank_v(h, x, m, list, m_dev, s, &err);
+  int nslabs = run_lowrank_v(h, x, m, list, m_dev, s, &err);
+  if (err != hipSuccess) return err;
+  nslabs = collapse_slabs(h, m, nslabs, s, &err);
   if (err != hipSuccess) return err;
   {
     GemmDesc gu = gemm_base(h);
@@ -584,7 +595,9 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
   }
   if (c.rank > 0) {
     hipError_t err = hipSuccess;
-    const int nslabs = run_lowrank_v(h, x, m, nullptr, nullptr, s, &err);
+    int nslabs = run_lowrank_v(h, x, m, nullptr, nullptr, s, &err);
+    if (err != hipSuccess) return FFN_E_HIP;
+    nslabs = collapse_slabs(h, m, nslabs, s, &err);
     if (err != hipSuccess) return FFN_E_HIP;
     g.A0 = h->u;
     g.lda = c.rank;

@@ -65,6 +65,22 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// slab[0][i] = sum over z of slab[z][i], added in slab order (the low-rank
+// first stage's split-K slabs, collapsed once before the gate GEMM reads t).
+__global__ __launch_bounds__(256) void k_slab_sum(float* slabs, int nslabs, size_t stride, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = slabs[i];
+  for (int z = 1; z < nslabs; ++z) s += slabs[(size_t)z * stride + i];
+  slabs[i] = s;
+}
+
+hipError_t launch_slab_sum(float* slabs, int nslabs, size_t stride, size_t n, hipStream_t s) {
+  if (nslabs <= 1 || n == 0) return hipSuccess;
+  ffn_launch(k_slab_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, slabs, nslabs, stride, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   int blocks = (int)((n + 255) / 256);

@@ -93,6 +93,8 @@ hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int 
 // c[i] = || row i of the neuron-major matrix [F x d] ||_2 (fp32, correctly rounded sqrt).
 hipError_t launch_rownorm(const void* w, float* c, int F, int d, int dtype, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+// slab 0 += slabs 1..nslabs-1 (in order), n floats each, slab stride `stride`.
+hipError_t launch_slab_sum(float* slabs, int nslabs, size_t stride, size_t n, hipStream_t s);
 
 struct TopkDesc {
   int M, F, k, T, dtype;
