@@ -123,12 +123,13 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
       const int r1 = dec_rows_per_wg(K, c.tile_w, 1, nullptr), r2 = dec_rows_per_wg(K, c.tile_w, 2, nullptr);
       R = (r1 && r2) ? std::min(r1, r2) : (r1 ? r1 : r2);
     }
-    // partial rows of the gate sub-tiles (partial-row mode) or of the down
-    // kernel's entry groups (split mode), whichever is larger
-    const size_t mm = std::min<size_t>(M, kDecMaxM);
-    // (top-k selection: the list-driven down kernel's groups for one token)
-    const size_t parts = R ? std::max<size_t>(F / R, 32) : (c.dtype == FFN_BF16 ? 32 : 0);
-    w.dec_part = (float*)take(parts ? parts * mm * d * sizeof(float) : 16);
+    // partial rows of the gate sub-tiles (partial-row mode, up to 8 tokens)
+    // or of the down kernel's entry groups (split mode, up to 16 tokens; also
+    // top-k selection's list-driven down product for one token)
+    const size_t rows_part = R ? (F / R) * std::min<size_t>(M, 8) : 0;
+    const size_t rows_split = c.dtype == FFN_BF16 ? 32 * std::min<size_t>(M, kDecMaxM) : 0;
+    const size_t rows = std::max(rows_part, rows_split);
+    w.dec_part = (float*)take(rows ? rows * d * sizeof(float) : 16);
   }
   // split-K partials of the dense backup's down product at prefill sizes
   const bool can_route = !topk && c.ell_w < c.tile_w;
@@ -634,7 +635,7 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.rank = c.rank;
   d.K = c.rank ? c.rank : c.d_model;
   d.sel = c.sel;
-  d.R = dec_rows_per_wg(d.K, c.tile_w, m, &d.ipw);   // at most 64 sub-tiles per TwELL tile
+  d.R = dec_gate_rows(d.K, c.tile_w, m, c.rank > 0, &d.ipw);   // at most 64 sub-tiles per TwELL tile
   if (d.R == 0 || d.F / d.R > 2048) return false;
   const size_t stat = 8 * 1024;    // static LDS of the decode kernels, upper bound
   if (dec_gate_lds(d) + stat > (size_t)h->lds_max) return false;
@@ -662,8 +663,10 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   // the chip, up and down products on matrix cores) is faster than the
   // column-chunk kernel, whose scattered loads grow with the union
   d.mode = m == 1 ? DEC_PART : DEC_SPLIT;
-  if (h->tune.dec_mode >= 1 && h->tune.dec_mode <= 3) d.mode = h->tune.dec_mode - 1;
+  if (h->tune.dec_mode >= 1 && h->tune.dec_mode <= 3 && m <= 8) d.mode = h->tune.dec_mode - 1;
   if (d.mode == DEC_SPLIT && !dec_split_ok(d)) d.mode = DEC_CHUNK;
+  // 9..16 tokens: the split sequence only, with the matrix-core first stage
+  if (m > 8 && (d.mode != DEC_SPLIT || (c.rank && d.nslab == 0))) return false;
   *out = d;
   return true;
 }

@@ -113,7 +113,7 @@ __device__ __forceinline__ void dec_gemv_finish(const uint4 (&a)[IPW], int K, in
   __syncthreads();
 }
 
-// Low-rank gate of 5..8 tokens on matrix cores: G[r, m] = U[n0 + r, :] t_m
+// Low-rank gate of 5..16 tokens on matrix cores: G[r, m] = U[n0 + r, :] t_m
 // for the R = 16 * NG rows of a sub-tile. t is fp32 and is not rounded: it is
 // split into bf16 hi + lo parts (t - hi rounded again), so each step is two
 // exact-product v_mfma_f32_16x16x32_bf16 accumulating in fp32. Waves
@@ -173,6 +173,60 @@ __device__ __forceinline__ void dec_mfma_finish(const uint4 (&a)[DS], int K, con
     if (r16 < MAXM) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) s_g[(g * 16 + 4 * q + v) * MAXM + r16] = r16 < M ? s[v] : 0.f;
+    }
+  }
+  __syncthreads();
+}
+
+// Full gate of 9..16 tokens on matrix cores: G[r, m] = W_gate[n0 + r, :] x_m for
+// the 32 rows of a sub-tile (two 16-row groups of four waves). x is bf16, so
+// one exact-product v_mfma_f32_16x16x32_bf16 per step; a wave owns ds = K / 128
+// consecutive steps (at most 16), operand lane l holding row l % 16 (A) or
+// token l % 16 (B, from LDS, zero from M on) at the 16-byte chunk 4 j + l / 16.
+constexpr int kFgMaxSteps = 16;
+
+__device__ __forceinline__ void dec_fg_issue(const uint16_t* __restrict__ A, int K, int row0,
+                                             uint4 (&a)[kFgMaxSteps]) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int ds = K / 128, g = wave >> 2, j0 = (wave & 3) * ds;
+  const uint16_t* ar = A + (size_t)(row0 + g * 16 + (lane & 15)) * K + (lane >> 4) * 8;
+#pragma unroll
+  for (int j = 0; j < kFgMaxSteps; ++j) a[j] = j < ds ? ldg16(ar + (j0 + j) * 32) : uint4{0, 0, 0, 0};
+}
+
+template <int MAXM>
+__device__ __forceinline__ void dec_fg_finish(const uint4 (&a)[kFgMaxSteps], int K, const uint16_t* s_x, int M,
+                                              f32x4_t* s_acc, float* s_g) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int ds = K / 128, g = wave >> 2, j0 = (wave & 3) * ds;
+  const int q = lane >> 4, r16 = lane & 15;
+  const uint16_t* xr = s_x + (size_t)min(r16, M - 1) * K + q * 8;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kFgMaxSteps; ++j) {
+    if (j < ds) {
+      uint4 b = *reinterpret_cast<const uint4*>(xr + (j0 + j) * 32);
+      if (r16 >= M) b = uint4{0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(b), acc, 0, 0, 0);
+    }
+  }
+  s_acc[wave * 64 + lane] = acc;
+  __syncthreads();
+  // group g's four tiles summed in wave order; lane l of the group's first
+  // wave holds rows 4 (l / 16) + v, token l % 16
+  if ((wave & 3) == 0) {
+    f32x4_t t = s_acc[wave * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const f32x4_t u = s_acc[(wave + w) * 64 + lane];
+      t[0] += u[0];
+      t[1] += u[1];
+      t[2] += u[2];
+      t[3] += u[3];
+    }
+    if (r16 < MAXM) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_g[(g * 16 + 4 * q + v) * MAXM + r16] = r16 < M ? t[v] : 0.f;
     }
   }
   __syncthreads();
@@ -297,28 +351,36 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   __shared__ uint64_t s_bal[MAXM];
   __shared__ int s_urow[64];
   __shared__ float s_h[PART ? 64 * MAXM : 1];
-  __shared__ f32x4_t s_acc[LOWRANK && MAXM == 8 && NW == 8 ? NW * 64 : 1];
+  __shared__ f32x4_t s_acc[((LOWRANK && MAXM >= 8) || MAXM == 16) && NW == 8 ? NW * 64 : 1];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int M = d.M, dm = d.d, F = d.F;
   const int K = d.K;
   int P = 1;
   while (P * 512 < K) P <<= 1;
-  const int R = NW * IPW / P;
+  // 9..16 tokens with a full gate: 32-row sub-tiles on matrix cores (the host
+  // plans this shape only when K allows it)
+  constexpr bool FG = !LOWRANK && MAXM == 16 && NW == 8;
+  const int R = FG ? 32 : NW * IPW / P;
   const int sub = blockIdx.x, n0 = sub * R;
   uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn);                               // [MAXM x d] bf16
   float* s_t = reinterpret_cast<float*>(reinterpret_cast<char*>(s_dyn) + (size_t)MAXM * dm * 2);  // [MAXM x rank]
 
   // ---- gate row loads first; the token inputs are staged while they fly
-  // 5..8 tokens, low rank, 32-row sub-tiles over a K of 512: the gate on
+  // 5..16 tokens, low rank, 32-row sub-tiles over a K of 512: the gate on
   // matrix cores (t split into bf16 hi + lo); otherwise the VALU GEMV (at 2..4
   // tokens it is as fast, with fewer barriers)
-  constexpr bool MF = LOWRANK && MAXM == 8 && NW == 8;
+  constexpr bool MF = LOWRANK && MAXM >= 8 && NW == 8;
   constexpr int MF_DS = 4;                              // steps per wave: K = 512, two row groups
   const bool use_mf = MF && R == 32 && K == 512;
+  const bool use_fg = FG && R == 32 && K % 128 == 0 && K <= 128 * kFgMaxSteps;
   uint4 a[IPW];
   uint4 am[MF ? MF_DS : 1];
+  uint4 af[FG ? kFgMaxSteps : 1];
   if constexpr (MF) {
     if (use_mf) dec_mfma_issue<8, 2, MF_DS>(reinterpret_cast<const uint16_t*>(d.a_gate), K, n0, am);
+    else dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
+  } else if constexpr (FG) {
+    if (use_fg) dec_fg_issue(reinterpret_cast<const uint16_t*>(d.a_gate), K, n0, af);
     else dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
   } else {
     dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
@@ -354,6 +416,9 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   if constexpr (MF) {
     if (use_mf) dec_mfma_finish<8, 2, MF_DS, MAXM>(am, K, s_t, M, s_acc, s_g);
     else dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
+  } else if constexpr (FG) {
+    if (use_fg) dec_fg_finish<MAXM>(af, K, s_x, M, s_acc, s_g);
+    else dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
   } else {
     dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
   }
@@ -361,8 +426,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   // ---- selection: one wave per token; the sub-tile's mask is one ballot (R <= 64)
   const int T = d.T, Q = T / R, q = (n0 % T) / R, j = n0 / T;
   const int ntiles = F / T, nsub = F / R;
-  if (wave < M) {
-    const int m = wave;
+  for (int m = wave; m < M; m += NW) {             // one wave per token (two at 16 tokens)
     const float b = dec_bias(d, m), cut = dec_cut(d, m);
     bool act = false;
     if (lane < R) {
@@ -502,11 +566,15 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   }
 
   // ---- TwELL pack: this sub-tile's entries at their offset inside tile j
-  if (wave < M) {
-    const int m = wave;
+  for (int m = wave; m < M; m += NW) {
     const uint64_t bal = s_bal[m];
     int pre = 0;
-    if (Q > 1) pre = wave_sum_i(lane < q ? lb_count(twp, epoch, tw) : 0);
+    if (Q > 1) {
+      // the wave's first token's first read was issued early
+      const uint64_t* wp = d.lb + (size_t)m * nsub + (size_t)j * Q + lane;
+      const uint64_t first = m == wave ? tw : (lane < q ? load64_relaxed(wp) : 0ull);
+      pre = wave_sum_i(lane < q ? lb_count(wp, epoch, first) : 0);
+    }
     const size_t slot0 = ((size_t)m * ntiles + j) * d.E;
     const bool act = (bal >> lane) & 1ull;
     const int pos = pre + __popcll(bal & lanemask_lt());
@@ -1010,7 +1078,7 @@ static int pow2_pieces(int K) {
   return P;
 }
 
-static int dec_maxm(int M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
+static int dec_maxm(int M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16))); }
 
 size_t dec_lowrank_lds(const DecodeDesc& d) { return (size_t)dec_maxm(d.M) * d.d * 2; }
 size_t dec_gate_lds(const DecodeDesc& d) {
@@ -1053,6 +1121,7 @@ hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s) {
   DecodeDesc e = d;
   e.ipw = pow2_pieces(d.d);
   if (e.ipw > 8) return hipErrorInvalidValue;
+  if (d.M > 8) return hipErrorInvalidValue;            // 9..16 tokens: the matrix-core kernel only
   switch (dec_maxm(d.M)) {
     case 1: return go_lowrank_m<1>(e, s);
     case 2: return go_lowrank_m<2>(e, s);
@@ -1073,11 +1142,17 @@ static hipError_t go_gate_k(const DecodeDesc& d, hipStream_t s) {
 
 template <int IPW, int MAXM, bool LOWRANK>
 static hipError_t go_gate_mode(const DecodeDesc& d, hipStream_t s) {
-  // a pack-only pass (no hidden values) uses the chunk-mode kernel with up = 0
-  const int mode = d.up ? d.mode : DEC_CHUNK;
-  if (mode == DEC_PART) return go_gate_k<IPW, MAXM, LOWRANK, DEC_PART>(d, s);
-  if (mode == DEC_SPLIT) return go_gate_k<IPW, MAXM, LOWRANK, DEC_SPLIT>(d, s);
-  return go_gate_k<IPW, MAXM, LOWRANK, DEC_CHUNK>(d, s);
+  // 9..16 tokens: the split sequence only (also for a pack-only pass, up = 0)
+  if constexpr (MAXM == 16) {
+    if (d.up && d.mode != DEC_SPLIT) return hipErrorInvalidValue;
+    return go_gate_k<IPW, MAXM, LOWRANK, DEC_SPLIT>(d, s);
+  } else {
+    // a pack-only pass (no hidden values) uses the chunk-mode kernel with up = 0
+    const int mode = d.up ? d.mode : DEC_CHUNK;
+    if (mode == DEC_PART) return go_gate_k<IPW, MAXM, LOWRANK, DEC_PART>(d, s);
+    if (mode == DEC_SPLIT) return go_gate_k<IPW, MAXM, LOWRANK, DEC_SPLIT>(d, s);
+    return go_gate_k<IPW, MAXM, LOWRANK, DEC_CHUNK>(d, s);
+  }
 }
 
 template <int IPW, int MAXM>
@@ -1098,18 +1173,23 @@ static hipError_t go_gate_m(const DecodeDesc& d, hipStream_t s) {
 hipError_t launch_dec_gate(const DecodeDesc& d, hipStream_t s) {
   if (d.M < 1 || d.M > kDecMaxM) return hipErrorInvalidValue;
   const int P = pow2_pieces(d.K);
-  if (dec_gate_waves(dec_maxm(d.M)) * d.ipw != d.R * P || d.R > 64 || d.R < 2 || d.T % d.R != 0 || d.F % d.R != 0 || d.T / d.R > 64)
+  // 9..16 tokens with a full gate: 32-row sub-tiles on matrix cores
+  const bool fg = d.M > 8 && !d.rank;
+  if (fg ? (d.R != 32 || d.K % 128 != 0 || d.K > 128 * kFgMaxSteps || d.ipw != 4)
+         : dec_gate_waves(dec_maxm(d.M)) * d.ipw != d.R * P)
     return hipErrorInvalidValue;
+  if (d.R > 64 || d.R < 2 || d.T % d.R != 0 || d.F % d.R != 0 || d.T / d.R > 64) return hipErrorInvalidValue;
   switch (dec_maxm(d.M)) {
     case 1: return go_gate_m<1>(d, s);
     case 2: return go_gate_m<2>(d, s);
     case 4: return go_gate_m<4>(d, s);
-    default: return go_gate_m<8>(d, s);
+    case 8: return go_gate_m<8>(d, s);
+    default: return go_gate_m<16>(d, s);
   }
 }
 
 hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s) {
-  if (d.M < 1 || d.M > kDecMaxM || d.d % 32 != 0 || d.F / d.R > kDecMaxSub || !d.part) return hipErrorInvalidValue;
+  if (d.M < 1 || d.M > 8 || d.d % 32 != 0 || d.F / d.R > kDecMaxSub || !d.part) return hipErrorInvalidValue;
   const dim3 grid(d.d / 32 + (d.route_pass ? 1 : 0)), blk(kRedThreads);
   switch (dec_maxm(d.M)) {
     case 1: ffn_launch((k_dec_reduce<1>), grid, blk, 0, s, d); break;
@@ -1121,6 +1201,19 @@ hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s) {
 }
 
 size_t dec_up_lds(const DecodeDesc& d) { return (size_t)d.M * (d.d + 8) * 2; }
+
+// Sub-tile rows of the decode gate for m tokens, gate contraction K and
+// TwELL tile T (0: the decode shape does not apply); *ipw gets the VALU
+// pieces per wave. From 9 tokens a full gate uses 32-row sub-tiles on matrix
+// cores.
+int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw) {
+  if (m > 8 && !lowrank) {
+    if (K % 128 != 0 || K > 128 * kFgMaxSteps || T % 32 != 0 || T / 32 > 64) return 0;
+    if (ipw) *ipw = 4;
+    return 32;
+  }
+  return dec_rows_per_wg(K, T, m, ipw);
+}
 
 // Shapes the split sequence handles: d a multiple of 256 and at most 4096
 // (a wave's eighth of d in registers), the padded list within the up grid's
@@ -1178,7 +1271,7 @@ int dec_rows_per_wg(int K, int T, int m, int* ipw_out) {
 }
 
 hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s) {
-  if (d.M < 1 || d.M > kDecMaxM || d.d % 64 != 0 || d.F / d.R > kDecMaxSub) return hipErrorInvalidValue;
+  if (d.M < 1 || d.M > 8 || d.d % 64 != 0 || d.F / d.R > kDecMaxSub) return hipErrorInvalidValue;
   const dim3 grid(d.d / 8 + (d.route_pass ? 1 : 0)), blk(kDownThreads);
   switch (dec_maxm(d.M)) {
     case 1: ffn_launch((k_dec_down<1>), grid, blk, 0, s, d); break;

@@ -221,7 +221,7 @@ struct DecodeDesc {
   float* tslab;
   RouteDesc route;
 };
-constexpr int kDecMaxM = 8;
+constexpr int kDecMaxM = 16;       // split sequence; the chunk and partial-row modes stop at 8
 // waves of the gate workgroup: 16 for one token; 8 (twice the registers per
 // thread) when the up / down accumulators hold several tokens
 constexpr int dec_gate_waves(int maxm) { return maxm == 1 ? 16 : 8; }
@@ -240,6 +240,7 @@ int dec_down2_groups(int d_model, int d_ff);
 // Gate rows per decode workgroup for a gate contraction length K, TwELL tile
 // width T and m tokens (0 when the decode shape does not apply).
 int dec_rows_per_wg(int K, int T, int m, int* ipw);
+int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw);
 // Slices of d of the matrix-core first stage for m tokens (0: the VALU kernel).
 int dec_lowrank_slabs(int m, int d_model, int rank);
 

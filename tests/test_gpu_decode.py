@@ -43,6 +43,9 @@ DECODE = [
     ("c3", 2, dict(d=4096, f=1024, rank=512, T=128, E=64)),
     ("c3", 5, dict(d=1024, f=2048, rank=512, T=128, E=16)),  # matrix-core gate (R32, K512), ragged M
     ("c3", 7, dict(d=512, f=4096, rank=512, T=64, E=8)),     # matrix-core gate, two sub-tiles per tile
+    ("c2", 16, dict(d=2048, f=4096, T=128, E=64)),           # 9..16 tokens: split sequence, two tokens a wave
+    ("c2", 11, dict(d=512, f=2048, T=64, E=8)),
+    ("c3", 13, dict(d=1024, f=2048, rank=512, T=128, E=16)),
 ]
 
 
