@@ -183,8 +183,8 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t
 
 /* Which kernel sequence ffn_sparse_forward runs for m tokens (host-only
  * query, no GPU work). The decode sequences (bf16, bias / threshold
- * selection, 1 <= m <= 8) run the low-rank first stage (rank > 0) and the gate
- * kernel (selection + TwELL pack), then:
+ * selection, 1 <= m <= 16; modes 1 and 2 up to 8 tokens) run the low-rank
+ * first stage (rank > 0) and the gate kernel (selection + TwELL pack), then:
  *   1 = column chunks: the gate kernel computes h of its active neurons, one
  *       workgroup per 16-byte column chunk of y sums h * W_down rows;
  *   2 = partial rows: the gate kernel also sums its active neurons' down rows
