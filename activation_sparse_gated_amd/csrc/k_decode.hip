@@ -440,6 +440,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
       if (Q > 1)
         store64_relaxed(d.lb + (size_t)m * nsub + sub, ((uint64_t)epoch << 32) | (uint32_t)__popcll(bal));
     }
+    if constexpr (MAXM <= 8) break;                   // at most one token a wave
   }
   if (threadIdx.x < MAXM && threadIdx.x >= M) s_bal[threadIdx.x] = 0ull;
   __syncthreads();
@@ -591,6 +592,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
         reinterpret_cast<uint16_t*>(d.val)[slot0 + s] = 0;
       }
     }
+    if constexpr (MAXM <= 8) break;                   // at most one token a wave
   }
 }
 
