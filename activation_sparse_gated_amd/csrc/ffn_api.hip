@@ -171,12 +171,14 @@ int device_cus() {
 // organisation), FFN_SPARSE_NO_PREFILL_GEMM (1: the decode-shaped MFMA kernel
 // for 128+ tokens as well), FFN_SPARSE_NO_TOPK_DOWN (1: top-k selection's down
 // product through the per-token TwELL kernel), FFN_SPARSE_NO_XCD (1: the
-// per-token sparse kernel at prefill token counts too). They change launch shapes and
+// per-token sparse kernel at prefill token counts too), FFN_SPARSE_LR_SLABS
+// (slices of d in the decode path's matrix-core low-rank first stage: 1, 2, 4
+// or 8). They change launch shapes and
 // kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {
   int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0,
-      no_topk_down = 0, no_xcd = 0;
+      no_topk_down = 0, no_xcd = 0, lr_slabs = 0;
 };
 
 static int env_int(const char* name) {
@@ -637,9 +639,6 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.sel = c.sel;
   d.R = dec_gate_rows(d.K, c.tile_w, m, c.rank > 0, &d.ipw);   // at most 64 sub-tiles per TwELL tile
   if (d.R == 0 || d.F / d.R > 2048) return false;
-  const size_t stat = 8 * 1024;    // static LDS of the decode kernels, upper bound
-  if (dec_gate_lds(d) + stat > (size_t)h->lds_max) return false;
-  if (c.rank && dec_lowrank_lds(d) + stat > (size_t)h->lds_max) return false;
   d.a_gate = c.rank ? h->u : h->w_gate;
   d.v = h->v;
   d.w_up = h->w_up;
@@ -655,7 +654,7 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.ul_nrn = h->ws.ul_nrn;
   d.ul_h = h->ws.ul_h;
   d.ngroups = dec_down2_groups(d.d, d.F);
-  d.nslab = c.rank ? dec_lowrank_slabs(m, c.d_model, c.rank) : 0;
+  d.nslab = c.rank ? dec_lowrank_slabs(m, c.d_model, c.rank, h->tune.lr_slabs) : 0;
   d.tslab = h->ws.lr_slabs;
   d.ldh = (d.F + 31) / 32 * 32;
   // partial rows cost M x d x 4 bytes per sub-tile: they pay off for one
@@ -667,6 +666,12 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   if (d.mode == DEC_SPLIT && !dec_split_ok(d)) d.mode = DEC_CHUNK;
   // 9..16 tokens: the split sequence only, with the matrix-core first stage
   if (m > 8 && (d.mode != DEC_SPLIT || (c.rank && d.nslab == 0))) return false;
+  // LDS of the gate pass with hidden values (the larger of the two passes)
+  const size_t stat = 8 * 1024;    // static LDS of the decode kernels, upper bound
+  DecodeDesc dl = d;
+  dl.up = 1;
+  if (dec_gate_lds(dl) + stat > (size_t)h->lds_max) return false;
+  if (c.rank && d.nslab == 0 && dec_lowrank_lds(d) + stat > (size_t)h->lds_max) return false;
   *out = d;
   return true;
 }
@@ -878,6 +883,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.no_pf = env_int("FFN_SPARSE_NO_PREFILL_GEMM");
   h->tune.no_topk_down = env_int("FFN_SPARSE_NO_TOPK_DOWN");
   h->tune.no_xcd = env_int("FFN_SPARSE_NO_XCD");
+  h->tune.lr_slabs = env_int("FFN_SPARSE_LR_SLABS");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;

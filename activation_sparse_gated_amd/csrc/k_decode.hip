@@ -264,23 +264,25 @@ __global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank(const DecodeDes
 }
 
 // ------------------------------------------------------------------ k_dec_lowrank_mf
-// t = V x for 2..8 tokens on matrix cores (bf16 inputs, exact products): a
+// t = V x for 2..16 tokens on matrix cores (bf16 inputs, exact products): a
 // small dense contraction, 16 rows of V x d x the tokens per row group. The
-// grid is (rank / 16 row groups) x (nslab slices of d); the 4 waves of a
-// workgroup split its slice, step j of a wave being one
-// v_mfma_f32_16x16x32_bf16 with operand lane l holding row l % 16 (A: V, B:
-// token l % 16, zero from M on) at the 16-byte chunk 4 j + l / 16. The four
-// partial tiles are summed in LDS in wave order and written as slab z,
-// fp32 [M x rank]; the gate kernel adds the nslab slabs in slab order.
-constexpr int kLrWaves = 4;
-constexpr int kLrMaxSteps = 4;                        // 32-element steps per wave
+// grid is (rank / 16 row groups) x (nslab slices of d); the NWV waves of a
+// workgroup (blockDim / 64: 4, 8 or 16) split its slice, step j of a wave
+// being one v_mfma_f32_16x16x32_bf16 with operand lane l holding row l % 16
+// (A: V, B: token l % 16, zero from M on) at the 16-byte chunk 4 j + l / 16.
+// The partial tiles are summed in LDS in wave order and written as slab z,
+// fp32 [M x rank]; the gate kernel adds the nslab slabs in slab order. Few
+// slabs keep the gate's reads of t small (every gate workgroup reads all of
+// them); wide workgroups keep the first stage's loads in flight.
+constexpr int kLrMaxWaves = 16;
+constexpr int kLrMaxSteps = 8;                        // 32-element steps per wave
 
-__global__ __launch_bounds__(64 * kLrWaves) void k_dec_lowrank_mf(const DecodeDesc d) {
-  __shared__ f32x4_t s_acc[kLrWaves][64];
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(64 * kLrMaxWaves) void k_dec_lowrank_mf(const DecodeDesc d) {
+  __shared__ f32x4_t s_acc[kLrMaxWaves][64];
+  const int lane = lane_id(), wave = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15, M = d.M, dm = d.d, z = blockIdx.y;
-  const int steps = dm / (32 * kLrWaves * d.nslab);
-  const int k0 = (z * kLrWaves + wave) * steps * 32;
+  const int steps = dm / (32 * nwv * d.nslab);
+  const int k0 = (z * nwv + wave) * steps * 32;
   const int row = blockIdx.x * 16 + r16;
   const uint16_t* vr = reinterpret_cast<const uint16_t*>(d.v) + (size_t)row * dm + k0 + q * 8;
   const uint16_t* xr = reinterpret_cast<const uint16_t*>(d.x) + (size_t)min(r16, M - 1) * dm + k0 + q * 8;
@@ -303,8 +305,7 @@ __global__ __launch_bounds__(64 * kLrWaves) void k_dec_lowrank_mf(const DecodeDe
   __syncthreads();
   if (wave == 0) {
     f32x4_t t = s_acc[0][lane];
-#pragma unroll
-    for (int w = 1; w < kLrWaves; ++w) {
+    for (int w = 1; w < nwv; ++w) {
       const f32x4_t u = s_acc[w][lane];
       t[0] += u[0];
       t[1] += u[1];
@@ -318,11 +319,25 @@ __global__ __launch_bounds__(64 * kLrWaves) void k_dec_lowrank_mf(const DecodeDe
   }
 }
 
-// Slices of d for the matrix-core first stage (0: not applicable).
-int dec_lowrank_slabs(int m, int d_model, int rank) {
+// Waves per workgroup of the matrix-core first stage for S slices of d (0: no
+// shape fits): the fewest of 4, 8, 16 whose wave slices take at most
+// kLrMaxSteps steps.
+static int lowrank_mf_waves(int d_model, int S) {
+  for (int nwv = 4; nwv <= kLrMaxWaves; nwv *= 2) {
+    const int per = 32 * nwv * S;
+    if (d_model % per == 0 && d_model / per <= kLrMaxSteps) return nwv;
+  }
+  return 0;
+}
+
+// Slices of d for the matrix-core first stage (0: not applicable). `want`
+// (a power of two, 0 for the default) asks for a slice count.
+int dec_lowrank_slabs(int m, int d_model, int rank, int want) {
   if (m < 2 || m > kDecMaxM || rank % 16 != 0 || d_model % 512 != 0) return 0;
-  const int S = std::min(8, d_model / 512);
-  return d_model / (32 * kLrWaves * S) <= kLrMaxSteps ? S : 0;
+  int S = want > 0 ? want : 8;                       // 2, 4 or 8 slabs measure within 1 us at 2..8 tokens
+  S = std::max(1, std::min(S, 8));
+  while (S < 8 && lowrank_mf_waves(d_model, S) == 0) S *= 2;
+  return lowrank_mf_waves(d_model, S) ? S : 0;
 }
 
 // ------------------------------------------------------------------ k_dec_gate
@@ -362,8 +377,11 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   constexpr bool FG = !LOWRANK && MAXM == 16 && NW == 8;
   const int R = FG ? 32 : NW * IPW / P;
   const int sub = blockIdx.x, n0 = sub * R;
+  // x is read by a full gate and by the up products of the partial-row and
+  // chunk modes; a low-rank split-mode or pack-only gate leaves it out of LDS
+  const bool need_x = dec_gate_needs_x(LOWRANK, MODE, d.up);
   uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn);                               // [MAXM x d] bf16
-  float* s_t = reinterpret_cast<float*>(reinterpret_cast<char*>(s_dyn) + (size_t)MAXM * dm * 2);  // [MAXM x rank]
+  float* s_t = reinterpret_cast<float*>(reinterpret_cast<char*>(s_dyn) + (need_x ? (size_t)MAXM * dm * 2 : 0));  // [MAXM x rank]
 
   // ---- gate row loads first; the token inputs are staged while they fly
   // 5..16 tokens, low rank, 32-row sub-tiles over a K of 512: the gate on
@@ -385,7 +403,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   } else {
     dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
   }
-  stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), M, dm / 8, dm / 8);
+  if (need_x) stage_rows<MAXM>(s_dyn, reinterpret_cast<const uint4*>(d.x), M, dm / 8, dm / 8);
   if (LOWRANK) {
     if (d.nslab > 0) {
       // t = the first stage's slabs, added in slab order
@@ -1083,8 +1101,17 @@ static int pow2_pieces(int K) {
 static int dec_maxm(int M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16))); }
 
 size_t dec_lowrank_lds(const DecodeDesc& d) { return (size_t)dec_maxm(d.M) * d.d * 2; }
+// The gate kernel's mode: the split sequence from 9 tokens, the chunk-mode
+// kernel for a pack-only pass, otherwise the planned mode.
+static int dec_gate_mode(const DecodeDesc& d) {
+  if (dec_maxm(d.M) == 16) return DEC_SPLIT;
+  return d.up ? d.mode : DEC_CHUNK;
+}
+
 size_t dec_gate_lds(const DecodeDesc& d) {
-  return (size_t)dec_maxm(d.M) * d.d * 2 + (d.rank ? (size_t)dec_maxm(d.M) * d.rank * 4 : 0);
+  const size_t mx = dec_maxm(d.M);
+  return (dec_gate_needs_x(d.rank > 0, dec_gate_mode(d), d.up) ? mx * d.d * 2 : 0) +
+         (d.rank ? mx * d.rank * 4 : 0);
 }
 
 template <typename Kern>
@@ -1116,8 +1143,9 @@ hipError_t launch_dec_lowrank(const DecodeDesc& d, hipStream_t s) {
   if (d.M < 1 || d.M > kDecMaxM || d.rank <= 0) return hipErrorInvalidValue;
   // several tokens: the matrix-core kernel, writing nslab slabs
   if (d.nslab > 0) {
-    if (d.nslab != dec_lowrank_slabs(d.M, d.d, d.rank) || !d.tslab) return hipErrorInvalidValue;
-    ffn_launch(k_dec_lowrank_mf, dim3(d.rank / 16, d.nslab), dim3(64 * kLrWaves), 0, s, d);
+    const int nwv = d.nslab >= 1 && d.nslab <= 8 ? lowrank_mf_waves(d.d, d.nslab) : 0;
+    if (nwv == 0 || d.M < 2 || d.rank % 16 != 0 || !d.tslab) return hipErrorInvalidValue;
+    ffn_launch(k_dec_lowrank_mf, dim3(d.rank / 16, d.nslab), dim3(64 * nwv), 0, s, d);
     return hipGetLastError();
   }
   DecodeDesc e = d;
@@ -1150,7 +1178,7 @@ static hipError_t go_gate_mode(const DecodeDesc& d, hipStream_t s) {
     return go_gate_k<IPW, MAXM, LOWRANK, DEC_SPLIT>(d, s);
   } else {
     // a pack-only pass (no hidden values) uses the chunk-mode kernel with up = 0
-    const int mode = d.up ? d.mode : DEC_CHUNK;
+    const int mode = dec_gate_mode(d);
     if (mode == DEC_PART) return go_gate_k<IPW, MAXM, LOWRANK, DEC_PART>(d, s);
     if (mode == DEC_SPLIT) return go_gate_k<IPW, MAXM, LOWRANK, DEC_SPLIT>(d, s);
     return go_gate_k<IPW, MAXM, LOWRANK, DEC_CHUNK>(d, s);

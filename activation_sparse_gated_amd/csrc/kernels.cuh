@@ -217,7 +217,7 @@ struct DecodeDesc {
   int ldh;                     // split mode: row stride of hT (list entries, >= F rounded up to 32)
   int ngroups;                 // split mode: entry groups of the down kernel (partials in part)
   int route_pass;              // k_dec_down: the last workgroup routes the pack
-  int nslab;                   // low rank, 2..8 tokens: t as nslab fp32 slabs [nslab][M][rank] (0: t)
+  int nslab;                   // low rank, 2..16 tokens: t as nslab fp32 slabs [nslab][M][rank] (0: t)
   float* tslab;
   RouteDesc route;
 };
@@ -226,6 +226,12 @@ constexpr int kDecMaxM = 16;       // split sequence; the chunk and partial-row 
 // thread) when the up / down accumulators hold several tokens
 constexpr int dec_gate_waves(int maxm) { return maxm == 1 ? 16 : 8; }
 constexpr int kDecVWaves = 4;      // waves of the low-rank first-stage workgroup
+// Whether the gate kernel stages the tokens' x in LDS: a full gate reads it,
+// and so do the up products of the partial-row and chunk modes; a low-rank
+// gate in split mode or a pack-only pass (up = 0) does not.
+__host__ __device__ constexpr bool dec_gate_needs_x(bool lowrank, int mode, int up) {
+  return !lowrank || (up != 0 && mode != DEC_SPLIT);
+}
 // Dynamic LDS bytes of k_dec_gate / k_dec_lowrank for a descriptor.
 size_t dec_gate_lds(const DecodeDesc& d);
 size_t dec_lowrank_lds(const DecodeDesc& d);
@@ -242,6 +248,6 @@ int dec_down2_groups(int d_model, int d_ff);
 int dec_rows_per_wg(int K, int T, int m, int* ipw);
 int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw);
 // Slices of d of the matrix-core first stage for m tokens (0: the VALU kernel).
-int dec_lowrank_slabs(int m, int d_model, int rank);
+int dec_lowrank_slabs(int m, int d_model, int rank, int want);
 
 }  // namespace ffn
