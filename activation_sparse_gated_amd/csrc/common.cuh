@@ -34,6 +34,25 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 v) {
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Copies n elements into LDS, element p from src(p), the block's threads
+// taking elements in turn. Each thread issues up to NB loads before its first
+// LDS store, so a pass costs one memory round trip per NB * blockDim elements
+// (a plain strided copy loop waits for every load before the next).
+// Loads past the end re-read element n - 1 (no branch around a load).
+template <int NB, typename T, typename Src>
+__device__ __forceinline__ void stage_lds(T* dst, int n, Src src) {
+  for (int base = threadIdx.x; base < n; base += NB * blockDim.x) {
+    T v[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) v[b] = src(min(base + b * (int)blockDim.x, n - 1));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int p = base + b * blockDim.x;
+      if (p < n) dst[p] = v[b];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- wave ops
 // Butterfly sum: every lane ends with the same value (fp add is commutative).
 __device__ __forceinline__ float wave_sum(float v) {

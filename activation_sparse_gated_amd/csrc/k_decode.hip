@@ -233,13 +233,15 @@ __device__ __forceinline__ void dec_fg_finish(const uint4 (&a)[kFgMaxSteps], int
 }
 
 // Stages `rows` rows of `cols16` 16-byte chunks (row stride ld16 chunks in
-// global memory) into LDS, zero-filling rows [rows, MAXM).
+// global memory) into LDS, zero-filling rows [rows, MAXM); up to 8 loads per
+// thread in flight.
 template <int MAXM>
 __device__ __forceinline__ void stage_rows(uint4* dst, const uint4* src, int rows, int cols16, size_t ld16) {
-  for (int p = threadIdx.x; p < MAXM * cols16; p += blockDim.x) {
+  constexpr int NB = MAXM < 8 ? 2 * MAXM : 8;
+  stage_lds<NB>(dst, MAXM * cols16, [&](int p) {
     const int m = p / cols16, c = p - m * cols16;
-    dst[p] = m < rows ? src[(size_t)m * ld16 + c] : uint4{0, 0, 0, 0};
-  }
+    return m < rows ? src[(size_t)m * ld16 + c] : uint4{0, 0, 0, 0};
+  });
 }
 
 // ------------------------------------------------------------------ k_dec_lowrank
@@ -408,22 +410,31 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
     if (d.nslab > 0) {
       // t = the first stage's slabs, added in slab order
       const int c4 = d.rank / 4;
-      for (int p = threadIdx.x; p < MAXM * c4; p += blockDim.x) {
-        const int m = p / c4, c = p - m * c4;
-        float4 v[8];                                   // all slab loads in flight together
+      constexpr int NP = MAXM >= 16 ? 1 : 2;          // chunks per thread in flight, 8 slab loads each
+      for (int base = threadIdx.x; base < MAXM * c4; base += NP * blockDim.x) {
+        float4 v[NP][8];
 #pragma unroll
-        for (int z = 0; z < 8; ++z)
-          v[z] = (m < M && z < d.nslab) ? *reinterpret_cast<const float4*>(d.tslab + ((size_t)z * M + m) * d.rank + c * 4)
-                                         : float4{0.f, 0.f, 0.f, 0.f};
-        float4 acc = v[0];
+        for (int i = 0; i < NP; ++i) {
+          const int p = base + i * blockDim.x, m = p / c4, c = p - m * c4;
 #pragma unroll
-        for (int z = 1; z < 8; ++z) {
-          acc.x += v[z].x;
-          acc.y += v[z].y;
-          acc.z += v[z].z;
-          acc.w += v[z].w;
+          for (int z = 0; z < 8; ++z)
+            v[i][z] = (p < MAXM * c4 && m < M && z < d.nslab)
+                          ? *reinterpret_cast<const float4*>(d.tslab + ((size_t)z * M + m) * d.rank + c * 4)
+                          : float4{0.f, 0.f, 0.f, 0.f};
         }
-        reinterpret_cast<float4*>(s_t)[p] = acc;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int p = base + i * blockDim.x;
+          float4 acc = v[i][0];
+#pragma unroll
+          for (int z = 1; z < 8; ++z) {
+            acc.x += v[i][z].x;
+            acc.y += v[i][z].y;
+            acc.z += v[i][z].z;
+            acc.w += v[i][z].w;
+          }
+          if (p < MAXM * c4) reinterpret_cast<float4*>(s_t)[p] = acc;
+        }
       }
     } else {
       stage_rows<MAXM>(reinterpret_cast<uint4*>(s_t), reinterpret_cast<const uint4*>(d.t), M, d.rank / 4, d.rank / 4);
@@ -841,21 +852,33 @@ __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
   // masks and their prefix; x into LDS
   const int per = (nsub + NT - 1) / NT;                 // sub-tiles per thread (<= 4)
   const int s0 = min(nsub, tid * per), s1 = min(nsub, s0 + per);
-  int loc = 0;
-  for (int s = s0; s < s1; ++s) {
-    const uint64_t w = d.umask[s];
-    s_mask[s] = w;
-    loc += __popcll(w);
-  }
+  // the masks' loads and x's go out together (one memory round trip)
+  uint64_t mw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mw[i] = d.umask[min(s0 + i, nsub - 1)];
   {
     uint16_t* sx = reinterpret_cast<uint16_t*>(s_dyn);
     const int c16 = dm / 8;
-    for (int p = tid; p < M * c16; p += NT) {
-      const int m = p / c16, c = p - m * c16;
-      *reinterpret_cast<uint4*>(sx + (size_t)m * ldx + c * 8) =
-          ldg16(reinterpret_cast<const uint16_t*>(d.x) + (size_t)m * dm + c * 8);
+    // M * d / 8 <= 16 * NT (d <= 4096, M <= 16): one unrolled round, the
+    // guards uniform across the block
+    const int n = M * c16;
+    uint4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (u * NT < n) v[u] = ldg16(reinterpret_cast<const uint16_t*>(d.x) + (size_t)min(tid + u * NT, n - 1) * 8);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int p = tid + u * NT, m = p / c16, c = p - m * c16;
+      if (u * NT < n && p < n) *reinterpret_cast<uint4*>(sx + (size_t)m * ldx + c * 8) = v[u];
     }
   }
+  int loc = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (s0 + i < s1) {
+      s_mask[s0 + i] = mw[i];
+      loc += __popcll(mw[i]);
+    }
   int total;
   int run = block_excl_scan<NT>(loc, s_scan, &total);
   for (int s = s0; s < s1; ++s) {

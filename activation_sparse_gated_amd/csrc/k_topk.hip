@@ -31,9 +31,24 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   const float* srow = d.s_buf + (size_t)tok * F;
   float* s_hv = reinterpret_cast<float*>(s_keys + F);
   const float* hrow = d.h_buf + (size_t)tok * F;
-  for (int i = tid; i < F; i += TOPK_THREADS) {
-    s_keys[i] = __float_as_uint(srow[i]);
-    if (HLDS) s_hv[i] = hrow[i];                 // h too, in the same round of loads
+  {
+    // every load of the thread (scores, and h too) in flight before the first
+    // LDS store: one memory round trip
+    float sv[CW], hv[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int i = min(tid + c * TOPK_THREADS, F - 1);  // past the end: a re-read, not stored
+      sv[c] = srow[i];
+      hv[c] = HLDS ? hrow[i] : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int i = tid + c * TOPK_THREADS;
+      if (i < F) {
+        s_keys[i] = __float_as_uint(sv[c]);
+        if (HLDS) s_hv[i] = hv[c];
+      }
+    }
   }
   __syncthreads();
   const int C = (F + TOPK_THREADS - 1) / TOPK_THREADS;    // <= CW
