@@ -54,15 +54,45 @@ __device__ __forceinline__ void stage_lds(T* dst, int n, Src src) {
 }
 
 // ---------------------------------------------------------------- wave ops
-// Butterfly sum: every lane ends with the same value (fp add is commutative).
+// Exchange with a partner lane at butterfly level O (a power of two). Levels
+// 16 and 32 cross DPP rows and go through ds_bpermute; levels 1..8 stay in
+// the VALU as DPP moves: quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2, the
+// half-row mirror (partner lane ^ 7) for 4 and the row mirror (lane ^ 15) for
+// 8. A mirror partner differs from the lane in bit O and in lower bits only,
+// so at each level it still pairs the lanes with bit O clear with those with
+// it set, among lanes whose higher bits agree: butterfly reductions keep their
+// lane-to-value mapping and sum every lane exactly once.
+template <int O>
+__device__ __forceinline__ int wave_xchg_i(int v) {
+  if constexpr (O == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (O == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (O == 4) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  else if constexpr (O == 8) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  else return __shfl_xor(v, O, FFN_WAVE);
+}
+template <int O>
+__device__ __forceinline__ float wave_xchg(float v) {
+  return __int_as_float(wave_xchg_i<O>(__float_as_int(v)));
+}
+
+// Butterfly sum: every lane ends with the same value (fp add is commutative
+// and each level adds two lane groups that already agree).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, FFN_WAVE);
+  v += wave_xchg<32>(v);
+  v += wave_xchg<16>(v);
+  v += wave_xchg<8>(v);
+  v += wave_xchg<4>(v);
+  v += wave_xchg<2>(v);
+  v += wave_xchg<1>(v);
   return v;
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, FFN_WAVE);
+  v += wave_xchg_i<32>(v);
+  v += wave_xchg_i<16>(v);
+  v += wave_xchg_i<8>(v);
+  v += wave_xchg_i<4>(v);
+  v += wave_xchg_i<2>(v);
+  v += wave_xchg_i<1>(v);
   return v;
 }
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
@@ -73,13 +103,17 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 }
 
 // Inclusive scan of ints across the wave (Hillis-Steele with shuffles).
+// Inclusive scan across the wave in DPP moves: a Hillis-Steele scan inside
+// each 16-lane row (row_shr 1, 2, 4, 8; lanes whose source lies before the row
+// add 0), then row_bcast15 adds row 0's total to row 1 and row 2's to row 3,
+// and row_bcast31 adds the first 32 lanes' total to rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, FFN_WAVE);
-    if (l >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
   return v;
 }
 

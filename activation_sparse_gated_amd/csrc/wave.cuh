@@ -7,9 +7,10 @@ namespace ffn {
 
 // ------------------------------------------------------------------ wave transpose reduction
 // Reduces N values per lane across the 64 lanes of a wave. Each halving step
-// keeps one half of the values and swaps the other half with the partner lane,
-// so N - 1 + (6 - log2 N) shuffles replace N full butterflies. Afterwards
-// v[0] of lane L holds the wave total of value index L >> (6 - log2 N).
+// keeps one half of the values and swaps the other half with the partner lane
+// (wave_xchg: DPP inside a 16-lane row, ds_bpermute across rows), so
+// N - 1 + (6 - log2 N) exchanges replace N full butterflies. Afterwards v[0]
+// of lane L holds the wave total of value index L >> (6 - log2 N).
 template <int N, int O>
 struct WaveTRed {
   template <int V>
@@ -20,7 +21,7 @@ struct WaveTRed {
       const float lo = v[j], hi = v[j + N / 2];
       const float keep = upper ? hi : lo;
       const float send = upper ? lo : hi;
-      v[j] = keep + __shfl_xor(send, O, FFN_WAVE);
+      v[j] = keep + wave_xchg<O>(send);
     }
     WaveTRed<N / 2, O / 2>::run(v, lane);
   }
@@ -29,7 +30,7 @@ template <int O>
 struct WaveTRed<1, O> {
   template <int V>
   __device__ __forceinline__ static void run(float (&v)[V], int lane) {
-    v[0] += __shfl_xor(v[0], O, FFN_WAVE);
+    v[0] += wave_xchg<O>(v[0]);
     WaveTRed<1, O / 2>::run(v, lane);
   }
 };
