@@ -54,11 +54,14 @@ __device__ __forceinline__ void stage_lds(T* dst, int n, Src src) {
 }
 
 // ---------------------------------------------------------------- wave ops
-// Exchange with a partner lane at butterfly level O (a power of two). Levels
-// 16 and 32 cross DPP rows and go through ds_bpermute; levels 1..8 stay in
-// the VALU as DPP moves: quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2, the
-// half-row mirror (partner lane ^ 7) for 4 and the row mirror (lane ^ 15) for
-// 8. A mirror partner differs from the lane in bit O and in lower bits only,
+// Exchange with a partner lane at butterfly level O (a power of two), all in
+// the VALU: levels 1..8 as DPP moves, quad_perm [1,0,3,2] and [2,3,0,1] for
+// 1 and 2, the half-row mirror (partner lane ^ 7) for 4 and the row mirror
+// (lane ^ 15) for 8; levels 16 and 32 with gfx950's v_permlane16_swap /
+// v_permlane32_swap on two copies of the value (the swap moves the odd
+// 16-lane rows, or the upper 32 lanes, of one copy into the even rows, or
+// lower lanes, of the other, so each lane finds its partner's value in one of
+// the two results). A mirror partner differs from the lane in bit O and in lower bits only,
 // so at each level it still pairs the lanes with bit O clear with those with
 // it set, among lanes whose higher bits agree: butterfly reductions keep their
 // lane-to-value mapping and sum every lane exactly once.
@@ -68,7 +71,14 @@ __device__ __forceinline__ int wave_xchg_i(int v) {
   else if constexpr (O == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
   else if constexpr (O == 4) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
   else if constexpr (O == 8) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
-  else return __shfl_xor(v, O, FFN_WAVE);
+  else if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? (int)r[0] : (int)r[1];
+  } else {
+    static_assert(O == 32, "butterfly level");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? (int)r[0] : (int)r[1];
+  }
 }
 template <int O>
 __device__ __forceinline__ float wave_xchg(float v) {
