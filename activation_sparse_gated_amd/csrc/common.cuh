@@ -85,6 +85,18 @@ __device__ __forceinline__ float wave_xchg(float v) {
   return __int_as_float(wave_xchg_i<O>(__float_as_int(v)));
 }
 
+// Exact xor partner (lane ^ O), for butterflies over some lane bits only:
+// DPP quad_perm for 1 and 2, the permlane swaps for 16 and 32, ds_bpermute
+// for 4 and 8 (the row mirrors pair lane ^ 7 and lane ^ 15 there).
+template <int O>
+__device__ __forceinline__ float wave_xor(float v) {
+  if constexpr (O == 4 || O == 8) return __shfl_xor(v, O, FFN_WAVE);
+  else return wave_xchg<O>(v);
+}
+
+// Value of a wave-uniform lane `src` (a scalar read, no LDS round trip).
+__device__ __forceinline__ int wave_read(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+
 // Butterfly sum: every lane ends with the same value (fp add is commutative
 // and each level adds two lane groups that already agree).
 __device__ __forceinline__ float wave_sum(float v) {

@@ -99,6 +99,15 @@ __device__ __forceinline__ void dec_gemv_finish(const uint4 (&a)[IPW], int K, in
   }
   WaveTRed<V, 32>::run(v, lane);
   constexpr int SH = 6 - Log2<V>::value;
+  if (P == 1) {
+    // one piece per row: the wave totals are the row values
+    if ((lane & ((1 << SH) - 1)) == 0) {
+      const int j = lane >> SH, i = j / MAXM, m = j % MAXM;
+      s_g[(wave * IPW + i) * MAXM + m] = v[0];
+    }
+    __syncthreads();
+    return;
+  }
   if ((lane & ((1 << SH) - 1)) == 0) {
     const int j = lane >> SH, i = j / MAXM, m = j % MAXM;
     s_part[(wave * IPW + i) * MAXM + m] = v[0];
@@ -453,6 +462,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   }
 
   // ---- selection: one wave per token; the sub-tile's mask is one ballot (R <= 64)
+  constexpr bool ONE = MAXM == 1 && MODE != DEC_SPLIT;
   const int T = d.T, Q = T / R, q = (n0 % T) / R, j = n0 / T;
   const int ntiles = F / T, nsub = F / R;
   for (int m = wave; m < M; m += NW) {             // one wave per token (two at 16 tokens)
@@ -468,6 +478,14 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
       s_bal[m] = bal;
       if (Q > 1)
         store64_relaxed(d.lb + (size_t)m * nsub + sub, ((uint64_t)epoch << 32) | (uint32_t)__popcll(bal));
+    }
+    if constexpr (ONE) {
+      // one token: the union is this ballot, and its row list is written
+      // before the barrier that publishes the ballot
+      if (d.up) {
+        if ((bal >> lane) & 1ull) s_urow[__popcll(bal & lanemask_lt())] = lane;
+        if (lane == 0) d.umask[sub] = bal;
+      }
     }
     if constexpr (MAXM <= 8) break;                   // at most one token a wave
   }
@@ -487,19 +505,21 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) uni |= s_bal[m];
     const int nu = __popcll(uni);
-    if (threadIdx.x == 0) d.umask[sub] = uni;
-    if (MODE == DEC_SPLIT) {
-      // split mode: the activations of the union neurons for k_dec_up
-      for (int p = threadIdx.x; p < R * MAXM; p += NW * 64) {
-        const int r = p / MAXM, m = p % MAXM;
-        if (m < M && ((uni >> r) & 1ull)) {
-          const bool on = (s_bal[m] >> r) & 1ull;
-          d.ad[(size_t)m * F + n0 + r] = on ? s_g[r * MAXM + m] + dec_bias(d, m) : 0.f;
+    if constexpr (!ONE) {
+      if (threadIdx.x == 0) d.umask[sub] = uni;
+      if (MODE == DEC_SPLIT) {
+        // split mode: the activations of the union neurons for k_dec_up
+        for (int p = threadIdx.x; p < R * MAXM; p += NW * 64) {
+          const int r = p / MAXM, m = p % MAXM;
+          if (m < M && ((uni >> r) & 1ull)) {
+            const bool on = (s_bal[m] >> r) & 1ull;
+            d.ad[(size_t)m * F + n0 + r] = on ? s_g[r * MAXM + m] + dec_bias(d, m) : 0.f;
+          }
         }
       }
+      if (wave == 0 && ((uni >> lane) & 1ull)) s_urow[__popcll(uni & lanemask_lt())] = lane;
+      __syncthreads();
     }
-    if (wave == 0 && ((uni >> lane) & 1ull)) s_urow[__popcll(uni & lanemask_lt())] = lane;
-    __syncthreads();
     const int pd = (dm + 511) / 512;
     // one up product: the owner wave reads W_up[n, :] (8 KB at d = 4096) and
     // reduces the dot with every token across its lanes

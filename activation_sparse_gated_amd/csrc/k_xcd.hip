@@ -77,13 +77,13 @@ __global__ __launch_bounds__(64 * kXWaves) void k_xcd_up(const XcdDesc u) {
   for (int j = xr; j < ntiles; j += 8) {
     if (j != xr) load_slots(j);
     const size_t slot0 = ((size_t)t * ntiles + j) * E;
-    const int c = __shfl(cl, j & 63, FFN_WAVE);
+    const int c = wave_read(cl, j & 63);                       // j is wave-uniform
     for (int g0 = 0; g0 < c; g0 += RPG) {
       uint4 w[RPG][CPL];
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
         const int s = g0 + r;
-        const int n = __shfl(nrn[(s >> 6) & 1], s & 63, FFN_WAVE);
+        const int n = wave_read((s >> 6) & 1 ? nrn[1] : nrn[0], s & 63);   // s is wave-uniform
         const uint16_t* row = wup + (size_t)n * d + lane * 8;
 #pragma unroll
         for (int k = 0; k < CPL; ++k) w[r][k] = s < c ? ldg16(row + k * 512) : uint4{0, 0, 0, 0};
@@ -111,6 +111,17 @@ __global__ __launch_bounds__(64 * kXWaves) void k_xcd_up(const XcdDesc u) {
 // neurons' W_down row slices: LPE lanes cover one row's d / 8 columns (16
 // bytes each), so a load instruction covers 64 / LPE rows, and U instructions
 // are in flight. The 64 / LPE row lanes are summed across the wave at the end.
+// acc[k] summed over the lane bits from log2 O up (exact xor butterfly, in
+// level order O, 2 O, .., 32).
+template <int O>
+__device__ __forceinline__ void xor_sum8(float (&acc)[8]) {
+  if constexpr (O < 64) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += wave_xor<O>(acc[k]);
+    xor_sum8<O * 2>(acc);
+  }
+}
+
 template <int LPE>
 __global__ __launch_bounds__(64 * kXWaves) void k_xcd_down(const XcdDesc u) {
   constexpr int EPI = 64 / LPE;                        // rows per load instruction
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(64 * kXWaves) void k_xcd_down(const XcdDesc u) {
         s_h[wave][p] = hh[i];
       }
     }
-    s_ne[wave] = __shfl(incl, 63, FFN_WAVE);
+    s_ne[wave] = wave_read(incl, 63);
   }
   __builtin_amdgcn_wave_barrier();
   float acc[8];
@@ -181,10 +192,7 @@ __global__ __launch_bounds__(64 * kXWaves) void k_xcd_down(const XcdDesc u) {
     }
   }
   // sum the EPI row lanes (lane bits >= log2 LPE), in a fixed order
-#pragma unroll
-  for (int o = LPE; o < 64; o <<= 1)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], o, FFN_WAVE);
+  xor_sum8<LPE>(acc);
   if (sub == 0) {
     uint4 out;
     out.x = f2bf(acc[0]) | (f2bf(acc[1]) << 16);
