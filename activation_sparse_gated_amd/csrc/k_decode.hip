@@ -779,14 +779,19 @@ __global__ __launch_bounds__(kRedThreads) void k_dec_reduce(const DecodeDesc d) 
   const int tid = threadIdx.x, q = tid & 7, r = tid >> 3;
   const int sl = blockIdx.x, M = d.M, dm = d.d, nsub = d.F / d.R;
   // ascending list of the sub-tiles that wrote a partial row
-  const int per = (nsub + kRedThreads - 1) / kRedThreads;
+  const int per = (nsub + kRedThreads - 1) / kRedThreads;   // <= 8 (nsub <= kDecMaxSub)
   const int s0 = min(nsub, tid * per), s1 = min(nsub, s0 + per);
-  int loc = 0;
-  for (int s = s0; s < s1; ++s) loc += d.umask[s] != 0ull;
+  uint64_t w[8];                                         // all mask loads in flight together
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = i < per ? d.umask[min(s0 + i, nsub - 1)] : 0ull;
+  uint32_t nz = 0u;                                      // bit i: sub-tile s0 + i wrote a row
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (w[i] != 0ull && s0 + i < s1) nz |= 1u << i;
   int ne;
-  int pos = block_excl_scan<kRedThreads>(loc, s_scan, &ne);
-  for (int s = s0; s < s1; ++s)
-    if (d.umask[s] != 0ull) s_list[pos++] = s;
+  int pos = block_excl_scan<kRedThreads>(__popc(nz), s_scan, &ne);
+  for (int i = 0; i < s1 - s0; ++i)
+    if ((nz >> i) & 1u) s_list[pos++] = s0 + i;
   __syncthreads();
 
   float acc[MAXM][4];
