@@ -173,7 +173,7 @@ int device_cus() {
 // product through the per-token TwELL kernel), FFN_SPARSE_NO_XCD (1: the
 // per-token sparse kernel at prefill token counts too), FFN_SPARSE_LR_SLABS
 // (slices of d in the decode path's matrix-core low-rank first stage: 1, 2, 4
-// or 8). They change launch shapes and
+// or 8; -1: the VALU first stage up to 8 tokens). They change launch shapes and
 // kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {

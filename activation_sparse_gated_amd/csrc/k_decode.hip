@@ -341,10 +341,12 @@ static int lowrank_mf_waves(int d_model, int S) {
   return 0;
 }
 
-// Slices of d for the matrix-core first stage (0: not applicable). `want`
-// (a power of two, 0 for the default) asks for a slice count.
+// Slices of d for the matrix-core first stage (0: not applicable, or the VALU
+// kernel). `want` (a power of two, 0 for the default, negative for the VALU
+// kernel up to 8 tokens) asks for a slice count.
 int dec_lowrank_slabs(int m, int d_model, int rank, int want) {
   if (m < 2 || m > kDecMaxM || rank % 16 != 0 || d_model % 512 != 0) return 0;
+  if (want < 0 && m <= 8) return 0;                    // the VALU first stage (t in one piece)
   int S = want > 0 ? want : 8;                       // 2, 4 or 8 slabs measure within 1 us at 2..8 tokens
   S = std::max(1, std::min(S, 8));
   while (S < 8 && lowrank_mf_waves(d_model, S) == 0) S *= 2;
