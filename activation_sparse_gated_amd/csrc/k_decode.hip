@@ -861,9 +861,7 @@ constexpr int kUpNB = 3;                               // groups of 16 entries i
 constexpr int kUpMaxEnt = 128;                         // entries per workgroup (F <= 128 * kUpGrid)
 
 __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
-  extern __shared__ uint4 s_dyn[];                     // x: M rows of d + 8 bf16
-  __shared__ uint64_t s_mask[kDecMaxSub];
-  __shared__ int s_pre[kDecMaxSub];
+  extern __shared__ uint4 s_dyn[];                     // x: M rows of d + 8 bf16; masks; prefixes
   __shared__ int s_scan[kUpWaves];
   __shared__ int s_nrn[kUpMaxEnt];
   __shared__ f32x4_t s_acc[kUpWaves][kUpNB][64];
@@ -875,6 +873,9 @@ __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
   const int k0 = wave * steps * 32;                    // first element of the wave's K range
   const int ldx = dm + 8;                              // LDS row stride of x (elements)
   constexpr int NT = 64 * kUpWaves;
+  // the sub-tile masks and their prefixes follow x (nsub entries each)
+  uint64_t* s_mask = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(s_dyn) + (size_t)M * ldx * 2);
+  int* s_pre = reinterpret_cast<int*>(s_mask + nsub);
 
   // masks and their prefix; x into LDS
   const int per = (nsub + NT - 1) / NT;                 // sub-tiles per thread (<= 4)
@@ -1280,7 +1281,12 @@ hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t dec_up_lds(const DecodeDesc& d) { return (size_t)d.M * (d.d + 8) * 2; }
+// Dynamic LDS of k_dec_up: x (M rows of d + 8 bf16; 16-byte multiple for d a
+// multiple of 256), then the nsub sub-tile masks and prefixes.
+size_t dec_up_lds(const DecodeDesc& d) { return (size_t)d.M * (d.d + 8) * 2 + (size_t)(d.F / d.R) * 12; }
+// Static LDS of k_dec_up (s_scan, s_nrn, s_acc) and gfx950's LDS per workgroup.
+constexpr size_t kUpStaticLds = kUpWaves * 4 + kUpMaxEnt * 4 + (size_t)kUpWaves * kUpNB * 64 * 16;
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
 
 // Sub-tile rows of the decode gate for m tokens, gate contraction K and
 // TwELL tile T (0: the decode shape does not apply); *ipw gets the VALU
@@ -1296,12 +1302,13 @@ int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw) {
 }
 
 // Shapes the split sequence handles: d a multiple of 256 and at most 4096
-// (a wave's eighth of d in registers), the padded list within the up grid's
-// groups and each down workgroup's entries within its id buffer.
+// (a wave's eighth of d in registers), the tokens' x and the sub-tile masks
+// within the up kernel's LDS (16 tokens at d = 4096), the padded list within
+// the up grid's groups and each down workgroup's entries within its id buffer.
 bool dec_split_ok(const DecodeDesc& d) {
   const int nkb = (d.F + 31) / 32;
   return d.d % 256 == 0 && d.d <= 32 * kUpWaves * kUpMaxSteps && (d.F + kUpGrid - 1) / kUpGrid <= kUpMaxEnt &&
-         dec_up_lds(d) <= 80 * 1024 &&
+         dec_up_lds(d) + kUpStaticLds + 512 <= kLdsPerWorkgroup &&
          d.F / d.R <= kDecMaxSub && d.ngroups >= 1 && d.ngroups <= 32 && (nkb + d.ngroups - 1) / d.ngroups * 32 <= kDown2MaxIds &&
          d.ldh >= nkb * 32;
 }

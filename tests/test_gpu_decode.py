@@ -46,6 +46,8 @@ DECODE = [
     ("c2", 16, dict(d=2048, f=4096, T=128, E=64)),           # 9..16 tokens: split sequence, two tokens a wave
     ("c2", 11, dict(d=512, f=2048, T=64, E=8)),
     ("c3", 13, dict(d=1024, f=2048, rank=512, T=128, E=16)),
+    ("c3", 16, dict(d=4096, f=2048, rank=512, T=128, E=16)),  # 16 tokens' x at d = 4096 in the up kernel's LDS
+    ("c3", 12, dict(d=4096, f=4096, rank=512, T=64, E=8)),
 ]
 
 
