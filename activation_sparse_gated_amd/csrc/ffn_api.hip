@@ -166,7 +166,7 @@ int device_cus() {
 // Optional launch-shape overrides (0 = automatic), read once at init from the
 // environment: FFN_SPARSE_GATE_NT, FFN_SPARSE_GATE_WAVES, FFN_SPARSE_UD_SPLIT,
 // FFN_SPARSE_UD_GROUP, FFN_SPARSE_UD_WAVES, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
-// at decode sizes), FFN_SPARSE_NO_DECODE (1: the general kernels at 1..8 tokens
+// at decode sizes), FFN_SPARSE_NO_DECODE (1: the general kernels at 1..16 tokens
 // too), FFN_SPARSE_DEC_MODE (1 + DecMode: force the decode down-projection
 // organisation), FFN_SPARSE_NO_PREFILL_GEMM (1: the decode-shaped MFMA kernel
 // for 128+ tokens as well), FFN_SPARSE_NO_TOPK_DOWN (1: top-k selection's down
@@ -620,10 +620,11 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
   return hip_status(launch_gemm(g, e, s));
 }
 
-// Decode path (k_decode.hip) for bf16 bias / threshold configs at 1..8
-// tokens: 16-wave gate workgroups of R = 16 * IPW / P rows (P = pieces of 512
-// elements per gate row, IPW pieces per wave, R dividing the TwELL tile), all
-// token inputs staged in LDS.
+// Decode path (k_decode.hip) for bf16 bias / threshold configs at 1..16
+// tokens: gate workgroups of R rows (16 waves for one token, 8 otherwise; R =
+// waves * IPW / P on the VALU, P = pieces of 512 elements per gate row, or 32
+// rows on matrix cores; R divides the TwELL tile), then the partial-row,
+// chunk or split organisation of the up and down products.
 bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   const auto& c = h->cfg;
   if (c.dtype != FFN_BF16 || c.sel == FFN_SEL_TOPK_WINA || m < 1 || m > kDecMaxM) return false;

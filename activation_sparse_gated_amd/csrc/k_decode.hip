@@ -1,5 +1,5 @@
-// Decode path of the sparse gated FFN on gfx950: bf16 weights, at most 8
-// tokens, ReLU gate with a bias or threshold selection.
+// Decode path of the sparse gated FFN on gfx950: bf16 weights, 1..16 tokens,
+// ReLU gate with a bias or threshold selection.
 //
 // At a handful of tokens every product is a memory-bound weight stream
 // (about one FLOP per byte), so the path is organised around reading each
@@ -9,34 +9,38 @@
 //   k_dec_lowrank  t = V x (low-rank gate only; LoPA page, "How LoPA Gating
 //                  Restructures FFN Computation"): 1 KB pieces of V's rows,
 //                  several per wave, reduced in LDS; from two tokens
-//                  k_dec_lowrank_mf, the same product on matrix cores.
+//                  k_dec_lowrank_mf, the same product on matrix cores, as
+//                  fp32 slabs over slices of d.
 //   k_dec_gate     one workgroup per sub-tile of R gate rows (R divides the
 //                  TwELL tile width T). The gate rows are streamed and dotted
-//                  with every token; the epilogue applies the selection and
-//                  writes the TwELL pack straight from LDS (Sparser/Faster/
-//                  Lighter page, "TwELL 減掉轉換開銷"): a sub-tile learns its
-//                  slot offset inside the TwELL tile from the counts the
-//                  earlier sub-tiles publish (epoch-tagged words). Before it
-//                  waits for those, the workgroup computes the up products of
-//                  its neurons that are active for any token, u = <W_up[i,:], x>
-//                  (each W_up row read once for all tokens), stores h = a * u
-//                  in the dense hidden array h[token, neuron] and the
-//                  sub-tile's union mask (one 64-bit word). A token
-//                  whose tile overflows the ELL width still has every active
-//                  neuron in the list, so no dense backup is needed at these
-//                  token counts (Sparser/Faster/Lighter page, "Hybrid
+//                  with every token (VALU, or matrix cores from 5 tokens with a
+//                  low-rank gate and from 9 with a full one); the epilogue
+//                  applies the selection and writes the TwELL pack straight
+//                  from LDS (Sparser/Faster/Lighter page, "TwELL 減掉轉換開銷"):
+//                  a sub-tile learns its slot offset inside the TwELL tile from
+//                  the counts the earlier sub-tiles publish (epoch-tagged
+//                  words). Before it waits for those, the workgroup starts on
+//                  the neurons active for any token (the sub-tile's union mask,
+//                  one 64-bit word), in one of three organisations:
+//     partial rows (one token): it reads the up and down rows of its active
+//                  neurons in one memory round and writes one partial y row;
+//                  k_dec_reduce adds the non-empty rows in sub-tile order.
+//     chunk:       it stores h = a * <W_up[i,:], x> densely; k_dec_down (one
+//                  workgroup per 16-byte column chunk of y) reads the union
+//                  masks, deals their set bits to its threads and accumulates
+//                  h * W_down^T[i, chunk] for every token.
+//     split (2..16 tokens): it publishes the activations only; k_dec_up deals
+//                  the union list evenly over 256 workgroups and runs the up
+//                  products on matrix cores (bf16 h per list entry), and
+//                  k_dec_down2 + k_dec_reduce2 run the down products on matrix
+//                  cores over 64-column slices of y and entry groups.
+//                  A token whose tile overflows the ELL width still has every
+//                  active neuron in the lists, so no dense backup is needed at
+//                  these token counts (Sparser/Faster/Lighter page, "Hybrid
 //                  應對非均勻稀疏", routes busy rows; here they cost one more
-//                  list entry per neuron).
-//   k_dec_down     one workgroup per 16-byte column chunk of y: it reads the
-//                  union masks in one round, deals their set bits to its
-//                  threads (prefix of popcounts in LDS), then reads h and the
-//                  rows in a second round and accumulates h * W_down^T[i, chunk]
-//                  for every token, reduces across its lanes in a fixed
-//                  order and writes y once. No partial rows, no atomics, and
-//                  the result is bitwise reproducible. The eight chunks of a
-//                  128-byte line go to the same XCD (workgroups are dealt to
-//                  the eight XCDs round-robin), so its L2 serves the line to
-//                  all of them. An extra workgroup routes the pack.
+//                  list entry per neuron). Every y element is summed in a fixed
+//                  order, so y is bitwise reproducible; the last kernel's extra
+//                  workgroup routes the pack.
 #include <algorithm>
 #include <type_traits>
 
