@@ -70,6 +70,7 @@ struct Workspace {
   uint64_t* umask;       // [F / 2] decode sub-tiles: neurons active for any token
   float* hd;             // [kDecMaxM x F] decode hidden values (column-chunk mode)
   float* dec_part;       // [F / R x min(max_m, 8) x d] decode partial y rows
+  size_t dec_part_rows;  // rows of d floats in dec_part
   float* xh;             // [M x F / T x E] prefill: h per pack slot (XCD-sliced up / down)
   float* kpart;          // [kPfSplitK x M x d] prefill dense backup: split-K partials (or null)
   int32_t* ul_total;     // [1] decode split mode: union-list length
@@ -130,6 +131,7 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
     const size_t rows_split = c.dtype == FFN_BF16 ? 32 * std::min<size_t>(M, kDecMaxM) : 0;
     const size_t rows = std::max(rows_part, rows_split);
     w.dec_part = (float*)take(rows ? rows * d * sizeof(float) : 16);
+    w.dec_part_rows = rows;
   }
   // split-K partials of the dense backup's down product at prefill sizes
   const bool can_route = !topk && c.ell_w < c.tile_w;
@@ -173,12 +175,13 @@ int device_cus() {
 // product through the per-token TwELL kernel), FFN_SPARSE_NO_XCD (1: the
 // per-token sparse kernel at prefill token counts too), FFN_SPARSE_LR_SLABS
 // (slices of d in the decode path's matrix-core low-rank first stage: 1, 2, 4
-// or 8; -1: the VALU first stage up to 8 tokens). They change launch shapes and
+// or 8; -1: the VALU first stage up to 8 tokens), FFN_SPARSE_DEC_IPW (gate row
+// pieces per wave in the decode gate: 1, 2, 4, or 8 for one token). They change launch shapes and
 // kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {
   int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0,
-      no_topk_down = 0, no_xcd = 0, lr_slabs = 0;
+      no_topk_down = 0, no_xcd = 0, lr_slabs = 0, dec_ipw = 0;
 };
 
 static int env_int(const char* name) {
@@ -638,7 +641,11 @@ bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   d.rank = c.rank;
   d.K = c.rank ? c.rank : c.d_model;
   d.sel = c.sel;
-  d.R = dec_gate_rows(d.K, c.tile_w, m, c.rank > 0, &d.ipw);   // at most 64 sub-tiles per TwELL tile
+  d.R = dec_gate_rows(d.K, c.tile_w, m, c.rank > 0, &d.ipw, h->tune.dec_ipw);   // at most 64 sub-tiles per TwELL tile
+  // a forced piece count may give more partial rows than the workspace holds
+  // (it is sized for the default shapes): then the default shape
+  if (d.R && h->tune.dec_ipw && (size_t)(d.F / d.R) * std::min(m, 8) > h->ws.dec_part_rows)
+    d.R = dec_gate_rows(d.K, c.tile_w, m, c.rank > 0, &d.ipw);
   if (d.R == 0 || d.F / d.R > 2048) return false;
   d.a_gate = c.rank ? h->u : h->w_gate;
   d.v = h->v;
@@ -885,6 +892,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.no_topk_down = env_int("FFN_SPARSE_NO_TOPK_DOWN");
   h->tune.no_xcd = env_int("FFN_SPARSE_NO_XCD");
   h->tune.lr_slabs = env_int("FFN_SPARSE_LR_SLABS");
+  h->tune.dec_ipw = env_int("FFN_SPARSE_DEC_IPW");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;

@@ -245,8 +245,8 @@ hipError_t launch_dec_down2(const DecodeDesc& d, hipStream_t s);   // + the grou
 int dec_down2_groups(int d_model, int d_ff);
 // Gate rows per decode workgroup for a gate contraction length K, TwELL tile
 // width T and m tokens (0 when the decode shape does not apply).
-int dec_rows_per_wg(int K, int T, int m, int* ipw);
-int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw);
+int dec_rows_per_wg(int K, int T, int m, int* ipw, int want_ipw = 0);
+int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw, int want_ipw = 0);
 // Slices of d of the matrix-core first stage for m tokens (0: the VALU kernel).
 int dec_lowrank_slabs(int m, int d_model, int rank, int want);
 

@@ -26,15 +26,17 @@ def say(*a):
 
 
 # (workload, tokens, overrides): gate rows per workgroup R = NW * IPW / P with
-# P = pieces of 512 per gate row, NW = 16 waves for one token and 8 otherwise;
-# the comment gives (P, R, sub-tiles per TwELL tile)
+# P = pieces of 512 per gate row, NW = 16 waves and IPW up to 8 for one token,
+# 8 waves and IPW up to 4 otherwise; the comment gives (P, R, sub-tiles per
+# TwELL tile)
 DECODE = [
     ("c2", 1, dict(d=256, f=1024, T=128, E=16)),          # P1 R64 Q2
     ("c2", 3, dict(d=512, f=2048, T=64, E=8)),            # P1 R32 Q2
     ("c2", 8, dict(d=1024, f=2048, T=128, E=16)),         # P2 R16 Q8
     ("c2", 2, dict(d=2048, f=4096, T=128, E=64)),         # P4 R8  Q16
     ("c2", 4, dict(d=4096, f=2048, T=64, E=8)),           # P8 R4  Q16
-    ("c2", 1, dict(d=4096, f=2048, T=64, E=8)),           # P8 R8  Q8
+    ("c2", 1, dict(d=4096, f=2048, T=64, E=8)),           # P8 R16 Q4
+    ("c2", 1, dict(d=2048, f=4096, T=128, E=64)),         # P4 R32 Q4
     ("c2", 4, dict(d=192, f=768, T=32, E=4)),             # P1 R32 Q1, partial piece
     ("c2", 7, dict(d=256, f=1024, T=16, E=16)),           # P1 R16 Q1
     ("c3", 1, dict(d=512, f=1792, rank=64, T=128, E=16)),
