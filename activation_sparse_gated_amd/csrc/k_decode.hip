@@ -505,6 +505,38 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   uint64_t tw = 0;
   if (tok_wave && lane < q) tw = load64_relaxed(twp);
 
+  // TwELL pack of token m: this sub-tile's entries at their offset inside
+  // tile j (wave-wide: one lane per row of the sub-tile)
+  auto write_pack = [&](int m) {
+    const uint64_t bal = s_bal[m];
+    int pre = 0;
+    if (Q > 1) {
+      // the wave's first token's first read was issued early
+      const uint64_t* wp = d.lb + (size_t)m * nsub + (size_t)j * Q + lane;
+      const uint64_t first = m == wave ? tw : (lane < q ? load64_relaxed(wp) : 0ull);
+      pre = wave_sum_i(lane < q ? lb_count(wp, epoch, first) : 0);
+    }
+    const size_t slot0 = ((size_t)m * ntiles + j) * d.E;
+    const bool act = (bal >> lane) & 1ull;
+    const int pos = pre + __popcll(bal & lanemask_lt());
+    if (act && pos < d.E) {
+      d.idx[slot0 + pos] = (uint16_t)(q * R + lane);
+      const float z = s_g[lane * MAXM + m] + dec_bias(d, m);
+      reinterpret_cast<uint16_t*>(d.val)[slot0 + pos] = (uint16_t)f2bf(z);
+    }
+    if (q == Q - 1) {
+      const int total = pre + __popcll(bal);
+      if (lane == 0) d.cnt[(size_t)m * ntiles + j] = total;
+      for (int s = min(total, d.E) + lane; s < d.E; s += 64) {
+        d.idx[slot0 + s] = 0xFFFF;
+        reinterpret_cast<uint16_t*>(d.val)[slot0 + s] = 0;
+      }
+    }
+  };
+  // one token, partial rows: wave 0 writes the pack while the first batch's
+  // row loads are in flight (the up rows go to waves 1.., wave 0 last)
+  bool packed = false;
+
   // ---- up products of the neurons active for any token: h = a * <W_up[i,:], x>
   if (d.up) {
     uint64_t uni = 0ull;
@@ -585,7 +617,12 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
           const int k = k0 + i;
           dw[i] = (k < nu && colt) ? *reinterpret_cast<const DV*>(wdn + (size_t)(n0 + s_urow[k]) * dm) : DV{};
         }
-        for (int k = k0 + wave; k < min(nu, k0 + DB); k += NW) up_row(k, true);
+        if constexpr (ONE) {
+          if (k0 == 0 && wave == 0) write_pack(0);
+          for (int k = k0 + (wave + NW - 1) % NW; k < min(nu, k0 + DB); k += NW) up_row(k, true);
+        } else {
+          for (int k = k0 + wave; k < min(nu, k0 + DB); k += NW) up_row(k, true);
+        }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < DB; ++i) {
@@ -608,6 +645,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
         }
         __syncthreads();                                // s_h is rewritten by the next batch
       }
+      if (ONE && nu > 0) packed = true;
       if (nu > 0 && colt) {
 #pragma unroll
         for (int m = 0; m < MAXM; ++m)
@@ -621,33 +659,12 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
     }
   }
 
-  // ---- TwELL pack: this sub-tile's entries at their offset inside tile j
-  for (int m = wave; m < M; m += NW) {
-    const uint64_t bal = s_bal[m];
-    int pre = 0;
-    if (Q > 1) {
-      // the wave's first token's first read was issued early
-      const uint64_t* wp = d.lb + (size_t)m * nsub + (size_t)j * Q + lane;
-      const uint64_t first = m == wave ? tw : (lane < q ? load64_relaxed(wp) : 0ull);
-      pre = wave_sum_i(lane < q ? lb_count(wp, epoch, first) : 0);
+  // ---- TwELL pack (unless written during the up and down loads above)
+  if (!packed) {
+    for (int m = wave; m < M; m += NW) {
+      write_pack(m);
+      if constexpr (MAXM <= 8) break;                 // at most one token a wave
     }
-    const size_t slot0 = ((size_t)m * ntiles + j) * d.E;
-    const bool act = (bal >> lane) & 1ull;
-    const int pos = pre + __popcll(bal & lanemask_lt());
-    if (act && pos < d.E) {
-      d.idx[slot0 + pos] = (uint16_t)(q * R + lane);
-      const float z = s_g[lane * MAXM + m] + dec_bias(d, m);
-      reinterpret_cast<uint16_t*>(d.val)[slot0 + pos] = (uint16_t)f2bf(z);
-    }
-    if (q == Q - 1) {
-      const int total = pre + __popcll(bal);
-      if (lane == 0) d.cnt[(size_t)m * ntiles + j] = total;
-      for (int s = min(total, d.E) + lane; s < d.E; s += 64) {
-        d.idx[slot0 + s] = 0xFFFF;
-        reinterpret_cast<uint16_t*>(d.val)[slot0 + s] = 0;
-      }
-    }
-    if constexpr (MAXM <= 8) break;                   // at most one token a wave
   }
 }
 
