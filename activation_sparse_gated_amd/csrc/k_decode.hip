@@ -405,15 +405,19 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   // matrix cores (t split into bf16 hi + lo); otherwise the VALU GEMV (at 2..4
   // tokens it is as fast, with fewer barriers)
   constexpr bool MF = LOWRANK && MAXM >= 8 && NW == 8;
-  constexpr int MF_DS = 4;                              // steps per wave: K = 512, two row groups
-  const bool use_mf = MF && R == 32 && K == 512;
+  // K = 512 (16 steps) over the waves of a row group: 32-row sub-tiles (two
+  // groups of four waves, 4 steps each) or, with IPW = 8, 64-row sub-tiles
+  // (four groups of two waves, 8 steps each)
+  constexpr int MF_NG = IPW == 8 ? 4 : 2;
+  constexpr int MF_DS = 16 / (NW / MF_NG);
+  const bool use_mf = MF && R == 16 * MF_NG && K == 512;
   const bool use_fg = FG && R == 32 && K % 128 == 0 && K <= 128 * kFgMaxSteps;
   uint4 a[IPW];
   uint4 am[MF ? MF_DS : 1];
   uint4 af[FG ? kFgMaxSteps : 1];
   if constexpr (MF) {
-    if (use_mf) dec_mfma_issue<8, 2, MF_DS>(reinterpret_cast<const uint16_t*>(d.a_gate), K, n0, am);
-    else dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
+    if (use_mf) dec_mfma_issue<8, MF_NG, MF_DS>(reinterpret_cast<const uint16_t*>(d.a_gate), K, n0, am);
+    else if constexpr (IPW <= 4) dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
   } else if constexpr (FG) {
     if (use_fg) dec_fg_issue(reinterpret_cast<const uint16_t*>(d.a_gate), K, n0, af);
     else dec_gemv_issue<NW, IPW>(reinterpret_cast<const uint16_t*>(d.a_gate), F, K, P, n0, a);
@@ -458,8 +462,8 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
   const uint32_t epoch = __hip_atomic_load(&d.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   __syncthreads();
   if constexpr (MF) {
-    if (use_mf) dec_mfma_finish<8, 2, MF_DS, MAXM>(am, K, s_t, M, s_acc, s_g);
-    else dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
+    if (use_mf) dec_mfma_finish<8, MF_NG, MF_DS, MAXM>(am, K, s_t, M, s_acc, s_g);
+    else if constexpr (IPW <= 4) dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
   } else if constexpr (FG) {
     if (use_fg) dec_fg_finish<MAXM>(af, K, s_x, M, s_acc, s_g);
     else dec_gemv_finish<NW, IPW, MAXM, LOWRANK>(a, K, P, s_x, s_t, s_part, s_g);
@@ -1259,7 +1263,10 @@ static hipError_t go_gate_m(const DecodeDesc& d, hipStream_t s) {
     case 2: return go_gate<2, MAXM>(d, s);
     case 4: return go_gate<4, MAXM>(d, s);
     case 8:
-      if constexpr (MAXM == 1) return go_gate<8, MAXM>(d, s);   // one token only
+      if constexpr (MAXM == 1) return go_gate<8, MAXM>(d, s);   // one token
+      if constexpr (MAXM >= 8) {                                 // the low-rank gate on matrix cores, 64-row sub-tiles
+        if (d.rank && d.K == 512 && d.R == 64) return go_gate_mode<8, MAXM, true>(d, s);
+      }
       break;
   }
   return hipErrorInvalidValue;
@@ -1307,6 +1314,12 @@ constexpr size_t kLdsPerWorkgroup = 160 * 1024;
 // pieces per wave. From 9 tokens a full gate uses 32-row sub-tiles on matrix
 // cores.
 int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw, int want_ipw) {
+  // low rank on matrix cores (5..16 tokens, K = 512): 64-row sub-tiles unless
+  // 4 pieces a wave (32 rows) are asked for
+  if (lowrank && m > 4 && m <= kDecMaxM && K == 512 && T % 64 == 0 && T / 64 <= 64 && want_ipw != 4) {
+    if (ipw) *ipw = 8;
+    return 64;
+  }
   if (m > 8 && !lowrank) {
     if (K % 128 != 0 || K > 128 * kFgMaxSteps || T % 32 != 0 || T / 32 > 64) return 0;
     if (ipw) *ipw = 4;
