@@ -1264,9 +1264,9 @@ static hipError_t go_gate_m(const DecodeDesc& d, hipStream_t s) {
     case 4: return go_gate<4, MAXM>(d, s);
     case 8:
       if constexpr (MAXM == 1) return go_gate<8, MAXM>(d, s);   // one token
-      if constexpr (MAXM >= 8) {                                 // the low-rank gate on matrix cores, 64-row sub-tiles
-        if (d.rank && d.K == 512 && d.R == 64) return go_gate_mode<8, MAXM, true>(d, s);
-      }
+      // several tokens: the low-rank gate over 64-row sub-tiles (on matrix
+      // cores from 5 tokens)
+      if (d.rank && d.K == 512 && d.R == 64) return go_gate_mode<8, MAXM, true>(d, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -1314,9 +1314,9 @@ constexpr size_t kLdsPerWorkgroup = 160 * 1024;
 // pieces per wave. From 9 tokens a full gate uses 32-row sub-tiles on matrix
 // cores.
 int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw, int want_ipw) {
-  // low rank on matrix cores (5..16 tokens, K = 512): 64-row sub-tiles unless
-  // 4 pieces a wave (32 rows) are asked for
-  if (lowrank && m > 4 && m <= kDecMaxM && K == 512 && T % 64 == 0 && T / 64 <= 64 && want_ipw != 4) {
+  // low rank, K = 512, 2..16 tokens (matrix cores from 5): 64-row sub-tiles
+  // (8 pieces a wave) unless 4 pieces a wave (32 rows) are asked for
+  if (lowrank && m >= 2 && m <= kDecMaxM && K == 512 && T % 64 == 0 && T / 64 <= 64 && want_ipw != 4) {
     if (ipw) *ipw = 8;
     return 64;
   }
