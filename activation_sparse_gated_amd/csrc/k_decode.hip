@@ -499,7 +499,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
     }
     if constexpr (MAXM <= 8) break;                   // at most one token a wave
   }
-  if (threadIdx.x < MAXM && threadIdx.x >= M) s_bal[threadIdx.x] = 0ull;
+  if ((int)threadIdx.x < MAXM && (int)threadIdx.x >= M) s_bal[threadIdx.x] = 0ull;
   __syncthreads();
 
   // first read of the earlier sub-tiles' counts of tile j (per token), while

@@ -23,10 +23,11 @@ constexpr int TOPK_THREADS = 1024;
 template <int CW, bool HLDS>
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   extern __shared__ uint32_t s_keys[];           // F score bit patterns, then the kept ranks; h (HLDS)
-  __shared__ uint32_t s_hist[2048];
+  __shared__ uint32_t s_hist[2][2048];           // radix histograms, alternating by pass
   __shared__ int s_tstart[1024 + 1];             // kept count before each tile (F / T <= 1024)
   __shared__ int s_scan[16];
-  __shared__ uint32_t s_digit, s_above;
+  __shared__ int s_wtot[2][TOPK_THREADS / 64];   // per-wave histogram sums, alternating by pass
+  __shared__ uint32_t s_digit[3], s_above[3];
   const int tok = blockIdx.x, F = d.F, tid = threadIdx.x;
   const float* srow = d.s_buf + (size_t)tok * F;
   float* s_hv = reinterpret_cast<float*>(s_keys + F);
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
         if (HLDS) s_hv[i] = hv[c];
       }
     }
+    for (int i = tid; i < 2048; i += TOPK_THREADS) s_hist[0][i] = 0u;   // the first pass's histogram
   }
   __syncthreads();
   const int C = (F + TOPK_THREADS - 1) / TOPK_THREADS;    // <= CW
@@ -62,27 +64,37 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   int need = k;                                   // elements still to take at the current prefix
   if (k > 0 && k < F) {
     const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
+    // three barriers a pass: after the histogram, after the per-wave sums,
+    // after the cut digit; the histogram and the sums alternate between two
+    // buffers, and the next pass's histogram is cleared while this one is read
+    const int lane = tid & 63, wave = tid >> 6;
     for (int pass = 0; pass < 3; ++pass) {
       const int sh = shifts[pass], nb = 1 << widths[pass];
-      for (int i = tid; i < 2048; i += TOPK_THREADS) s_hist[i] = 0u;
-      __syncthreads();
+      uint32_t* hist = s_hist[pass & 1];
 #pragma unroll
       for (int c = 0; c < CW; ++c)
-        if (c < n && (key[c] & pmask) == prefix) atomicAdd(&s_hist[(key[c] >> sh) & (nb - 1)], 1u);
+        if (c < n && (key[c] & pmask) == prefix) atomicAdd(&hist[(key[c] >> sh) & (nb - 1)], 1u);
       __syncthreads();
       // cumulative counts from the largest digit down: thread t owns digits
       // nb-1-2t and nb-2-2t
       const int d0 = nb - 1 - 2 * tid, d1 = d0 - 1;
-      const int c0 = d0 >= 0 ? (int)s_hist[d0] : 0, c1 = d1 >= 0 ? (int)s_hist[d1] : 0;
-      int total;
-      const int ex = block_excl_scan<TOPK_THREADS>(c0 + c1, s_scan, &total);
-      if (d0 >= 0 && ex < need && need <= ex + c0) { s_digit = (uint32_t)d0; s_above = (uint32_t)ex; }
-      if (d1 >= 0 && ex + c0 < need && need <= ex + c0 + c1) { s_digit = (uint32_t)d1; s_above = (uint32_t)(ex + c0); }
+      const int c0 = d0 >= 0 ? (int)hist[d0] : 0, c1 = d1 >= 0 ? (int)hist[d1] : 0;
+      const int incl = wave_incl_scan(c0 + c1);
+      if (lane == 63) s_wtot[pass & 1][wave] = incl;
+      if (pass < 2)
+        for (int i = tid; i < 2048; i += TOPK_THREADS) s_hist[(pass + 1) & 1][i] = 0u;
       __syncthreads();
-      prefix |= s_digit << sh;
+      int base = 0;
+#pragma unroll
+      for (int w = 0; w < TOPK_THREADS / 64; ++w)
+        if (w < wave) base += s_wtot[pass & 1][w];
+      const int ex = base + incl - (c0 + c1);
+      if (d0 >= 0 && ex < need && need <= ex + c0) { s_digit[pass] = (uint32_t)d0; s_above[pass] = (uint32_t)ex; }
+      if (d1 >= 0 && ex + c0 < need && need <= ex + c0 + c1) { s_digit[pass] = (uint32_t)d1; s_above[pass] = (uint32_t)(ex + c0); }
+      __syncthreads();
+      prefix |= s_digit[pass] << sh;
       pmask |= (uint32_t)(nb - 1) << sh;
-      need -= (int)s_above;
-      __syncthreads();
+      need -= (int)s_above[pass];
     }
   }
 
