@@ -739,7 +739,10 @@ UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const f
   const int gcap = std::max(1, std::min(std::min(ntiles, 64), kUpdownCap / per_tile));
   const long long units = (long long)m * ntiles;
   int G = 1, S = 1;
-  if (units > 2LL * h->cus) G = (int)std::min<long long>(gcap, units / (2LL * h->cus));
+  // tiles per group rounded up, so that the workgroups fit in two per CU
+  // (rounded down, 24 tokens at the LoPA shape took 552 workgroups, a third
+  // round on some CUs: 108.6 against 93.2 us)
+  if (units > 2LL * h->cus) G = (int)std::min<long long>(gcap, (units + 2LL * h->cus - 1) / (2LL * h->cus));
   if (h->tune.ud_group > 0) G = std::min(gcap, h->tune.ud_group);
   if (h->tune.ud_split > 0) S = std::min(16, h->tune.ud_split);
   const int epc = c.dtype == FFN_BF16 ? 8 : 4;
