@@ -739,10 +739,24 @@ UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const f
   const int gcap = std::max(1, std::min(std::min(ntiles, 64), kUpdownCap / per_tile));
   const long long units = (long long)m * ntiles;
   int G = 1, S = 1;
-  // tiles per group rounded up, so that the workgroups fit in two per CU
-  // (rounded down, 24 tokens at the LoPA shape took 552 workgroups, a third
-  // round on some CUs: 108.6 against 93.2 us)
-  if (units > 2LL * h->cus) G = (int)std::min<long long>(gcap, (units + 2LL * h->cus - 1) / (2LL * h->cus));
+  if (units > 2LL * h->cus) {
+    // Tiles per group: the workgroups should fit two per CU (a third round on
+    // some CUs cost 24 tokens at the LoPA shape 108.6 against 93.2 us). With
+    // one phase, workgroup b = token * groups + group runs on XCD b mod 8, so a
+    // group count that is a multiple of 8 keeps each group's weight rows on
+    // one XCD's L2: that grouping is taken when it still gives 1.5 workgroups
+    // per CU (56 tokens: 137 against 181 us), else the finest grouping that
+    // fits (40 tokens: 118 against 134 us).
+    auto groups = [&](int g) { return (long long)((ntiles + g - 1) / g); };
+    int aligned = 0, fit = 0;
+    for (int g = 1; g <= gcap; ++g) {
+      const long long wg = (long long)m * groups(g);
+      if (!fit && wg <= 2LL * h->cus) fit = g;
+      if (!aligned && groups(g) % 8 == 0 && wg <= 2LL * h->cus) aligned = g;
+    }
+    if (aligned && (long long)m * groups(aligned) * 2 >= 3LL * h->cus) G = aligned;
+    else G = fit ? fit : gcap;
+  }
   if (h->tune.ud_group > 0) G = std::min(gcap, h->tune.ud_group);
   if (h->tune.ud_split > 0) S = std::min(16, h->tune.ud_split);
   const int epc = c.dtype == FFN_BF16 ? 8 : 4;
