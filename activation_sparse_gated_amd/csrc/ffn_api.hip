@@ -176,12 +176,14 @@ int device_cus() {
 // per-token sparse kernel at prefill token counts too), FFN_SPARSE_LR_SLABS
 // (slices of d in the decode path's matrix-core low-rank first stage: 1, 2, 4
 // or 8; -1: the VALU first stage up to 8 tokens), FFN_SPARSE_DEC_IPW (gate row
-// pieces per wave in the decode gate: 1, 2, 4, or 8 for one token). They change launch shapes and
+// pieces per wave in the decode gate: 1, 2, 4, or 8 for one token),
+// FFN_SPARSE_UD_ORDER (1: the sparse workgroups token-major, not group-major
+// within each XCD class). They change launch shapes and
 // kernel choice only, never the result
 // beyond floating-point summation order.
 struct Tuning {
   int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0,
-      no_topk_down = 0, no_xcd = 0, lr_slabs = 0, dec_ipw = 0;
+      no_topk_down = 0, no_xcd = 0, lr_slabs = 0, dec_ipw = 0, ud_order = 0;
 };
 
 static int env_int(const char* name) {
@@ -769,6 +771,9 @@ UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const f
   }
   u.tiles_per_group = G;
   u.slot_split = S;
+  // group-major within each XCD class where the grouping allows it (LoPA, 32
+  // tokens: 84 against 92 us token-major; even at 48 and 64 tokens)
+  u.xcd_major = (h->tune.ud_order != 1 && S == 1 && ud_groups(u) % 8 == 0) ? 1 : 0;
   u.w_gate = h->w_gate;
   u.u_rows = h->u;
   u.lr_t = h->ws.lr_t;
@@ -913,6 +918,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.no_xcd = env_int("FFN_SPARSE_NO_XCD");
   h->tune.lr_slabs = env_int("FFN_SPARSE_LR_SLABS");
   h->tune.dec_ipw = env_int("FFN_SPARSE_DEC_IPW");
+  h->tune.ud_order = env_int("FFN_SPARSE_UD_ORDER");
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;

@@ -126,7 +126,19 @@ __global__ __launch_bounds__(64 * NW) void k_updown(const UpdownDesc u) {
   int bid = blockIdx.x;
   const int s = bid % S;
   bid /= S;
-  const int g = bid % ngroups, t = bid / ngroups;
+  // token-major: workgroup = token * groups + group; group-major within XCD
+  // classes (groups a multiple of 8, one phase): workgroup = ((group / 8) * M +
+  // token) * 8 + group % 8, so workgroup b still runs on XCD group % 8 and the
+  // workgroups resident together on an XCD share one tile group
+  int g, t;
+  if (u.xcd_major) {
+    const int rest = bid >> 3;
+    t = rest % u.M;
+    g = (rest / u.M) * 8 + (bid & 7);
+  } else {
+    g = bid % ngroups;
+    t = bid / ngroups;
+  }
 
   // ---- one round of independent loads: tile counts, x_t, the group's slots
   const int j0 = g * G, j1 = min(j0 + G, ntiles), ng = j1 - j0;
@@ -369,6 +381,7 @@ static hipError_t go_updown(const UpdownDesc& u, hipStream_t s) {
 hipError_t launch_updown(const UpdownDesc& u, hipStream_t s) {
   if (u.M <= 0) return hipSuccess;
   if (u.tiles_per_group < 1 || u.tiles_per_group > 64 || u.slot_split < 1) return hipErrorInvalidValue;
+  if (u.xcd_major && (ud_groups(u) % 8 != 0 || u.slot_split != 1)) return hipErrorInvalidValue;
   const int epc = u.dtype == DT_BF16 ? 8 : 4;
   if (u.d / epc > 512 || (u.d / epc + u.nwaves - 1) / u.nwaves > 64) return hipErrorInvalidValue;
   return u.dtype == DT_BF16 ? go_updown<DT_BF16>(u, s) : go_updown<DT_F32>(u, s);

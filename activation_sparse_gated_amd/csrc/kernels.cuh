@@ -127,6 +127,7 @@ struct UpdownDesc {
   int tiles_per_group;    // G: tiles handled by one workgroup
   int slot_split;         // S: workgroups sharing one tile group (entry phase)
   int nwaves;             // waves per workgroup (4 or 8)
+  int xcd_major;          // 1: workgroups dealt group-major within each XCD class (groups % 8 == 0, S == 1)
   int route_pass;         // block 0 also routes the pack (route / dense_list / n_dense, epoch)
   RouteDesc route;
   int include_routed;     // evaluate routed tokens here: overflowing tiles densely
