@@ -202,7 +202,41 @@ enum CtrlWord : int {
   CTRL_GATE_DONE = 1,   // completion ticket of the gate kernel
   CTRL_VSTAGE_DONE = 2, // reserved
   CTRL_TOPK_DONE = 3,   // completion ticket of the top-k kernel
+  CTRL_ERR = 4,         // nonzero once a bounded wait gave up (read by the host)
+  CTRL_SPIN_LIMIT = 5,  // polls a wait makes before it gives up
+  CTRL_WAIT_SKEW = 6,   // added to the epoch a wait expects (0; nonzero only to test the give-up path)
   CTRL_TILE_TICKETS = 64  // per-tile split-K tickets start here
 };
+constexpr uint32_t kDefaultSpinLimit = 1u << 20;   // about a second of polling
+
+// What a waiting workgroup expects: the epoch its wait accepts and how many
+// polls it may make. Read once per kernel from the control block.
+struct WaitCtl {
+  uint32_t want, limit;
+};
+__device__ __forceinline__ WaitCtl wait_ctl(const uint32_t* ctrl, uint32_t epoch) {
+  const uint32_t skew = __hip_atomic_load(&ctrl[CTRL_WAIT_SKEW], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t limit = __hip_atomic_load(&ctrl[CTRL_SPIN_LIMIT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return WaitCtl{epoch + skew, limit};
+}
+
+// Bounded wait on an epoch-tagged 64-bit word (tag in the high half, a count
+// or value in the low half), starting from an already loaded value w: polls
+// until the tag equals wc.want. After wc.limit polls it gives up, raises the
+// control block's error word (the host reads it through
+// ffn_sparse_device_status) and returns the low half as it stands, so every
+// wave still runs to the end of its kernel.
+__device__ __forceinline__ uint32_t tagged_wait(const uint64_t* p, uint64_t w, const WaitCtl& wc, uint32_t* ctrl) {
+  uint32_t n = 0;
+  while ((uint32_t)(w >> 32) != wc.want) {
+    if (++n > wc.limit) {
+      __hip_atomic_store(&ctrl[CTRL_ERR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    w = load64_relaxed(p);
+  }
+  return (uint32_t)w;
+}
 
 }  // namespace ffn

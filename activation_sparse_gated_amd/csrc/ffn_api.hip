@@ -165,22 +165,20 @@ int device_cus() {
 
 }  // namespace
 
-// Optional launch-shape overrides (0 = automatic), read once at init from the
-// environment: FFN_SPARSE_GATE_NT, FFN_SPARSE_GATE_WAVES, FFN_SPARSE_UD_SPLIT,
-// FFN_SPARSE_UD_GROUP, FFN_SPARSE_UD_WAVES, FFN_SPARSE_V_KS, FFN_SPARSE_NO_GEMV (1: MFMA tiles even
-// at decode sizes), FFN_SPARSE_NO_DECODE (1: the general kernels at 1..16 tokens
-// too), FFN_SPARSE_DEC_MODE (1 + DecMode: force the decode down-projection
+// Path switches (0 = automatic), read once at init from the environment; each
+// forces a kernel sequence the parity tests also run:
+// FFN_SPARSE_NO_DECODE (1: the general kernels at 1..16 tokens too),
+// FFN_SPARSE_DEC_MODE (1 + DecMode: force the decode down-projection
 // organisation), FFN_SPARSE_NO_PREFILL_GEMM (1: the decode-shaped MFMA kernel
 // for 128+ tokens as well), FFN_SPARSE_NO_TOPK_DOWN (1: top-k selection's down
 // product through the per-token TwELL kernel), FFN_SPARSE_NO_XCD (1: the
-// per-token sparse kernel at prefill token counts too), FFN_SPARSE_LR_SLABS
-// (slices of d in the decode path's matrix-core low-rank first stage: 1, 2, 4
-// or 8; -1: the VALU first stage up to 8 tokens), FFN_SPARSE_DEC_IPW (gate row
-// pieces per wave in the decode gate: 1, 2, 4, or 8 for one token),
-// FFN_SPARSE_UD_ORDER (1: the sparse workgroups token-major, not group-major
-// within each XCD class). They change launch shapes and
-// kernel choice only, never the result
-// beyond floating-point summation order.
+// per-token sparse kernel at prefill token counts too).
+// Launch-shape overrides for tuning exist only in a library compiled with
+// -DFFN_SPARSE_TUNING (FFN_SPARSE_GATE_NT, _GATE_WAVES, _UD_SPLIT, _UD_GROUP,
+// _UD_WAVES, _V_KS, _NO_GEMV, _LR_SLABS, _DEC_IPW, _UD_ORDER); the product
+// build ignores them, so a caller's environment cannot select a launch shape
+// the tests do not run. None changes the result beyond floating-point
+// summation order.
 struct Tuning {
   int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0,
       no_topk_down = 0, no_xcd = 0, lr_slabs = 0, dec_ipw = 0, ud_order = 0;
@@ -198,6 +196,10 @@ struct ffn_sparse_handle {
   int cus;
   int lds_max;
   Tuning tune;
+  // set when a launch failed part-way through a call or a bounded wait gave
+  // up: the look-back words may then be out of step with the epoch, so every
+  // later call returns FFN_E_HIP until the handle is re-initialised
+  bool failed = false;
   // timing
   bool timing = false;
   int cap = 0;
@@ -833,6 +835,16 @@ ffn_status run_updown(ffn_sparse_handle* h, UpdownDesc& u, hipStream_t s) {
   return hip_status(launch_updown_reduce(u, s));
 }
 
+// Runs one call on a handle: refused while the handle is marked failed; a
+// launch failure part-way through a call marks it.
+template <typename Fn>
+ffn_status guarded(ffn_sparse_handle* h, Fn fn) {
+  if (h && h->failed) return FFN_E_HIP;
+  const ffn_status st = fn();
+  if (st == FFN_E_HIP && h) h->failed = true;
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -904,6 +916,12 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->ws = ws;
   h->cus = cus;
   h->lds_max = device_lds_max();
+  h->tune.no_decode = env_int("FFN_SPARSE_NO_DECODE");
+  h->tune.dec_mode = env_int("FFN_SPARSE_DEC_MODE");
+  h->tune.no_pf = env_int("FFN_SPARSE_NO_PREFILL_GEMM");
+  h->tune.no_topk_down = env_int("FFN_SPARSE_NO_TOPK_DOWN");
+  h->tune.no_xcd = env_int("FFN_SPARSE_NO_XCD");
+#ifdef FFN_SPARSE_TUNING
   h->tune.gate_nt = env_int("FFN_SPARSE_GATE_NT");
   h->tune.gate_waves = env_int("FFN_SPARSE_GATE_WAVES");
   h->tune.ud_split = env_int("FFN_SPARSE_UD_SPLIT");
@@ -911,14 +929,10 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.v_ks = env_int("FFN_SPARSE_V_KS");
   h->tune.no_gemv = env_int("FFN_SPARSE_NO_GEMV");
   h->tune.ud_waves = env_int("FFN_SPARSE_UD_WAVES");
-  h->tune.no_decode = env_int("FFN_SPARSE_NO_DECODE");
-  h->tune.dec_mode = env_int("FFN_SPARSE_DEC_MODE");
-  h->tune.no_pf = env_int("FFN_SPARSE_NO_PREFILL_GEMM");
-  h->tune.no_topk_down = env_int("FFN_SPARSE_NO_TOPK_DOWN");
-  h->tune.no_xcd = env_int("FFN_SPARSE_NO_XCD");
   h->tune.lr_slabs = env_int("FFN_SPARSE_LR_SLABS");
   h->tune.dec_ipw = env_int("FFN_SPARSE_DEC_IPW");
   h->tune.ud_order = env_int("FFN_SPARSE_UD_ORDER");
+#endif
   if (cfg->rank > 0) {
     h->u = w_gate_or_u;
     h->v = v_or_null;
@@ -941,6 +955,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   if (err == hipSuccess && cfg->sel == FFN_SEL_TOPK_WINA)
     err = launch_rownorm(h->w_down_nm, ws.colnorm, cfg->d_ff, cfg->d_model, cfg->dtype, s);
   if (err == hipSuccess) err = launch_fill_u32(ws.ctrl, 0u, kCtrlWords + kTicketWords, s);
+  if (err == hipSuccess) err = launch_fill_u32(ws.ctrl + CTRL_SPIN_LIMIT, kDefaultSpinLimit, 1, s);
   if (err == hipSuccess)
     err = launch_fill_u32(reinterpret_cast<uint32_t*>(ws.lb), 0u,
                           (size_t)cfg->max_m * (cfg->d_ff / 16) * 2, s);
@@ -957,7 +972,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   return FFN_OK;
 }
 
-ffn_status ffn_sparse_gate_pack(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+static ffn_status gate_pack_impl(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
                                 float bias_scalar, const float* tau, int32_t k, ffn_twell_pack* pack,
                                 float* g_debug, float* s_debug, void* stream) {
   ffn_status st = check_call(h, x, m, tau, k);
@@ -975,7 +990,7 @@ ffn_status ffn_sparse_gate_pack(ffn_sparse_handle* h, const void* x, int32_t m, 
   return hip_status(launch_route(route_desc(h, m, pack), s));
 }
 
-ffn_status ffn_sparse_updown(ffn_sparse_handle* h, const void* x, int32_t m, const ffn_twell_pack* pack,
+static ffn_status updown_impl(ffn_sparse_handle* h, const void* x, int32_t m, const ffn_twell_pack* pack,
                              void* y, void* stream) {
   ffn_status st = check_call(h, x, m, reinterpret_cast<const float*>(1), 0);
   if (st != FFN_OK) return st;
@@ -986,7 +1001,7 @@ ffn_status ffn_sparse_updown(ffn_sparse_handle* h, const void* x, int32_t m, con
   return run_updown(h, u, s);
 }
 
-ffn_status ffn_sparse_dense_fallback(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+static ffn_status dense_fallback_impl(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
                                      float bias_scalar, const float* tau, int32_t k,
                                      const ffn_twell_pack* pack, void* y, void* stream) {
   ffn_status st = check_call(h, x, m, tau, k);
@@ -1036,7 +1051,7 @@ static int topk_down_kind(const ffn_sparse_handle* h, int m) {
   return (m == 1 && topk_list_desc(h, nullptr, &ld)) ? 1 : 2;
 }
 
-ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+static ffn_status forward_impl(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
                               float bias_scalar, const float* tau, int32_t k, ffn_twell_pack* pack,
                               void* y, void* stream) {
   ffn_status st = check_call(h, x, m, tau, k);
@@ -1092,7 +1107,7 @@ ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, co
   return hip_status(run_dense_down(h, m, pack->dense_list, pack->n_dense, y, FFN_K_FALLBACK, s));
 }
 
-ffn_status ffn_sparse_dense_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+static ffn_status dense_forward_impl(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
                                     float bias_scalar, const float* tau, void* y, void* stream) {
   ffn_status st = check_call(h, x, m, tau, 0);
   if (st != FFN_OK) return st;
@@ -1102,6 +1117,59 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle* h, const void* x, int32_t
   hipError_t err = run_dense_hidden(h, x, m, nullptr, nullptr, bias, bias_scalar, tau, FFN_K_DENSE, s);
   if (err != hipSuccess) return FFN_E_HIP;
   return hip_status(run_dense_down(h, m, nullptr, nullptr, y, FFN_K_DENSE, s));
+}
+
+ffn_status ffn_sparse_gate_pack(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+                                float bias_scalar, const float* tau, int32_t k, ffn_twell_pack* pack,
+                                float* g_debug, float* s_debug, void* stream) {
+  return guarded(h, [&] { return gate_pack_impl(h, x, m, bias, bias_scalar, tau, k, pack, g_debug, s_debug, stream); });
+}
+
+ffn_status ffn_sparse_updown(ffn_sparse_handle* h, const void* x, int32_t m, const ffn_twell_pack* pack,
+                             void* y, void* stream) {
+  return guarded(h, [&] { return updown_impl(h, x, m, pack, y, stream); });
+}
+
+ffn_status ffn_sparse_dense_fallback(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+                                     float bias_scalar, const float* tau, int32_t k,
+                                     const ffn_twell_pack* pack, void* y, void* stream) {
+  return guarded(h, [&] { return dense_fallback_impl(h, x, m, bias, bias_scalar, tau, k, pack, y, stream); });
+}
+
+ffn_status ffn_sparse_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+                              float bias_scalar, const float* tau, int32_t k, ffn_twell_pack* pack,
+                              void* y, void* stream) {
+  return guarded(h, [&] { return forward_impl(h, x, m, bias, bias_scalar, tau, k, pack, y, stream); });
+}
+
+ffn_status ffn_sparse_dense_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+                                    float bias_scalar, const float* tau, void* y, void* stream) {
+  return guarded(h, [&] { return dense_forward_impl(h, x, m, bias, bias_scalar, tau, y, stream); });
+}
+
+ffn_status ffn_sparse_device_status(ffn_sparse_handle* h, void* stream) {
+  if (!h) return FFN_E_INVALID;
+  if (h->failed) return FFN_E_HIP;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t err = 0;
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpy(&err, h->ws.ctrl + CTRL_ERR, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess || err != 0) {
+    h->failed = true;
+    return FFN_E_HIP;
+  }
+  return FFN_OK;
+}
+
+ffn_status ffn_sparse_debug_waits(ffn_sparse_handle* h, uint32_t epoch_skew, uint32_t spin_limit, void* stream) {
+  if (!h) return FFN_E_INVALID;
+  if (h->failed) return FFN_E_HIP;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (launch_fill_u32(h->ws.ctrl + CTRL_WAIT_SKEW, epoch_skew, 1, s) != hipSuccess ||
+      launch_fill_u32(h->ws.ctrl + CTRL_SPIN_LIMIT, spin_limit, 1, s) != hipSuccess) {
+    h->failed = true;
+    return FFN_E_HIP;
+  }
+  return FFN_OK;
 }
 
 int32_t ffn_sparse_forward_path(const ffn_sparse_handle* h, int32_t m) {

@@ -73,7 +73,7 @@ __device__ __forceinline__ void epi_store_f32(const EpiDesc& e, const TileView& 
 //      offset (ballot + prefix popcount), and the last sub-tile writes cnt and
 //      the padding.
 constexpr int kTwellMaxSlots = 128;
-__device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, const uint32_t* ctrl) {
+__device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, uint32_t* ctrl) {
   __shared__ int s_off[kTwellMaxSlots];
   __shared__ float s_bias[kTwellMaxSlots], s_cut[kTwellMaxSlots];
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -82,6 +82,7 @@ __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, c
   // pass epoch of the look-back words (advanced by the routing pass after
   // every gate pass); only sub-tiled TwELL tiles need it
   const uint32_t epoch = Q > 1 ? __hip_atomic_load(&ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
+  const WaitCtl wc = Q > 1 ? wait_ctl(ctrl, epoch) : WaitCtl{0u, 0u};
   // every token's bias and cut, read in one parallel round
   for (int m = threadIdx.x; m < v.mcnt; m += blockDim.x) {
     s_off[m] = 0;
@@ -113,9 +114,7 @@ __device__ __forceinline__ void epi_twell(const EpiDesc& e, const TileView& v, c
     for (int p = threadIdx.x; p < v.mcnt * q; p += blockDim.x) {
       const int pp = p / v.mcnt, m = p - pp * v.mcnt;   // consecutive threads: consecutive tokens
       const uint64_t* wp = e.lb + ((size_t)j * Q + pp) * e.lb_ld + v.m0 + m;
-      uint64_t w;
-      while (((w = load64_relaxed(wp)) >> 32) != epoch) __builtin_amdgcn_s_sleep(1);
-      atomicAdd(&s_off[m], (int)(uint32_t)w);
+      atomicAdd(&s_off[m], (int)tagged_wait(wp, load64_relaxed(wp), wc, ctrl));
     }
   }
   __syncthreads();
@@ -198,7 +197,7 @@ __device__ __forceinline__ void epi_y(const EpiDesc& e, const TileView& v) {
 }
 
 template <int NMAT, int EPI>
-__device__ __forceinline__ void run_epilogue(const EpiDesc& e, const TileView& v, const uint32_t* ctrl, int ksi) {
+__device__ __forceinline__ void run_epilogue(const EpiDesc& e, const TileView& v, uint32_t* ctrl, int ksi) {
   if (EPI == EPI_STORE_F32) epi_store_f32(e, v, ksi);
   if (EPI == EPI_WINA) epi_wina(e, v);
   if (EPI == EPI_DENSE_H) epi_dense_h<NMAT>(e, v);

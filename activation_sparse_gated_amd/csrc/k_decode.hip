@@ -363,15 +363,10 @@ __device__ __forceinline__ float dec_cut(const DecodeDesc& d, int t) {
   return d.sel == SEL_THRESH ? fmaxf(d.tau[t], 0.f) : 0.f;
 }
 
-// Waits until an epoch-tagged look-back word carries this pass's epoch and
-// returns its count.
-__device__ __forceinline__ int lb_count(const uint64_t* p, uint32_t epoch, uint64_t first) {
-  uint64_t w = first;
-  while ((uint32_t)(w >> 32) != epoch) {
-    __builtin_amdgcn_s_sleep(1);
-    w = load64_relaxed(p);
-  }
-  return (int)(uint32_t)w;
+// Waits (bounded) until an epoch-tagged look-back word carries this pass's
+// epoch and returns its count.
+__device__ __forceinline__ int lb_count(const uint64_t* p, const WaitCtl& wc, uint64_t first, uint32_t* ctrl) {
+  return (int)tagged_wait(p, first, wc, ctrl);
 }
 
 template <int NW, int IPW, int MAXM, bool LOWRANK, int MODE>
@@ -460,6 +455,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
     }
   }
   const uint32_t epoch = __hip_atomic_load(&d.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  const WaitCtl wc = wait_ctl(d.ctrl, epoch);
   __syncthreads();
   if constexpr (MF) {
     if (use_mf) dec_mfma_finish<8, MF_NG, MF_DS, MAXM>(am, K, s_t, M, s_acc, s_g);
@@ -518,7 +514,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
       // the wave's first token's first read was issued early
       const uint64_t* wp = d.lb + (size_t)m * nsub + (size_t)j * Q + lane;
       const uint64_t first = m == wave ? tw : (lane < q ? load64_relaxed(wp) : 0ull);
-      pre = wave_sum_i(lane < q ? lb_count(wp, epoch, first) : 0);
+      pre = wave_sum_i(lane < q ? lb_count(wp, wc, first, d.ctrl) : 0);
     }
     const size_t slot0 = ((size_t)m * ntiles + j) * d.E;
     const bool act = (bal >> lane) & 1ull;
@@ -874,11 +870,15 @@ constexpr int kUpGrid = 256;
 constexpr int kUpMaxSteps = 16;                        // 32-element steps per wave (d <= 4096)
 constexpr int kUpNB = 3;                               // groups of 16 entries in flight
 constexpr int kUpMaxEnt = 128;                         // entries per workgroup (F <= 128 * kUpGrid)
+// id slots: the group loop reads kUpNB groups of 16 at a time, so the slots
+// run to the next multiple of 16 * kUpNB; slots from the workgroup's entry
+// count on hold -1 (no row)
+constexpr int kUpNrnSlots = (kUpMaxEnt + 16 * kUpNB - 1) / (16 * kUpNB) * (16 * kUpNB);
 
 __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
   extern __shared__ uint4 s_dyn[];                     // x: M rows of d + 8 bf16; masks; prefixes
   __shared__ int s_scan[kUpWaves];
-  __shared__ int s_nrn[kUpMaxEnt];
+  __shared__ int s_nrn[kUpNrnSlots];
   __shared__ f32x4_t s_acc[kUpWaves][kUpNB][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int M = d.M, dm = d.d, F = d.F, R = d.R, nsub = F / R;
@@ -932,7 +932,7 @@ __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
   if (b == 0 && tid == 0) *d.ul_total = total;
   const int e0 = (int)((long long)total * b / G), e1 = (int)((long long)total * (b + 1) / G);
   const int ne = e1 - e0;
-  for (int i = tid; i < kUpMaxEnt; i += NT) {
+  for (int i = tid; i < kUpNrnSlots; i += NT) {
     int n = -1;
     if (i < ne) {
       const int e = e0 + i;
@@ -1306,7 +1306,7 @@ hipError_t launch_dec_reduce(const DecodeDesc& d, hipStream_t s) {
 // multiple of 256), then the nsub sub-tile masks and prefixes.
 size_t dec_up_lds(const DecodeDesc& d) { return (size_t)d.M * (d.d + 8) * 2 + (size_t)(d.F / d.R) * 12; }
 // Static LDS of k_dec_up (s_scan, s_nrn, s_acc) and gfx950's LDS per workgroup.
-constexpr size_t kUpStaticLds = kUpWaves * 4 + kUpMaxEnt * 4 + (size_t)kUpWaves * kUpNB * 64 * 16;
+constexpr size_t kUpStaticLds = kUpWaves * 4 + kUpNrnSlots * 4 + (size_t)kUpWaves * kUpNB * 64 * 16;
 constexpr size_t kLdsPerWorkgroup = 160 * 1024;
 
 // Sub-tile rows of the decode gate for m tokens, gate contraction K and

@@ -207,7 +207,9 @@ __global__ __launch_bounds__(64 * kXWaves) void k_xcd_down(const XcdDesc u) {
 // 512 up to 4096, at most 64 tiles, E a power of two up to 128, and every
 // non-overflowing token's list within a wave's LDS.
 bool xcd_ok(const XcdDesc& u) {
-  if (u.M < 1 || u.d % 512 != 0 || u.d > 4096 || u.ntiles < 1 || u.ntiles > 64 || u.E < 1 || u.E > 128 ||
+  // d / 512 must be 1, 2, 4 or 8: the widths the kernels are instantiated for
+  const int dq = u.d / 512;
+  if (u.M < 1 || u.d % 512 != 0 || u.d > 4096 || (dq & (dq - 1)) != 0 || u.ntiles < 1 || u.ntiles > 64 || u.E < 1 || u.E > 128 ||
       (u.E & (u.E - 1)) != 0 || (1 << u.lg_e) != u.E || u.ntiles * u.E > kXList)
     return false;
   return u.x && u.w_up && u.w_down_nm && u.cnt && u.idx && u.val && u.hp && u.y;

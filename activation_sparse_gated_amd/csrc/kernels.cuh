@@ -51,7 +51,7 @@ struct GemmDesc {
   int nwaves;             // waves per workgroup (4 or 16)
   int gemv;               // decode GEMV (VALU) instead of MFMA tiles (bf16, M <= 8)
   int ks;                 // workgroups splitting K; each writes its own output slab (>= 1)
-  const uint32_t* ctrl;   // control block (epoch of the look-back words)
+  uint32_t* ctrl;         // control block (epoch of the look-back words, wait limits, error word)
   int no_pf;              // 1: never the prefill-shaped kernel (tuning switch)
   // prefill-shaped kernel with ks > 1 (output rows y, device-side token count):
   // slice z of K writes fp32 partials kpart[(z * kpart_m + m) * nrows + n]
@@ -202,7 +202,7 @@ struct DecodeDesc {
   const float* bias; float bias_scalar; const float* tau;
   int32_t* cnt; uint16_t* idx; void* val;   // TwELL pack
   uint64_t* lb;                // per-token look-back words [8 x F / R]
-  const uint32_t* ctrl;        // control words (look-back epoch)
+  uint32_t* ctrl;              // control words (look-back epoch, wait limits, error word)
   float* g_debug;              // [M x F] or null
   int R;                       // gate rows per workgroup (divides T)
   int ipw;                     // gate pieces (1 KB of a row) per wave: 1, 2 or 4

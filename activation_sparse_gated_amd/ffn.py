@@ -145,6 +145,26 @@ class SparseFFN:
         return {0: "general", 1: "decode-chunk", 2: "decode-part", 3: "decode-split",
                 4: "topk-list", 5: "topk-masked-dense"}[r]
 
+    def device_status(self, stream=None) -> int:
+        """FFN_OK, or FFN_E_HIP when a launch failed or a bounded wait gave up
+        (synchronises the stream; see ffn_sparse_device_status)."""
+        return self.lib.ffn_sparse_device_status(self.handle, _stream_ptr(stream))
+
+    def debug_waits(self, epoch_skew: int, spin_limit: int, stream=None) -> None:
+        check(self.lib.ffn_sparse_debug_waits(self.handle, int(epoch_skew), int(spin_limit), _stream_ptr(stream)),
+              "ffn_sparse_debug_waits")
+
+    def reinit(self, stream=None) -> None:
+        """Re-initialise the handle on the same weights and workspace."""
+        w_gate, u, v, w_up, w_down = self._weights
+        self.close()
+        h = ctypes.c_void_p()
+        gate = w_gate if self.cfg.rank == 0 else u
+        check(self.lib.ffn_sparse_init(ctypes.byref(self.cfg), _ptr(gate), _ptr(v), _ptr(w_up), _ptr(w_down),
+                                       self.workspace.data_ptr(), self.workspace.numel(), _stream_ptr(stream),
+                                       ctypes.byref(h)), "ffn_sparse_init")
+        self.handle = h
+
     # ------------------------------------------------------------------ timing
     def timing_enable(self, enable: bool = True, capacity: int = 4096) -> None:
         check(self.lib.ffn_sparse_timing_enable(self.handle, 1 if enable else 0, capacity),

@@ -157,11 +157,26 @@ def main():
                           "copy_bytes": src.numel()}))
         return
 
+    def per_step(step, n):
+        """Per-step durations (us) from an event pair around each step (a
+        separate pass: the events add a little time to every step)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            step(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return {"p10": round(float(np.percentile(us, 10)), 3), "p50": round(float(np.median(us)), 3),
+                "p90": round(float(np.percentile(us, 90)), 3), "steps": n}
+
     # ---- timed region: the sparse forward pass (value) ----
     ms_sparse, steps = timed(sparse_step, args.steps, args.warmup, graph=args.graph)
     note(f"sparse step {ms_sparse * 1e3:.2f} us")
     ms_dense, _ = timed(dense_step, max(20, args.steps // 4), 5, graph=args.graph)
     note(f"dense step {ms_dense * 1e3:.2f} us")
+    dist_sparse = per_step(sparse_step, args.steps)
+    dist_dense = per_step(dense_step, max(20, args.steps // 4))
 
     # ---- touched bytes of one step (from the pack the step wrote) ----
     ffn0, pack0, y0, _ = layers[0]
@@ -258,22 +273,42 @@ def main():
                 "alg_bytes_per_launch": int(alg[dom]), "avg_us": round(kernels[dom]["avg_us"], 3)}
 
     # ---- CPU oracle on a bounded sample of the same workload ----
-    cpu = None
+    # (all the host threads BLAS uses here, then one thread; the oracle is
+    # plain NumPy fp64, untuned)
+    cpu = cpu1 = None
+    host = {}
     if not args.no_cpu:
         from oracle import ffn_oracle as O
+        from threadpoolctl import threadpool_info, threadpool_limits
         try:
-            from threadpoolctl import threadpool_info
-            cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            host["nproc"] = len(os.sched_getaffinity(0))
         except Exception:
-            cores = os.cpu_count() or 1
-        t0 = time.time()
-        reps = 0
-        while time.time() - t0 < args.cpu_seconds or reps == 0:
-            O.forward(wl)
-            reps += 1
-        el = time.time() - t0
+            host["nproc"] = os.cpu_count()
+        host["cpu_count"] = os.cpu_count()
+        try:
+            with open("/proc/cpuinfo") as fh:
+                host["cpu_model"] = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+        except Exception:
+            host["cpu_model"] = None
+
+        def oracle_rate(seconds):
+            t0 = time.time()
+            reps = 0
+            while time.time() - t0 < seconds or reps == 0:
+                O.forward(wl)
+                reps += 1
+            el = time.time() - t0
+            return reps, el
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        reps, el = oracle_rate(args.cpu_seconds)
         cpu = {"value": round(reps * m / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-               "sample": f"{reps} full oracle forward passes of the {m}-token batch ({el:.1f} s)"}
+               "sample": f"{reps} full oracle forward passes of the {m}-token batch ({el:.1f} s)",
+               "nproc": host["nproc"], "cpu_model": host["cpu_model"]}
+        with threadpool_limits(limits=1):
+            reps1, el1 = oracle_rate(args.cpu_seconds)
+        cpu1 = {"value": round(reps1 * m / el1, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{reps1} full oracle forward passes of the {m}-token batch ({el1:.1f} s), one thread"}
 
     tok_s = m * 1e3 / ms_sparse
     out = {
@@ -298,9 +333,12 @@ def main():
         "dense_ms_per_step": round(ms_dense, 5),
         "dense_effective_hbm_GBps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
         "speedup_vs_dense": round(ms_dense / ms_sparse, 3),
+        "step_us_dist": dist_sparse,
+        "dense_step_us_dist": dist_dense,
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
         "input_gen_s": round(t_gen, 1),
     }
     print(json.dumps(out))

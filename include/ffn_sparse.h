@@ -27,8 +27,9 @@
  *     config.dtype; accumulation is fp32.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream). Arguments are validated before anything is launched; on an error
- *     nothing is written. FFN_E_HIP reports a failed launch, after which the
- *     handle must be re-initialised.
+ *     nothing is written. FFN_E_HIP reports a failed launch (or, through
+ *     ffn_sparse_device_status, a wait that gave up), after which the handle
+ *     refuses further calls until it is re-initialised.
  *   - A handle owns host memory only and is bound to the workspace it was
  *     initialised with; calls on one handle must be serialised on one stream.
  *   - Required alignment: 16 bytes for every device pointer.
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FFN_SPARSE_ABI_VERSION 1
+#define FFN_SPARSE_ABI_VERSION 2
 
 typedef enum {
   FFN_OK = 0,
@@ -169,14 +170,24 @@ ffn_status ffn_sparse_dense_fallback(ffn_sparse_handle *h, const void *x, int32_
  * every y row and the complete pack. For m <= 64 the routed tokens are
  * evaluated by the sparse kernel itself (each overflowing tile densely, gate
  * recomputed); for larger m they go through the dense backup on matrix cores.
- * Routing is done inside the sparse kernel (no separate pass). */
+ * Routing is done inside the sparse kernel (no separate pass).
+ * Source: LoPA page, "How LoPA Gating Restructures FFN Computation" (gate
+ * projection, activation, elementwise product, down projection, with only the
+ * active neurons' rows read); Sparser/Faster/Lighter page, "TwELL
+ * 減掉轉換開銷" and "Hybrid 應對非均勻稀疏" (pack, fused up/down, dense
+ * backup; both paths give the same y); WINA page, section 3.1 (top-k score).
+ * Arguments as for gate_pack; y [m x d_model] device, written in full. */
 ffn_status ffn_sparse_forward(ffn_sparse_handle *h, const void *x, int32_t m,
                               const float *bias, float bias_scalar, const float *tau,
                               int32_t k, ffn_twell_pack *pack, void *y, void *stream);
 
 /* The same function evaluated densely over every neuron (the comparison
  * baseline): bias / threshold gates keep their elementwise mask; a TOPK config
- * keeps every neuron (k = d_ff). */
+ * keeps every neuron (k = d_ff). Every weight byte is streamed once per call
+ * through dense matrix products (GEMV / MFMA tiles), the "dense GPU matrix
+ * operations" the sparse path is measured against (LoPA page, "How LoPA
+ * Gating Restructures FFN Computation"). Arguments as for forward, without
+ * k and the pack. */
 ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t m,
                                     const float *bias, float bias_scalar, const float *tau,
                                     void *y, void *stream);
@@ -225,6 +236,25 @@ typedef enum {
 ffn_status ffn_sparse_timing_enable(ffn_sparse_handle *h, int32_t enable, int32_t capacity);
 ffn_status ffn_sparse_timing_read(ffn_sparse_handle *h, int32_t kind, int32_t *launches,
                                   double *total_ms);
+
+/* Error state of the work enqueued so far on `stream` (synchronises it).
+ * The kernels' cross-workgroup waits (the TwELL look-back of sub-tiled gate
+ * tiles) are bounded: a wait that gives up lets its kernel finish and raises
+ * an error word in the workspace. Returns FFN_OK, or FFN_E_HIP when a launch
+ * failed earlier or a wait gave up; the handle is then marked failed and every
+ * later call returns FFN_E_HIP until it is re-initialised with
+ * ffn_sparse_init (which clears the error word). FFN_E_INVALID for a null
+ * handle. */
+ffn_status ffn_sparse_device_status(ffn_sparse_handle *h, void *stream);
+
+/* Test hook for the give-up path of the bounded waits: from the next call on,
+ * a wait expects the pass epoch plus `epoch_skew` (0 in normal use, where the
+ * handle starts) and gives up after `spin_limit` polls (the default allows
+ * about a second). A nonzero skew makes every wait give up after its polls,
+ * so each kernel still exits and ffn_sparse_device_status then reports
+ * FFN_E_HIP. Enqueued on `stream`. */
+ffn_status ffn_sparse_debug_waits(ffn_sparse_handle *h, uint32_t epoch_skew, uint32_t spin_limit,
+                                  void *stream);
 
 /* Free the host-side handle (device memory belongs to the caller). */
 void ffn_sparse_destroy(ffn_sparse_handle *h);

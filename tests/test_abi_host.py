@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert lib.ffn_sparse_abi_version() == 1
+    assert lib.ffn_sparse_abi_version() == 2
 
 
 def test_status_strings(L):
@@ -114,4 +114,6 @@ def test_calls_reject_null_handle(L):
     assert lib.ffn_sparse_dense_forward(None, 16, 1, None, 0.0, None, 16, None) == -1
     assert lib.ffn_sparse_timing_enable(None, 1, 4) == -1
     assert lib.ffn_sparse_forward_path(None, 1) == -1
+    assert lib.ffn_sparse_device_status(None, None) == -1
+    assert lib.ffn_sparse_debug_waits(None, 0, 1, None) == -1
     lib.ffn_sparse_destroy(None)

@@ -177,3 +177,4 @@ def test_topk_down_organisations(m, kw):
         torch.cuda.synchronize()
         assert np.array_equal(host(y2), host(y))
         ys.append(host(y)[: wl.m].copy())
+
