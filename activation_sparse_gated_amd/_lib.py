@@ -20,7 +20,8 @@ EXPORTS = [
     "ffn_sparse_workspace_bytes", "ffn_sparse_pack_bytes", "ffn_sparse_init", "ffn_sparse_gate_pack",
     "ffn_sparse_updown", "ffn_sparse_dense_fallback", "ffn_sparse_forward", "ffn_sparse_dense_forward",
     "ffn_sparse_forward_path", "ffn_sparse_timing_enable", "ffn_sparse_timing_read", "ffn_sparse_destroy",
-    "ffn_sparse_device_status", "ffn_sparse_debug_waits",
+    "ffn_sparse_device_status", "ffn_sparse_debug_waits", "ffn_sparse_forward_noalloc",
+    "ffn_sparse_noalloc_scratch_bytes",
 ]
 
 
@@ -76,6 +77,9 @@ def load() -> ctypes.CDLL:
         "ffn_sparse_timing_read": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_double)]),
         "ffn_sparse_destroy": (None, [c_void_p]),
         "ffn_sparse_device_status": (c_int32, [c_void_p, c_void_p]),
+        "ffn_sparse_forward_noalloc": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_float, c_void_p,
+                                                 c_int32, P(Pack), c_void_p, c_void_p]),
+        "ffn_sparse_noalloc_scratch_bytes": (c_size_t, []),
         "ffn_sparse_debug_waits": (c_int32, [c_void_p, ctypes.c_uint32, ctypes.c_uint32, c_void_p]),
     }
     for name, (res, args) in sig.items():

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -18,6 +19,70 @@ using namespace ffn;
 namespace ffn {
 thread_local LaunchEvents tl_launch_events = {nullptr, nullptr};
 }  // namespace ffn
+
+// ---------------------------------------------------------------- scratch
+// Per-call device memory of ffn_sparse_forward_noalloc, for callers that
+// cannot allocate: a fixed-size array that each GPU the library runs on holds
+// until the process ends, shared by every no-allocation call on that GPU.
+// Host code never uses the array's name as an address: each device's copy is
+// resolved with hipGetSymbolAddress once, with that device current.
+//   [0, 256)                  control words (pass epoch, wait limits, error word)
+//   [256, +kScrLbBytes)       look-back words of the decode gate, kDecMaxM tokens x
+//                             kScrMaxF / 2 sub-tiles (epoch-tagged, cleared once)
+//   then kScrMaxF list ids, the list length, and the per-call regions (low-rank
+//   slabs and t, sub-tile masks, hidden values, partial y rows, list h)
+constexpr size_t kScratchBytes = 20u << 20;
+constexpr int kScrMaxF = 32768;
+constexpr size_t kScrCtrlBytes = 256;
+constexpr size_t kScrLbBytes = (size_t)kDecMaxM * (kScrMaxF / 2) * sizeof(uint64_t);
+constexpr size_t kScrIdsBytes = (size_t)kScrMaxF * sizeof(int32_t);
+constexpr size_t kScrFixedBytes = kScrCtrlBytes + kScrLbBytes + kScrIdsBytes + 256;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's copy of `scratch`; on the first request for a device its
+// address is resolved and its fixed regions are cleared on `s` (which is then
+// synchronised), the wait limit set.
+hipError_t scratch_for_device(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    uint32_t* w = reinterpret_cast<uint32_t*>(ptr);
+    e = launch_fill_u32(w, 0u, kScrFixedBytes / 4, s);
+    if (e == hipSuccess) e = launch_fill_u32(w + CTRL_SPIN_LIMIT, kDefaultSpinLimit, 1, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Error word of this device's scratch (0 when it has none yet).
+uint32_t scratch_error_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  void* ptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev];
+  }
+  uint32_t err = 0;
+  if (ptr && hipMemcpy(&err, reinterpret_cast<uint32_t*>(ptr) + CTRL_ERR, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)
+    return 1;
+  return err;
+}
+}  // namespace
 
 namespace {
 
@@ -910,6 +975,11 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   const int cus = device_cus();
   Workspace ws = carve(*cfg, reinterpret_cast<char*>(workspace), cus);
   if (ws_bytes < ws.total) return FFN_E_WORKSPACE;
+  {
+    // the no-allocation variant's scratch on this device (set up once)
+    void* scr = nullptr;
+    if (scratch_for_device(reinterpret_cast<hipStream_t>(stream), &scr) != hipSuccess) return FFN_E_HIP;
+  }
   ffn_sparse_handle* h = new (std::nothrow) ffn_sparse_handle();
   if (!h) return FFN_E_INVALID;
   h->cfg = *cfg;
@@ -1147,13 +1217,61 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle* h, const void* x, int32_t
   return guarded(h, [&] { return dense_forward_impl(h, x, m, bias, bias_scalar, tau, y, stream); });
 }
 
+ffn_status ffn_sparse_forward_noalloc(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+                                      float bias_scalar, const float* tau, int32_t k, ffn_twell_pack* pack,
+                                      void* y, void* stream) {
+  return guarded(h, [&]() -> ffn_status {
+    ffn_status st = check_call(h, x, m, tau, k);
+    if (st != FFN_OK) return st;
+    if (!pack_ok(pack) || (m > 0 && (!y || !aligned16(y)))) return FFN_E_INVALID;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (m == 0) return hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pack->n_dense), 0u, 1, s));
+    const auto& c = h->cfg;
+    DecodeDesc dd;
+    if (!plan_decode(h, m, &dd) || c.d_ff > kScrMaxF) return FFN_E_UNSUPPORTED;
+    void* base = nullptr;
+    if (scratch_for_device(s, &base) != hipSuccess) return FFN_E_HIP;
+    // per-call regions after the fixed ones, sized for this call
+    char* p = reinterpret_cast<char*>(base);
+    size_t off = kScrFixedBytes;
+    auto take = [&](size_t bytes) -> char* {
+      char* q = p + off;
+      off += align_up(bytes);
+      return q;
+    };
+    const size_t F = c.d_ff, d = c.d_model, r = c.rank, M = m;
+    Workspace w = h->ws;
+    w.ctrl = reinterpret_cast<uint32_t*>(p);
+    w.dec_lb = reinterpret_cast<uint64_t*>(p + kScrCtrlBytes);
+    w.ul_nrn = reinterpret_cast<int32_t*>(p + kScrCtrlBytes + kScrLbBytes);
+    w.ul_total = reinterpret_cast<int32_t*>(p + kScrCtrlBytes + kScrLbBytes + kScrIdsBytes);
+    w.lr_slabs = reinterpret_cast<float*>(take(std::max<size_t>(1, 8 * M * r) * sizeof(float)));
+    w.lr_t = reinterpret_cast<float*>(take(std::max<size_t>(1, M * r) * sizeof(float)));
+    w.umask = reinterpret_cast<uint64_t*>(take((F / 2) * sizeof(uint64_t)));
+    w.hd = reinterpret_cast<float*>(take(F * M * sizeof(float)));
+    const size_t rows = dd.mode == DEC_PART ? (F / dd.R) * M : (dd.mode == DEC_SPLIT ? (size_t)dd.ngroups * M : 1);
+    w.dec_part = reinterpret_cast<float*>(take(rows * d * sizeof(float)));
+    w.dec_part_rows = rows;
+    w.ul_h = reinterpret_cast<float*>(take(M * ((F + 31) / 32 * 32) * sizeof(uint16_t)));
+    if (off > kScratchBytes) return FFN_E_WORKSPACE;
+    const Workspace saved = h->ws;
+    h->ws = w;
+    st = forward_impl(h, x, m, bias, bias_scalar, tau, k, pack, y, stream);
+    h->ws = saved;
+    return st;
+  });
+}
+
+size_t ffn_sparse_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
 ffn_status ffn_sparse_device_status(ffn_sparse_handle* h, void* stream) {
   if (!h) return FFN_E_INVALID;
   if (h->failed) return FFN_E_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint32_t err = 0;
   if (hipStreamSynchronize(s) != hipSuccess ||
-      hipMemcpy(&err, h->ws.ctrl + CTRL_ERR, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess || err != 0) {
+      hipMemcpy(&err, h->ws.ctrl + CTRL_ERR, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess || err != 0 ||
+      scratch_error_word() != 0) {
     h->failed = true;
     return FFN_E_HIP;
   }

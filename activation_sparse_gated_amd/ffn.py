@@ -127,6 +127,17 @@ class SparseFFN:
                                           _stream_ptr(stream)), "ffn_sparse_forward")
         return y, pack
 
+    def forward_noalloc(self, x, pack: TwellPack, y, m=None, *, bias=None, bias_scalar=0.0, tau=None, k=0,
+                        stream=None):
+        """forward() through the allocation-free entry point: the caller passes
+        the pack and y; the library's per-GPU scratch array holds the rest."""
+        m = x.shape[0] if m is None else m
+        ps = pack.c_struct()
+        check(self.lib.ffn_sparse_forward_noalloc(self.handle, _ptr(x), m, _ptr(bias), float(bias_scalar),
+                                                  _ptr(tau), int(k), ctypes.byref(ps), _ptr(y),
+                                                  _stream_ptr(stream)), "ffn_sparse_forward_noalloc")
+        return y, pack
+
     def dense_forward(self, x, m=None, *, bias=None, bias_scalar=0.0, tau=None, y=None, stream=None):
         m = x.shape[0] if m is None else m
         y = self.new_output(m) if y is None else y

@@ -237,14 +237,42 @@ ffn_status ffn_sparse_timing_enable(ffn_sparse_handle *h, int32_t enable, int32_
 ffn_status ffn_sparse_timing_read(ffn_sparse_handle *h, int32_t kind, int32_t *launches,
                                   double *total_ms);
 
+/* ffn_sparse_forward for callers that cannot allocate device memory or
+ * synchronise inside the call (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments, same results (the
+ * same kernels on the same inputs, bit for bit), same conventions; the
+ * per-call scratch (control and look-back words, low-rank intermediate,
+ * sub-tile masks, hidden values, partial y rows, the compact list) comes from
+ * a fixed device array that the library holds on each GPU it runs on, of
+ * ffn_sparse_noalloc_scratch_bytes() bytes, instead of from the handle's
+ * workspace; the handle's workspace still holds what ffn_sparse_init
+ * precomputed (the other W_down layout). The call allocates and frees
+ * nothing and never synchronises the stream. It covers the decode sequences
+ * (bf16, bias / threshold selection, 1..16 tokens as ffn_sparse_forward_path
+ * reports 1, 2 or 3) with d_ff <= 32768; other configs or token counts return
+ * FFN_E_UNSUPPORTED, and a call whose scratch would exceed the array returns
+ * FFN_E_WORKSPACE, both before anything is launched. The array is set up by
+ * ffn_sparse_init on the current device (or by the first call on a device,
+ * which then synchronises `stream` once). Every no-allocation call on one GPU
+ * shares the array, which keeps the last call's contents (nothing in it needs
+ * clearing between calls): calls that overlap on one GPU, on different
+ * streams or from different handles, race and must not be issued. */
+ffn_status ffn_sparse_forward_noalloc(ffn_sparse_handle *h, const void *x, int32_t m,
+                                      const float *bias, float bias_scalar, const float *tau,
+                                      int32_t k, ffn_twell_pack *pack, void *y, void *stream);
+
+/* Size in bytes of the per-GPU scratch array of ffn_sparse_forward_noalloc. */
+size_t ffn_sparse_noalloc_scratch_bytes(void);
+
 /* Error state of the work enqueued so far on `stream` (synchronises it).
  * The kernels' cross-workgroup waits (the TwELL look-back of sub-tiled gate
  * tiles) are bounded: a wait that gives up lets its kernel finish and raises
  * an error word in the workspace. Returns FFN_OK, or FFN_E_HIP when a launch
  * failed earlier or a wait gave up; the handle is then marked failed and every
  * later call returns FFN_E_HIP until it is re-initialised with
- * ffn_sparse_init (which clears the error word). FFN_E_INVALID for a null
- * handle. */
+ * ffn_sparse_init (which clears the error word). A wait that gave up in a
+ * no-allocation call on this device is reported too. FFN_E_INVALID for a
+ * null handle. */
 ffn_status ffn_sparse_device_status(ffn_sparse_handle *h, void *stream);
 
 /* Test hook for the give-up path of the bounded waits: from the next call on,
