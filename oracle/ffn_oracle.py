@@ -143,6 +143,41 @@ def wina_scores(h, col_norms) -> np.ndarray:
     return np.abs(np.asarray(h, dtype=np.float64)) * np.asarray(col_norms, dtype=np.float64)
 
 
+def input_column_norms(w) -> np.ndarray:
+    """c_j = || W[:, j] ||_2 for input channel j of a linear layer W
+    [out x in]: the weight column that input element j multiplies.
+
+    [WINA page, section 3.1, applied to a layer's input: the weight part of
+    the score of input element j.] For the gate projection W is W_gate, or V
+    for the low-rank gate U (V x).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    return np.sqrt(np.sum(w * w, axis=0))
+
+
+def input_scores(x, col_norms) -> np.ndarray:
+    """s_j = |x_j| * c_j for every input channel j. [WINA page, section
+    3.1; with equal c_j this is the hidden-state magnitude rule of TEAL and
+    CATS that section 二 describes.]"""
+    return np.abs(np.asarray(x, dtype=np.float64)) * np.asarray(col_norms, dtype=np.float64)
+
+
+def gate_preactivation_input_sparse(x, kept, w_gate=None, u=None, v=None) -> np.ndarray:
+    """Gate pre-activation from the kept input channels only:
+    g_t = W_gate[:, S_t] x_t[S_t], or for the low-rank gate
+    g_t = U (V[:, S_t] x_t[S_t]) with the rank-r intermediate in fp64.
+    kept[t] lists S_t. [WINA page, section 3.1: the input elements outside
+    the kept set are treated as zero in the layer they feed.]
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_gate if w_gate is not None else v, dtype=np.float64)
+    first = np.stack([w[:, np.asarray(kept[t], dtype=np.int64)] @ x[t, np.asarray(kept[t], dtype=np.int64)]
+                      for t in range(x.shape[0])]) if x.shape[0] else np.zeros((0, w.shape[0]))
+    if w_gate is not None:
+        return first
+    return first @ np.asarray(u, dtype=np.float64).T
+
+
 def topk_lower_index(s_row, k: int) -> np.ndarray:
     """Indices of the k largest scores of one token, ties to the lower
     index, returned in ascending index order."""
@@ -226,9 +261,20 @@ def forward(wl, k: int | None = None, E: int | None = None, T: int | None = None
     m, f = wl.m, wl.f
     x = np.asarray(wl.x, dtype=np.float64)
     b = wl.bias_per_token() if bias is None else np.asarray(bias, dtype=np.float64)
-    g = gate_preactivation(x, wl.w_gate, wl.u, wl.v)
+    out = {}
+    k_in = getattr(wl, "in_keep", 0) or 0
+    if k_in:
+        # input-side selection of the gate projection: the k_in input channels
+        # with the largest |x_j| * ||W[:, j]||_2 (ties to the lower index)
+        c_in = input_column_norms(wl.w_gate if wl.w_gate is not None else wl.v)
+        s_in = input_scores(x, c_in)
+        kept = [topk_lower_index(s_in[t], k_in) for t in range(m)]
+        g = gate_preactivation_input_sparse(x, kept, wl.w_gate, wl.u, wl.v)
+        out.update(in_norms=c_in, in_scores=s_in, in_kept=kept)
+    else:
+        g = gate_preactivation(x, wl.w_gate, wl.u, wl.v)
     z = g + b.reshape(-1, 1)
-    out = {"g": g, "z": z}
+    out.update(g=g, z=z)
 
     if wl.sel == SEL_TOPK:
         a = activation(z, wl.act)
@@ -272,7 +318,8 @@ def dense_forward(wl, bias=None, tau=None) -> np.ndarray:
     """The same function evaluated densely over every neuron.
 
     Bias / threshold gates keep their elementwise mask; a top-k gate keeps
-    every neuron (the unsparsified FFN it approximates).
+    every neuron (the unsparsified FFN it approximates). The gate reads every
+    input channel (no input-side selection).
     """
     x = np.asarray(wl.x, dtype=np.float64)
     b = wl.bias_per_token() if bias is None else np.asarray(bias, dtype=np.float64)

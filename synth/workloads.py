@@ -83,6 +83,12 @@ CONFIGS = {
                dtype="bf16", act="silu", sel="topk", T=128, E=128),
     "c5": dict(num=5, name="prefill-hybrid-relu-bf16-2048x8192", d=2048, f=8192, rank=0,
                ms=(4096,), dtype="bf16", act="relu", sel="bias", T=1024, E=128),
+    # input-side selection of the gate projection (half of the input channels
+    # kept per token) on the 1B decode and LoPA shapes
+    "c6": dict(num=6, name="input-wina-gate-bf16-2048x8192", d=2048, f=8192, rank=0, ms=(1,),
+               dtype="bf16", act="relu", sel="bias", T=128, E=128, in_keep_frac=0.5),
+    "c7": dict(num=7, name="lopa-input-wina-bf16-4096x14336-r512", d=4096, f=14336, rank=512,
+               ms=(1,), dtype="bf16", act="relu", sel="thresh", T=128, E=128, in_keep_frac=0.5),
 }
 
 # stream ids
@@ -147,6 +153,7 @@ class Workload:
     delta: np.ndarray | None = None
     attempts: np.ndarray | None = None
     info: dict = field(default_factory=dict)
+    in_keep: int = 0          # input channels the gate keeps per token (0: all)
 
     def storage(self, a: np.ndarray) -> np.ndarray:
         """Array in the device storage type: fp32, or bf16 bit patterns."""
@@ -169,17 +176,41 @@ class Workload:
 class _Calib:
     """fp64 gate pre-activation and WINA scores used only to place cuts."""
 
-    def __init__(self, w_gate=None, u=None, v=None, w_up=None, w_down=None):
+    def __init__(self, w_gate=None, u=None, v=None, w_up=None, w_down=None, in_keep=0):
         self.w_gate, self.u, self.v, self.w_up = w_gate, u, v, w_up
         self.col_norm = None
         if w_down is not None:
             self.col_norm = np.sqrt(np.einsum("oi,oi->i", w_down, w_down))
+        self.in_keep = in_keep
+        if in_keep:
+            w_in = w_gate if w_gate is not None else v
+            self.in_norm = np.sqrt(np.einsum("oi,oi->i", w_in, w_in))
+
+    def input_order(self, x: np.ndarray):
+        """Input channels of one token by (|x_j| * column norm) desc, index asc."""
+        sc = np.abs(x) * self.in_norm
+        return np.lexsort((np.arange(sc.size), -sc)), sc
 
     def gate(self, xs: np.ndarray) -> np.ndarray:
-        """Pre-activation for tokens xs [n, d] -> [n, f]."""
+        """Pre-activation for tokens xs [n, d] -> [n, f] (from the kept input
+        channels when the workload selects them)."""
+        if self.in_keep:
+            xs = xs.copy()
+            for row in range(xs.shape[0]):
+                order, _ = self.input_order(xs[row])
+                xs[row, order[self.in_keep:]] = 0.0
         if self.w_gate is not None:
             return xs @ self.w_gate.T
         return (xs @ self.v.T) @ self.u.T
+
+    def input_gap_ok(self, x: np.ndarray) -> bool:
+        """The k_in-th and (k_in+1)-th input scores differ by 2**-11 relative
+        (the kept set is then the same under any fp32 evaluation)."""
+        if not self.in_keep or self.in_keep >= x.size:
+            return True
+        order, sc = self.input_order(x)
+        a, b = sc[order[self.in_keep - 1]], sc[order[self.in_keep]]
+        return a - b >= 2.0 ** -11 * a
 
     def wina_scores(self, xs: np.ndarray, bias: float = 0.0) -> np.ndarray:
         z = self.gate(xs) + bias
@@ -308,15 +339,18 @@ def _place_cut(cid, cfg, t, g, sc, f, k, num, seed, bias, tau, delta, info) -> b
 
 def make_workload(cid: str, m: int | None = None, seed: int = 0, *, d: int | None = None,
                   f: int | None = None, rank: int | None = None, T: int | None = None,
-                  E: int | None = None, k: int | None = None, certify: bool = True) -> Workload:
-    """Build one seeded instance of workload ``cid`` ("c1".."c5").
+                  E: int | None = None, k: int | None = None, certify: bool = True,
+                  in_keep: int | None = None) -> Workload:
+    """Build one seeded instance of workload ``cid`` ("c1".."c7").
 
     ``d``, ``f``, ``rank``, ``T``, ``E`` and ``k`` override the table for
     reduced-size test instances; the distributions and rules are unchanged.
     ``certify=False`` takes every token's first draw and places its cut at the
     requested count without a guard band (delta = 0): the inputs of the
     tolerant comparison, where a neuron within the kernels' error bound of
-    the cut may legitimately fall on either side.
+    the cut may legitimately fall on either side. ``in_keep`` overrides the
+    number of input channels the gate keeps (workloads with input-side
+    selection; a certified draw also leaves a gap at that count).
     """
     cfg = dict(CONFIGS[cid])
     num = cfg["num"]
@@ -345,7 +379,9 @@ def make_workload(cid: str, m: int | None = None, seed: int = 0, *, d: int | Non
         n_out = int(math.ceil(_OUTLIER_FRAC * d))
         outliers = np.sort(_rng(num, seed, _S_OUTLIER).choice(d, size=n_out, replace=False))
 
-    calib = _Calib(w_gate, u, v, w_up, w_down if cfg["sel"] == "topk" else None)
+    if in_keep is None:
+        in_keep = int(round(cfg.get("in_keep_frac", 0.0) * d))
+    calib = _Calib(w_gate, u, v, w_up, w_down if cfg["sel"] == "topk" else None, in_keep=in_keep)
     x = np.zeros((m, d))
     attempts = np.zeros(m, dtype=np.int64)
     delta = np.zeros(m)
@@ -368,13 +404,14 @@ def make_workload(cid: str, m: int | None = None, seed: int = 0, *, d: int | Non
         if pending.size == 0:
             break
         xs = np.stack([rnd(_draw_x(cfg, num, seed, t, a, d, outliers)) for t in pending])
+        in_ok = [calib.input_gap_ok(xs[row]) or not certify for row in range(len(pending))]
         gs = calib.gate(xs)
         scs = calib.wina_scores(xs) if cfg["sel"] == "topk" else None
         failed = []
         place = _place_cut if certify else _place_cut_plain
         for row, t in enumerate(pending):
-            ok = place(cid, cfg, t, gs[row], None if scs is None else scs[row], f, k,
-                       num, seed, bias, tau, delta, info)
+            ok = in_ok[row] and place(cid, cfg, t, gs[row], None if scs is None else scs[row], f, k,
+                                      num, seed, bias, tau, delta, info)
             if ok:
                 x[t] = xs[row]
                 attempts[t] = a
@@ -390,4 +427,5 @@ def make_workload(cid: str, m: int | None = None, seed: int = 0, *, d: int | Non
                     act=cfg["act"], sel=cfg["sel"], T=T, E=E, k=int(k), seed=seed, x=x,
                     w_up=w_up, w_down=w_down, w_gate=w_gate, u=u, v=v,
                     bias=bias if cid != "c1" else None, bias_scalar=bias_scalar,
-                    tau=tau, delta=delta, attempts=attempts, info=dict(info, certified=certify))
+                    tau=tau, delta=delta, attempts=attempts, info=dict(info, certified=certify),
+                    in_keep=int(in_keep))

@@ -22,6 +22,10 @@ def _pins_pass() -> bool:
         lambda: [P.test_twell_roundtrip(*c) for c in P.SMALL],
         lambda: P.test_topk_tie_break_lower_index(),
         lambda: P.test_lowrank_bruteforce_distinct_factors(),
+        lambda: P.test_input_wina_hand_example(),
+        lambda: P.test_input_wina_lemma31_optimal_for_orthogonal_columns(),
+        lambda: P.test_input_equal_norms_is_magnitude_topk(),
+        lambda: P.test_input_keep_all_equals_full_gate(),
     ]
     for chk in checks:
         try:
@@ -119,3 +123,46 @@ def test_mutation_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(O, attr, fn)
     assert not _pins_pass(), f"planted mistake {name!r} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# input-side selection of the gate projection
+# ---------------------------------------------------------------------------
+
+_orig_in_norms = O.input_column_norms
+_orig_in_scores = O.input_scores
+_orig_in_gate = O.gate_preactivation_input_sparse
+
+
+def _in_norms_of_rows(w):
+    w = np.asarray(w, dtype=np.float64)
+    r = np.sqrt(np.sum(w * w, axis=1))
+    return np.resize(r, w.shape[1])
+
+
+def _in_scores_magnitude_only(x, col_norms):
+    return np.abs(np.asarray(x, dtype=np.float64)) + 0.0 * np.asarray(col_norms)
+
+
+def _in_scores_squared_norm(x, col_norms):
+    return np.abs(np.asarray(x, dtype=np.float64)) * np.asarray(col_norms, dtype=np.float64) ** 2
+
+
+def _in_gate_ignores_selection(x, kept, w_gate=None, u=None, v=None):
+    return O.gate_preactivation(x, w_gate, u, v)
+
+
+def _in_gate_drops_last_kept(x, kept, w_gate=None, u=None, v=None):
+    return _orig_in_gate(x, [k[:-1] if len(k) else k for k in kept], w_gate, u, v)
+
+
+@pytest.mark.parametrize("name,attr,fn", [
+    ("row norms for column norms", "input_column_norms", _in_norms_of_rows),
+    ("|x| only", "input_scores", _in_scores_magnitude_only),
+    ("squared column norm", "input_scores", _in_scores_squared_norm),
+    ("selection ignored", "gate_preactivation_input_sparse", _in_gate_ignores_selection),
+    ("last kept channel dropped", "gate_preactivation_input_sparse", _in_gate_drops_last_kept),
+])
+def test_input_mutation_caught(monkeypatch, name, attr, fn):
+    monkeypatch.setattr(O, attr, fn)
+    assert not _pins_pass(), f"planted mistake not caught: {name}"

@@ -349,3 +349,117 @@ def test_generator_guard_band(cid, m, kw):
             cut = 0.0 if wl.sel == "bias" else max(wl.tau[t], 0.0)
             assert np.min(np.abs(z[t] - cut)) >= dl > 0
             assert int(ref["mask"][t].sum()) == int(wl.info["count"][t])
+
+
+# ---------------------------------------------------------------------------
+# input-side selection of the gate projection (WINA page, section 3.1 applied
+# to the gate's input; section 二 for the |x|-only rule)
+# ---------------------------------------------------------------------------
+
+def _read_input_toy():
+    sec, inp, exp = None, {}, []
+    for line in open(os.path.join(GOLDEN, "input_wina_toy.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("["):
+            sec = line
+            continue
+        parts = line.split()
+        if sec == "[inputs]":
+            inp[parts[0]] = [float(v) for v in parts[1:]]
+        elif parts[0] in ("c", "s"):
+            inp["exp_" + parts[0]] = [float(v) for v in parts[1:]]
+        else:
+            k = int(parts[1])
+            gi = parts.index("g")
+            exp.append((k, [int(v) for v in parts[3:gi]], [float(v) for v in parts[gi + 1:]]))
+    return inp, exp
+
+
+def test_input_wina_hand_example():
+    inp, exp = _read_input_toy()
+    x = np.array([inp["x"]])
+    cols = np.array(inp["w_gate_columns"]).reshape(4, 2)        # column j
+    w_gate = cols.T                                               # [F x d]
+    c = O.input_column_norms(w_gate)
+    assert list(c) == inp["exp_c"]
+    s = O.input_scores(x, c)[0]
+    assert list(s) == inp["exp_s"]
+    for k, kept, g in exp:
+        sel = O.topk_lower_index(s, k)
+        assert list(sel) == kept
+        assert list(O.gate_preactivation_input_sparse(x, [sel], w_gate=w_gate)[0]) == g
+        # the same gate as a low-rank factorisation: V = W_gate, U = I
+        gl = O.gate_preactivation_input_sparse(x, [sel], u=np.eye(2), v=w_gate)[0]
+        assert list(gl) == g
+    full = O.gate_preactivation(x, w_gate=w_gate)[0]
+    assert list(full) == exp[-1][2]
+
+
+def test_input_wina_lemma31_optimal_for_orthogonal_columns():
+    """For a layer with orthogonal columns the kept input set minimises
+    || W x - W_S x_S ||^2 over every k-subset, with minimum sum over dropped
+    channels of (x_j c_j)^2 (WINA page, section 3.2, Lemma 3.1, on the input
+    side)."""
+    import itertools
+    rng = np.random.default_rng(11)
+    for trial in range(4):
+        d, out = 6, 9
+        q, _ = np.linalg.qr(rng.standard_normal((out, d)))
+        w = q * rng.uniform(0.2, 3.0, size=d)                    # orthogonal columns, norms vary
+        x = rng.standard_normal((1, d)) * rng.uniform(0.1, 4.0, size=d)
+        c = O.input_column_norms(w)
+        s = O.input_scores(x, c)[0]
+        full = w @ x[0]
+        for k in range(0, d + 1):
+            sel = O.topk_lower_index(s, k)
+            err = np.sum((full - O.gate_preactivation_input_sparse(x, [sel], w_gate=w)[0]) ** 2)
+            best = min(np.sum((full - w[:, list(S)] @ x[0, list(S)]) ** 2) for S in itertools.combinations(range(d), k))
+            assert err <= best * (1 + 1e-9) + 1e-12
+            dropped = [j for j in range(d) if j not in set(sel.tolist())]
+            assert abs(err - np.sum((x[0, dropped] * c[dropped]) ** 2)) <= 1e-9 * max(1.0, err)
+
+
+def test_input_keep_all_equals_full_gate():
+    for cid, kw in (("c6", dict(d=256, f=512, T=128, E=128)), ("c7", dict(d=256, f=512, rank=64, T=128, E=128))):
+        wl = make_workload(cid, 3, 2, in_keep=256, **kw)
+        a = O.forward(wl)
+        g_full = O.gate_preactivation(wl.x, wl.w_gate, wl.u, wl.v)
+        assert np.max(np.abs(a["g"] - g_full)) <= 1e-12 * np.max(np.abs(g_full))
+        assert all(len(k) == 256 for k in a["in_kept"])
+
+
+def test_input_equal_norms_is_magnitude_topk():
+    """With every column norm equal the rule keeps the k largest |x_j|,
+    ties to the lower index (section 二's hidden-state rule)."""
+    rng = np.random.default_rng(5)
+    d, out, k = 32, 8, 12
+    w = rng.choice([-1.0, 1.0], size=(out, d))                   # every column norm exactly sqrt(8)
+    x = np.round(rng.standard_normal((1, d)) * 4) / 4            # many exact ties in |x|
+    s = O.input_scores(x, O.input_column_norms(w))[0]
+    sel = O.topk_lower_index(s, k)
+    mags = np.abs(x[0])
+    want = sorted(sorted(range(d), key=lambda j: (-mags[j], j))[:k])
+    assert np.array_equal(s, mags * np.sqrt(8.0))
+    assert list(sel) == want
+
+
+def test_input_sparse_forward_matches_bruteforce():
+    """The whole forward pass with the input-side gate: dense numpy with the
+    dropped input channels zeroed in the gate only (the up and down products
+    use the whole x)."""
+    for cid, kw in (("c6", dict(d=128, f=256, T=64, E=64)), ("c7", dict(d=128, f=256, rank=32, T=64, E=64))):
+        wl = make_workload(cid, 3, 4, **kw)
+        out = O.forward(wl)
+        for t in range(wl.m):
+            xg = np.zeros(wl.d)
+            kept = out["in_kept"][t]
+            xg[kept] = wl.x[t, kept]
+            g = wl.w_gate @ xg if wl.w_gate is not None else wl.u @ (wl.v @ xg)
+            z = g + wl.bias_per_token()[t]
+            cut = 0.0 if wl.sel == "bias" else max(wl.tau[t], 0.0)
+            a = np.where(z > cut, z, 0.0)
+            y = wl.w_down @ (a * (wl.w_up @ wl.x[t]))
+            assert np.allclose(out["y"][t], y, rtol=1e-12, atol=1e-12)
+            assert len(kept) == wl.in_keep
