@@ -28,7 +28,7 @@ EXPORTS = [
 class Config(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("d_ff", c_int32), ("rank", c_int32), ("dtype", c_int32),
                 ("act", c_int32), ("sel", c_int32), ("tile_w", c_int32), ("ell_w", c_int32),
-                ("wdown_out_major", c_int32), ("max_m", c_int32)]
+                ("wdown_out_major", c_int32), ("max_m", c_int32), ("in_keep", c_int32)]
 
 
 class Pack(ctypes.Structure):

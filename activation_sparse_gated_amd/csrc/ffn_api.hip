@@ -141,6 +141,12 @@ struct Workspace {
   int32_t* ul_total;     // [1] decode split mode: union-list length
   int32_t* ul_nrn;       // [F] decode split mode: union neurons
   float* ul_h;           // decode split mode: hT, bf16 [kDecMaxM][F rounded up to 32]
+  uint16_t* in_wt;       // input-side gate: W^T [d x N] (N = F, or rank)
+  float* in_norm;        // input-side gate: [d] column norms of W_gate (or V)
+  int32_t* in_kidx;      // input-side gate: [max_m x in_keep] kept channels
+  uint16_t* in_kval;     // input-side gate: [max_m x in_keep] their x values
+  float* in_part;        // input-side gate: [groups x max_m x N] partial sums
+  int in_groups;
   size_t total;
 };
 
@@ -207,6 +213,15 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
   w.ul_total = (int32_t*)take(sizeof(int32_t));
   w.ul_nrn = (int32_t*)take(F * sizeof(int32_t));
   w.ul_h = (float*)take((size_t)kDecMaxM * ((F + 31) / 32 * 32) * sizeof(uint16_t));
+  if (c.in_keep > 0) {
+    const size_t N = r ? r : F, k = c.in_keep;
+    w.in_groups = in_groups((int)N, (int)k);
+    w.in_wt = (uint16_t*)take(d * N * sizeof(uint16_t));
+    w.in_norm = (float*)take(d * sizeof(float));
+    w.in_kidx = (int32_t*)take(M * k * sizeof(int32_t));
+    w.in_kval = (uint16_t*)take(M * k * sizeof(uint16_t));
+    w.in_part = (float*)take((size_t)w.in_groups * M * N * sizeof(float));
+  }
   w.total = off;
   return w;
 }
@@ -408,6 +423,22 @@ EpiDesc epi_base(const ffn_sparse_handle* h, const float* bias, float bias_scala
   return e;
 }
 
+// One-token dense stream (k_sgemv.hip) for bf16 configs, m = 1 without a
+// gathered token list; false when it does not apply.
+bool one_token_stream(const ffn_sparse_handle* h, int m, const int32_t* gather, const int32_t* m_dev) {
+  return m == 1 && !gather && !m_dev && h->cfg.dtype == FFN_BF16 && !h->tune.no_gemv;
+}
+
+Sgemv1Desc sg_base(const ffn_sparse_handle* h, const float* bias, float bias_scalar, const float* tau) {
+  Sgemv1Desc d{};
+  d.bias = bias;
+  d.bias_scalar = bias_scalar;
+  d.tau = tau;
+  d.sel = h->cfg.sel;
+  d.act = h->cfg.act;
+  return d;
+}
+
 // First stage of the low-rank gate, t = V x, for `m` token slots (optionally
 // gathered): ks workgroups split K and each writes an fp32 slab
 // [m x rank] at lr_slabs + slab * max_m * rank. Returns the slab count.
@@ -424,6 +455,20 @@ int run_lowrank_v(ffn_sparse_handle* h, const void* x, int m, const int32_t* gat
   g.M = m;
   g.gather = gather;
   g.m_dev = m_dev;
+  if (one_token_stream(h, m, gather, m_dev)) {      // one token: a plain weight stream
+    Sgemv1Desc d = sg_base(h, nullptr, 0.f, nullptr);
+    d.N = c.rank;
+    d.K = c.d_model;
+    d.A = reinterpret_cast<const uint16_t*>(h->v);
+    d.vec = reinterpret_cast<const uint16_t*>(x);
+    d.epi = SG_OUT;
+    d.out = h->ws.lr_slabs;
+    if (sgemv1_plan(d, h->cus)) {
+      Timed tm(h, FFN_K_LOWRANK_V, s);
+      *err = launch_sgemv1(d, s);
+      return 1;
+    }
+  }
   if (!plan_plain(g, h)) {
     *err = hipErrorInvalidValue;
     return 0;
@@ -492,6 +537,35 @@ hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const in
                             const int32_t* m_dev, const float* bias, float bias_scalar,
                             const float* tau, int kind, hipStream_t s) {
   const auto& c = h->cfg;
+  if (one_token_stream(h, m, list, m_dev)) {
+    // one token: the up rows with the gate rows (W_gate with x, or U with
+    // t = V x) in one stream, h written as bf16
+    Sgemv1Desc d = sg_base(h, bias, bias_scalar, tau);
+    d.N = c.d_ff;
+    d.K = c.d_model;
+    d.A = reinterpret_cast<const uint16_t*>(h->w_up);
+    d.vec = reinterpret_cast<const uint16_t*>(x);
+    d.epi = SG_HID;
+    d.hout = h->ws.hbuf;
+    if (c.rank == 0) {
+      d.Ag = reinterpret_cast<const uint16_t*>(h->w_gate);
+      d.Kg = c.d_model;
+    } else {
+      d.Ag = reinterpret_cast<const uint16_t*>(h->u);
+      d.Kg = c.rank;
+      d.vecg = h->ws.lr_slabs;
+    }
+    if (sgemv1_plan(d, h->cus)) {
+      if (c.rank) {
+        hipError_t err = hipSuccess;
+        const int nslabs = run_lowrank_v(h, x, m, nullptr, nullptr, s, &err);
+        if (err != hipSuccess) return err;
+        if (nslabs != 1) return hipErrorInvalidValue;   // the one-token first stage writes t as one slab
+      }
+      Timed tm(h, kind, s);
+      return launch_sgemv1(d, s);
+    }
+  }
   EpiDesc e = epi_base(h, bias, bias_scalar, tau);
   e.kind = EPI_DENSE_H;
   e.tok_of = list;
@@ -554,6 +628,19 @@ hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const in
 hipError_t run_dense_down(ffn_sparse_handle* h, int m, const int32_t* list, const int32_t* m_dev,
                           void* y, int kind, hipStream_t s) {
   const auto& c = h->cfg;
+  if (one_token_stream(h, m, list, m_dev)) {         // one token: the output-major rows against h
+    Sgemv1Desc d = sg_base(h, nullptr, 0.f, nullptr);
+    d.N = c.d_model;
+    d.K = c.d_ff;
+    d.A = reinterpret_cast<const uint16_t*>(h->w_down_om);
+    d.vec = reinterpret_cast<const uint16_t*>(h->ws.hbuf);
+    d.epi = SG_Y;
+    d.y = y;
+    if (sgemv1_plan(d, h->cus)) {
+      Timed tm(h, kind, s);
+      return launch_sgemv1(d, s);
+    }
+  }
   GemmDesc g = gemm_base(h);
   g.A0 = h->w_down_om;
   g.nrows = c.d_model;
@@ -634,13 +721,30 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
     g.K = c.d_model;
     g.B = x;
     g.ldb = c.d_model;
-    if (!plan_plain(g, h)) return FFN_E_UNSUPPORTED;
     e.kind = EPI_WINA;
     e.colnorm = h->ws.colnorm;
     e.s_buf = h->ws.wina_s;
     e.h_buf = h->ws.wina_h;
     hipError_t err;
-    {
+    Sgemv1Desc sd = sg_base(h, bias, bias_scalar, tau);
+    sd.N = c.d_ff;
+    sd.K = c.d_model;
+    sd.A = reinterpret_cast<const uint16_t*>(h->w_up);
+    sd.vec = reinterpret_cast<const uint16_t*>(x);
+    sd.Ag = reinterpret_cast<const uint16_t*>(h->w_gate);
+    sd.Kg = c.d_model;
+    sd.epi = SG_SCORE;
+    sd.colnorm = h->ws.colnorm;
+    sd.s_buf = h->ws.wina_s;
+    sd.h_buf = h->ws.wina_h;
+    sd.g_debug = g_debug;
+    sd.s_debug = s_debug;
+    if (one_token_stream(h, m, nullptr, nullptr) && sgemv1_plan(sd, h->cus)) {
+      // one token: gate and up rows in one stream, the score epilogue per row
+      Timed tm(h, FFN_K_GATE, s);
+      err = launch_sgemv1(sd, s);
+    } else {
+      if (!plan_plain(g, h)) return FFN_E_UNSUPPORTED;
       Timed tm(h, FFN_K_GATE, s);
       err = launch_gemm(g, e, s);
     }
@@ -671,7 +775,59 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
     Timed tm(h, FFN_K_TOPK, s);
     return hip_status(launch_topk(td, s));
   }
-  if (c.rank > 0) {
+  if (c.in_keep > 0) {
+    // input-side gate: the kept channels, then their rows of W^T in channel
+    // groups; a full gate is selected and packed from the group sums, a
+    // low-rank gate sums the groups into t and continues with U t
+    InDesc in{};
+    in.M = m;
+    in.d = c.d_model;
+    in.k = c.in_keep;
+    in.N = c.rank ? c.rank : c.d_ff;
+    in.groups = h->ws.in_groups;
+    in.x = x;
+    in.colnorm = h->ws.in_norm;
+    in.kidx = h->ws.in_kidx;
+    in.kval = h->ws.in_kval;
+    in.wt = h->ws.in_wt;
+    in.part = h->ws.in_part;
+    in.T = c.tile_w;
+    in.E = c.ell_w;
+    in.sel = c.sel;
+    in.bias = bias;
+    in.bias_scalar = bias_scalar;
+    in.tau = tau;
+    in.cnt = pack->cnt;
+    in.idx = pack->idx;
+    in.val = pack->val;
+    in.g_debug = g_debug;
+    {
+      Timed tm(h, FFN_K_LOWRANK_V, s);
+      if (launch_in_select(in, s) != hipSuccess) return FFN_E_HIP;
+    }
+    {
+      Timed tm(h, FFN_K_LOWRANK_V, s);
+      if (launch_in_gemv(in, s) != hipSuccess) return FFN_E_HIP;
+    }
+    if (c.rank == 0) {
+      Timed tm(h, FFN_K_GATE, s);
+      return hip_status(launch_in_pack(in, s));
+    }
+    {
+      Timed tm(h, FFN_K_LOWRANK_V, s);
+      if (launch_slab_sum(h->ws.in_part, in.groups, (size_t)m * in.N, (size_t)m * in.N, s) != hipSuccess)
+        return FFN_E_HIP;
+    }
+    g.A0 = h->u;
+    g.lda = c.rank;
+    g.B = h->ws.in_part;                                 // t [m x rank], fp32
+    g.ldb = c.rank;
+    g.K = c.rank;
+    g.bmode = B_F32_SPLIT;
+    g.b_nsum = 1;
+    g.b_slab = (long long)m * c.rank;
+    e.t_out = h->ws.lr_t;
+  } else if (c.rank > 0) {
     hipError_t err = hipSuccess;
     int nslabs = run_lowrank_v(h, x, m, nullptr, nullptr, s, &err);
     if (err != hipSuccess) return FFN_E_HIP;
@@ -703,7 +859,7 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
 bool plan_decode(const ffn_sparse_handle* h, int m, DecodeDesc* out) {
   const auto& c = h->cfg;
   if (c.dtype != FFN_BF16 || c.sel == FFN_SEL_TOPK_WINA || m < 1 || m > kDecMaxM) return false;
-  if (h->tune.no_decode) return false;
+  if (h->tune.no_decode || c.in_keep > 0) return false;
   DecodeDesc d{};
   d.M = m;
   d.d = c.d_model;
@@ -945,6 +1101,12 @@ ffn_status ffn_sparse_check_config(const ffn_sparse_config* c) {
   if (c->sel == FFN_SEL_TOPK_WINA && (c->ell_w != c->tile_w || c->d_ff > 32768 || c->rank != 0))
     return FFN_E_UNSUPPORTED;
   if (c->d_ff / c->tile_w > 1024) return FFN_E_UNSUPPORTED;
+  if (c->in_keep < 0 || c->in_keep > c->d_model) return FFN_E_INVALID;
+  // input-side gate selection: bf16, bias / threshold, no routing (the dense
+  // backup would read every input channel), decode-sized batches
+  if (c->in_keep > 0 && (c->dtype != FFN_BF16 || c->sel == FFN_SEL_TOPK_WINA || c->ell_w != c->tile_w ||
+                         c->max_m > 64 || c->tile_w % 64 != 0))
+    return FFN_E_UNSUPPORTED;
   return FFN_OK;
 }
 
@@ -1024,6 +1186,12 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   }
   if (err == hipSuccess && cfg->sel == FFN_SEL_TOPK_WINA)
     err = launch_rownorm(h->w_down_nm, ws.colnorm, cfg->d_ff, cfg->d_model, cfg->dtype, s);
+  if (err == hipSuccess && cfg->in_keep > 0) {
+    // the gate's input matrix input-major, and its column norms
+    const int N = cfg->rank ? cfg->rank : cfg->d_ff;
+    err = launch_transpose(cfg->rank ? v_or_null : w_gate_or_u, ws.in_wt, N, cfg->d_model, 2, s);
+    if (err == hipSuccess) err = launch_rownorm(ws.in_wt, ws.in_norm, cfg->d_model, N, cfg->dtype, s);
+  }
   if (err == hipSuccess) err = launch_fill_u32(ws.ctrl, 0u, kCtrlWords + kTicketWords, s);
   if (err == hipSuccess) err = launch_fill_u32(ws.ctrl + CTRL_SPIN_LIMIT, kDefaultSpinLimit, 1, s);
   if (err == hipSuccess)
@@ -1292,6 +1460,7 @@ ffn_status ffn_sparse_debug_waits(ffn_sparse_handle* h, uint32_t epoch_skew, uin
 
 int32_t ffn_sparse_forward_path(const ffn_sparse_handle* h, int32_t m) {
   if (!h || m < 0 || m > h->cfg.max_m) return -1;
+  if (h->cfg.in_keep > 0) return 6;
   DecodeDesc dd;
   if (plan_decode(h, m, &dd)) return 1 + dd.mode;
   if (topk_down_kind(h, m) == 1) return 4;

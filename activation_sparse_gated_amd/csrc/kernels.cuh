@@ -138,6 +138,49 @@ struct UpdownDesc {
   int rank;
   const float* bias; float bias_scalar; const float* tau; int sel;
 };
+// Input-side selection of the gate projection (k_input.hip), bf16.
+struct InDesc {
+  int M, d, k, N, groups;       // tokens, input channels, kept per token, gate outputs (F or rank), channel groups
+  const void* x;                // [M x d] bf16
+  const float* colnorm;         // [d] ||W[:, j]||_2
+  int32_t* kidx;                // [M x k] kept channels, ascending
+  uint16_t* kval;               // [M x k] their x values (bf16)
+  const uint16_t* wt;           // W^T [d x N], input-major
+  float* part;                  // [groups x M x N] partial sums over the channel groups
+  // k_in_pack (full gate): selection and TwELL pack from the summed partials
+  int T, E, sel;
+  const float* bias; float bias_scalar; const float* tau;
+  int32_t* cnt; uint16_t* idx; void* val; float* g_debug;
+};
+int in_groups(int N, int k);
+bool in_ok(const InDesc& d);
+hipError_t launch_in_select(const InDesc& d, hipStream_t s);
+hipError_t launch_in_gemv(const InDesc& d, hipStream_t s);
+hipError_t launch_in_pack(const InDesc& d, hipStream_t s);
+
+// One-token dense weight streams (k_sgemv.hip), bf16, m = 1: rows of A
+// dotted with a vector, optionally with a gate matrix per row.
+enum SgEpi : int {
+  SG_OUT = 0,    // out[row] fp32
+  SG_Y = 1,      // y[row], bf16 or fp32
+  SG_HID = 2,    // hout[row] = bf16(a(g + b) * u), the selection's mask applied
+  SG_SCORE = 3   // WINA: h = a(g + b) u, s = |h| c into h_buf / s_buf
+};
+struct Sgemv1Desc {
+  int N, K, Kg;                 // rows; contraction of A; contraction of the gate rows
+  const uint16_t* A;            // [N x K] bf16 (u rows for SG_HID / SG_SCORE)
+  const uint16_t* vec;          // [K] bf16: x, or h for the down product
+  const uint16_t* Ag;           // [N x Kg] gate rows (W_gate or U), or null
+  const float* vecg;            // [Kg] fp32 gate vector (low-rank t), or null: the gate uses vec
+  int epi;                      // SgEpi
+  float* out; void* y; int y_f32; void* hout;
+  const float* bias; float bias_scalar; const float* tau; int sel, act;
+  const float* colnorm; float* s_buf; float* h_buf; float* g_debug; float* s_debug;
+  int seg, rpb, kvec;           // set by sgemv1_plan: item elements, rows per workgroup, staged vector length
+};
+bool sgemv1_plan(Sgemv1Desc& d, int cus);
+hipError_t launch_sgemv1(const Sgemv1Desc& d, hipStream_t s);
+
 // Sparse up / down over the pack at prefill token counts, one eighth of the
 // weights per XCD (k_xcd_up: tiles j = r mod 8; k_xcd_down: y column slice r).
 struct XcdDesc {

@@ -51,10 +51,10 @@ class SparseFFN:
                  tile_w: int, ell_w: int, max_m: int, rank: int = 0, dtype: str = "bf16",
                  act: str = "relu", sel: str = "bias", w_gate: torch.Tensor | None = None,
                  u: torch.Tensor | None = None, v: torch.Tensor | None = None,
-                 wdown_out_major: bool = True, stream=None):
+                 wdown_out_major: bool = True, in_keep: int = 0, stream=None):
         self.lib = _lib.load()
         self.cfg = Config(d_model, d_ff, rank, _lib.DTYPES[dtype], _lib.ACTS[act], _lib.SELS[sel],
-                          tile_w, ell_w, 1 if wdown_out_major else 0, max_m)
+                          tile_w, ell_w, 1 if wdown_out_major else 0, max_m, in_keep)
         check(self.lib.ffn_sparse_check_config(ctypes.byref(self.cfg)), "ffn_sparse_check_config")
         self.dtype = dtype
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -148,13 +148,14 @@ class SparseFFN:
 
     def forward_path(self, m: int) -> str:
         """Kernel sequence forward() runs for m tokens: 'general',
-        'decode-chunk' / 'decode-part' / 'decode-split', or (top-k selection)
-        'topk-list' / 'topk-masked-dense' (see the C header)."""
+        'decode-chunk' / 'decode-part' / 'decode-split', (top-k selection)
+        'topk-list' / 'topk-masked-dense', or 'input-gate' (input-side gate
+        selection; see the C header)."""
         r = self.lib.ffn_sparse_forward_path(self.handle, int(m))
         if r < 0:
             raise ValueError(f"invalid token count {m}")
         return {0: "general", 1: "decode-chunk", 2: "decode-part", 3: "decode-split",
-                4: "topk-list", 5: "topk-masked-dense"}[r]
+                4: "topk-list", 5: "topk-masked-dense", 6: "input-gate"}[r]
 
     def device_status(self, stream=None) -> int:
         """FFN_OK, or FFN_E_HIP when a launch failed or a bounded wait gave up

@@ -30,6 +30,8 @@ WORKLOADS = {
     "c3": "lopa-relu-thresh-bf16-4096x14336-r512",
     "c4": "wina-silu-topk-bf16-4096x11008",
     "c5": "prefill-hybrid-relu-bf16-2048x8192",
+    "c6": "input-wina-gate-bf16-2048x8192",
+    "c7": "lopa-input-wina-bf16-4096x14336-r512",
 }
 
 
@@ -83,7 +85,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cid = args.workload
-    m = args.m if args.m is not None else {"c2": 1, "c3": 1, "c4": 1, "c5": 4096}[cid]
+    m = args.m if args.m is not None else {"c2": 1, "c3": 1, "c4": 1, "c5": 4096, "c6": 1, "c7": 1}[cid]
     t_gen = time.time()
     wl = make_workload(cid, m, 0)
     t_gen = time.time() - t_gen
@@ -104,7 +106,7 @@ def main():
         w = {k: (v.clone() if v is not None else None) for k, v in base.items()}
         ffn = asg.SparseFFN(d_model=wl.d, d_ff=wl.f, rank=wl.rank, dtype="bf16", act=wl.act, sel=wl.sel,
                             tile_w=wl.T, ell_w=wl.E, max_m=m, w_gate=w["w_gate"], u=w["u"], v=w["v"],
-                            w_up=w["w_up"], w_down=w["w_down"], wdown_out_major=True)
+                            w_up=w["w_up"], w_down=w["w_down"], wdown_out_major=True, in_keep=wl.in_keep)
         layers.append((ffn, ffn.new_pack(m), ffn.new_output(m), ffn.new_output(m)))
     torch.cuda.synchronize()
 
@@ -199,6 +201,11 @@ def main():
                 active.add(j * T + int(idx[t, j, s]))
     n_union = len(active)
     gate_bytes = (F * r + r * d) * 2 if r else F * d * 2
+    gate_bytes_dense = gate_bytes
+    if wl.in_keep:
+        # input-side gate: only the kept channels' rows of the input-major W_gate
+        # (or V), plus x and the column norms the selection reads
+        gate_bytes = (F * r * 2 + wl.in_keep * r * 2 if r else wl.in_keep * F * 2) + m * d * 2 + d * 4
     if wl.sel == "topk":
         gate_bytes = 2 * F * d * 2
         row_bytes = d * 2
@@ -259,6 +266,12 @@ def main():
         alg["updown"] = F * d * 2 + m * F * 2 + m * d * 2      # all of W_down, the masked h rows, y
     if wl.sel == "topk":
         alg["gate"] = 2 * F * d * 2 + m * d * 2 + 2 * m * F * 4
+    if wl.in_keep:
+        # input-side gate: the kept rows of W_gate^T (or V^T) in the channel-group
+        # stream, reported under the first-stage kind; the gate kind is the
+        # selection and pack (full gate) or U t (low rank)
+        alg["lowrank_v"] = wl.in_keep * (r if r else F) * 2 + m * d * 2 + d * 4
+        alg["gate"] = (F * r * 2 + m * r * 4 if r else 0) + pack_bytes + m * 9
     dom = max((k for k in kernels if k in alg), key=lambda k: kernels[k]["avg_us"])
     achieved = alg[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e9
     traffic = None
@@ -329,6 +342,9 @@ def main():
                    "layers_rotated": len(layers),
                    "hip_graph": bool(args.graph), "kernel_path": path},
         "effective_hbm_GBps": round(touched / (ms_sparse * 1e-3) / 1e9, 1),
+        "gate_bytes": int(gate_bytes),
+        "gate_bytes_saved": int(gate_bytes_dense - gate_bytes) if wl.in_keep else 0,
+        "in_keep": int(wl.in_keep),
         "touched_bytes": int(touched),
         "dense_ms_per_step": round(ms_dense, 5),
         "dense_effective_hbm_GBps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FFN_SPARSE_ABI_VERSION 2
+#define FFN_SPARSE_ABI_VERSION 3
 
 typedef enum {
   FFN_OK = 0,
@@ -76,6 +76,13 @@ typedef struct {
   int32_t ell_w;            /* TwELL ELL width E: 0 <= E <= T                          */
   int32_t wdown_out_major;  /* 1: w_down is [d_model x d_ff]; 0: [d_ff x d_model]      */
   int32_t max_m;            /* largest token count a call may pass (>= 1)              */
+  int32_t in_keep;          /* 0: the gate reads every input channel; 1..d_model: per  */
+                            /* token it keeps the in_keep channels j with the largest  */
+                            /* |x_j| * ||W[:, j]||_2 (W = W_gate, or V for a low-rank  */
+                            /* gate; ties to the lower index) and reads only their     */
+                            /* weights (WINA page, section 3.1, applied to the gate's  */
+                            /* input). bf16, bias / threshold selection, ell_w ==      */
+                            /* tile_w and max_m <= 64 only.                            */
 } ffn_sparse_config;
 
 /* TwELL pack (tile-wise ELLPACK) of the selected activations, token-major.
@@ -212,6 +219,10 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t
  *       kernel writes h rows with the other neurons zeroed, and a dense down
  *       GEMM multiplies them (the union of the tokens' kept sets covers most of
  *       W_down).
+ * 6 = input-side gate selection (config in_keep > 0): the kept input
+ *     channels per token, the gate from their rows of the input-major W_gate
+ *     (or V) in channel groups, the selection and pack (or, low rank, t and
+ *     then U t), the sparse up + down over the pack;
  * 0 = the general sequence (gate, sparse up + down over the TwELL pack,
  * partial-row sum, dense backup); -1 = invalid handle or m. */
 int32_t ffn_sparse_forward_path(const ffn_sparse_handle *h, int32_t m);

@@ -30,7 +30,7 @@ def make_ffn(wl, max_m=None, wdown_out_major=True, E=None, T=None):
                      max_m=max(wl.m, 1) if max_m is None else max_m,
                      w_gate=to_dev(wl, wl.w_gate), u=to_dev(wl, wl.u), v=to_dev(wl, wl.v),
                      w_up=to_dev(wl, wl.w_up), w_down=to_dev(wl, w_down),
-                     wdown_out_major=wdown_out_major)
+                     wdown_out_major=wdown_out_major, in_keep=getattr(wl, "in_keep", 0))
 
 
 def sel_args(wl, bias=None, tau=None):
@@ -148,11 +148,25 @@ def gate_error_bound(wl) -> np.ndarray:
     the bound is |U| e_t + |U| (|t| + e_t) (2**-17 + gamma_D2 (1 + 2**-8)),
     with D2 = 2 r / 32 + 32 (two MFMA passes per chunk).
     """
-    x = np.abs(np.asarray(wl.x, dtype=np.float64))
+    xs = np.asarray(wl.x, dtype=np.float64)
+    d1 = _depth(wl, wl.d)
+    if getattr(wl, "in_keep", 0):
+        # the input-side gate reads only the kept channels (the oracle's
+        # selection) and sums their products in channel groups, in any
+        # order: depth d + 1
+        from oracle import ffn_oracle as O
+        c_in = O.input_column_norms(wl.w_gate if wl.w_gate is not None else wl.v)
+        s_in = O.input_scores(xs, c_in)
+        keep = np.zeros_like(xs)
+        for t_ in range(xs.shape[0]):
+            keep[t_, O.topk_lower_index(s_in[t_], wl.in_keep)] = 1.0
+        xs = xs * keep
+        d1 = wl.d + 1
+    x = np.abs(xs)
     if wl.w_gate is not None:
-        return gamma(_depth(wl, wl.d)) * (x @ np.abs(wl.w_gate).T)
-    t = np.asarray(wl.x, dtype=np.float64) @ np.asarray(wl.v, dtype=np.float64).T
-    e_t = gamma(_depth(wl, wl.d)) * (x @ np.abs(wl.v).T)
+        return gamma(d1) * (x @ np.abs(wl.w_gate).T)
+    t = xs @ np.asarray(wl.v, dtype=np.float64).T
+    e_t = gamma(d1) * (x @ np.abs(wl.v).T)
     au = np.abs(np.asarray(wl.u, dtype=np.float64))
     d2 = wl.rank + 1 if wl.dtype == "f32" else 2 * wl.rank // 32 + 32
     return 1.01 * (e_t @ au.T + ((np.abs(t) + e_t) @ au.T) * (2.0 ** -17 + gamma(d2) * (1 + 2.0 ** -8)))

@@ -31,7 +31,7 @@ def declared_symbols():
 
 def cfg(L, **kw):
     base = dict(d_model=2048, d_ff=8192, rank=0, dtype=1, act=0, sel=0, tile_w=128, ell_w=64,
-                wdown_out_major=1, max_m=16)
+                wdown_out_major=1, max_m=16, in_keep=0)
     base.update(kw)
     return L.Config(**base)
 
@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert lib.ffn_sparse_abi_version() == 2
+    assert lib.ffn_sparse_abi_version() == 3
 
 
 def test_status_strings(L):
@@ -71,6 +71,14 @@ def test_status_strings(L):
     (dict(sel=2, act=1, ell_w=128, rank=64), -2),
     (dict(rank=48), -2),
     (dict(tile_w=24, d_ff=8184, ell_w=8), -2),
+    (dict(in_keep=1024, ell_w=128), 0),    # input-side gate selection
+    (dict(in_keep=1024, rank=512, d_model=4096, d_ff=14336, sel=1, ell_w=128), 0),
+    (dict(in_keep=2049), -1),              # more than d_model
+    (dict(in_keep=-1), -1),
+    (dict(in_keep=1024), -2),              # needs ell_w == tile_w (no routing)
+    (dict(in_keep=1024, ell_w=128, max_m=65), -2),
+    (dict(in_keep=128, ell_w=128, dtype=0, d_model=256, d_ff=1024), -2),
+    (dict(in_keep=512, ell_w=128, sel=2, act=1), -2),
 ])
 def test_check_config(L, kw, want):
     lib = L.load()
