@@ -815,8 +815,7 @@ ffn_status gate_pack_core(ffn_sparse_handle* h, const void* x, int m, const floa
     }
     {
       Timed tm(h, FFN_K_LOWRANK_V, s);
-      if (launch_slab_sum(h->ws.in_part, in.groups, (size_t)m * in.N, (size_t)m * in.N, s) != hipSuccess)
-        return FFN_E_HIP;
+      if (launch_in_sum(in, s) != hipSuccess) return FFN_E_HIP;
     }
     g.A0 = h->u;
     g.lda = c.rank;

@@ -19,7 +19,7 @@
 //                selection z = g + b > cut, and the TwELL pack of one
 //                (token, tile) per workgroup (no look-back: the workgroup owns
 //                the tile); a low-rank gate instead adds the partials into t
-//                (k_slab_sum) and continues with U t
+//                (k_in_sum) and continues with U t
 #include <algorithm>
 
 #include "common.cuh"
@@ -159,6 +159,31 @@ __global__ __launch_bounds__(64 * kInGemvWaves) void k_in_gemv(const InDesc d) {
   }
 }
 
+// Sum of the channel groups' partials of output element o (token-major index
+// t N + n), in group order, 16 loads in flight at a time.
+__device__ __forceinline__ float group_sum(const InDesc& d, size_t o) {
+  const size_t stride = (size_t)d.M * d.N;
+  float g = 0.f;
+  for (int g0 = 0; g0 < d.groups; g0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = g0 + i < d.groups ? d.part[(size_t)(g0 + i) * stride + o] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (g0 + i < d.groups) g += v[i];
+  }
+  return g;
+}
+
+// ------------------------------------------------------------------ k_in_sum
+// Low-rank gate: t = the groups' partials summed in group order, into the
+// first group's slab.
+__global__ __launch_bounds__(256) void k_in_sum(const InDesc d) {
+  const size_t o = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= (size_t)d.M * d.N) return;
+  d.part[o] = group_sum(d, o);
+}
+
 // ------------------------------------------------------------------ k_in_pack
 constexpr int kInPackThreads = 256;
 
@@ -180,8 +205,7 @@ __global__ __launch_bounds__(kInPackThreads) void k_in_pack(const InDesc d) {
     bal[i] = 0ull;
     if (ch < nch) {
       const int n = j * T + ch * 64 + lane;
-      float g = 0.f;
-      for (int gr = 0; gr < d.groups; ++gr) g += d.part[((size_t)gr * d.M + t) * d.N + n];
+      const float g = group_sum(d, (size_t)t * d.N + n);
       if (d.g_debug) d.g_debug[(size_t)t * d.N + n] = g;
       z[i] = g + b;
       bal[i] = ballot64(z[i] > cut);
@@ -218,11 +242,14 @@ __global__ __launch_bounds__(kInPackThreads) void k_in_pack(const InDesc d) {
 }
 
 // ------------------------------------------------------------------ launches
+// Channel groups: about 256 workgroups in all, but at most 32 groups (each
+// output then sums at most 32 partials), and at least enough that a group
+// fits the waves' loads.
 int in_groups(int N, int k) {
   const int S = (N + 511) / 512;
-  int g = std::max(1, 256 / S);
+  int g = std::max(1, std::min(32, 256 / S));
   g = std::min(g, std::max(1, k));
-  while ((k + g - 1) / g > kInGemvWaves * kInMaxPerWave) ++g;   // channels per group within the waves' reach
+  while ((k + g - 1) / g > kInGemvWaves * kInMaxPerWave) ++g;
   return g;
 }
 
@@ -242,6 +269,13 @@ hipError_t launch_in_gemv(const InDesc& d, hipStream_t s) {
   if (!in_ok(d)) return hipErrorInvalidValue;
   const int S = (d.N + 511) / 512;
   ffn_launch(k_in_gemv, dim3(S * d.groups, d.M), dim3(64 * kInGemvWaves), 0, s, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_in_sum(const InDesc& d, hipStream_t s) {
+  if (!in_ok(d)) return hipErrorInvalidValue;
+  const size_t n = (size_t)d.M * d.N;
+  ffn_launch(k_in_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, d);
   return hipGetLastError();
 }
 

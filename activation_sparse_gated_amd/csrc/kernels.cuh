@@ -156,6 +156,7 @@ int in_groups(int N, int k);
 bool in_ok(const InDesc& d);
 hipError_t launch_in_select(const InDesc& d, hipStream_t s);
 hipError_t launch_in_gemv(const InDesc& d, hipStream_t s);
+hipError_t launch_in_sum(const InDesc& d, hipStream_t s);
 hipError_t launch_in_pack(const InDesc& d, hipStream_t s);
 
 // One-token dense weight streams (k_sgemv.hip), bf16, m = 1: rows of A
