@@ -1,4 +1,4 @@
-"""ctypes view of the C ABI in include/ffn_sparse.h (no computation here)."""
+"""ctypes view of the C ABI in include/ffn_sparse.h and include/ffn_gsi.h (no computation here)."""
 from __future__ import annotations
 
 import ctypes
@@ -22,13 +22,21 @@ EXPORTS = [
     "ffn_sparse_forward_path", "ffn_sparse_timing_enable", "ffn_sparse_timing_read", "ffn_sparse_destroy",
     "ffn_sparse_device_status", "ffn_sparse_debug_waits", "ffn_sparse_forward_noalloc",
     "ffn_sparse_noalloc_scratch_bytes",
+    "ffn_gsi_check_config", "ffn_gsi_workspace_bytes", "ffn_gsi_init", "ffn_gsi_forward",
+    "ffn_gsi_dense_forward", "ffn_gsi_image", "ffn_gsi_timing_enable", "ffn_gsi_timing_read",
+    "ffn_gsi_destroy",
 ]
+GSI_KERNEL_KINDS = {"proj": 0, "resid": 1, "out": 2, "dense": 3}
 
 
 class Config(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("d_ff", c_int32), ("rank", c_int32), ("dtype", c_int32),
                 ("act", c_int32), ("sel", c_int32), ("tile_w", c_int32), ("ell_w", c_int32),
                 ("wdown_out_major", c_int32), ("max_m", c_int32), ("in_keep", c_int32)]
+
+
+class GsiConfig(ctypes.Structure):
+    _fields_ = [("d_in", c_int32), ("d_out", c_int32), ("k", c_int32), ("max_m", c_int32)]
 
 
 class Pack(ctypes.Structure):
@@ -81,6 +89,17 @@ def load() -> ctypes.CDLL:
                                                  c_int32, P(Pack), c_void_p, c_void_p]),
         "ffn_sparse_noalloc_scratch_bytes": (c_size_t, []),
         "ffn_sparse_debug_waits": (c_int32, [c_void_p, ctypes.c_uint32, ctypes.c_uint32, c_void_p]),
+        "ffn_gsi_check_config": (c_int32, [P(GsiConfig)]),
+        "ffn_gsi_workspace_bytes": (c_size_t, [P(GsiConfig)]),
+        "ffn_gsi_init": (c_int32, [P(GsiConfig), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
+                                   P(c_void_p)]),
+        "ffn_gsi_forward": (c_int32, [c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p]),
+        "ffn_gsi_dense_forward": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+        "ffn_gsi_image": (c_void_p, [c_void_p]),
+        "ffn_gsi_timing_enable": (c_int32, [c_void_p, c_int32, c_int32]),
+        "ffn_gsi_timing_read": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_double)]),
+        "ffn_gsi_destroy": (None, [c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -32,6 +32,7 @@ WORKLOADS = {
     "c5": "prefill-hybrid-relu-bf16-2048x8192",
     "c6": "input-wina-gate-bf16-2048x8192",
     "c7": "lopa-input-wina-bf16-4096x14336-r512",
+    "gsi": "gsi-linear-bf16-4096x14336-k256",
 }
 
 
@@ -85,6 +86,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cid = args.workload
+    if cid == "gsi":
+        return bench_gsi(args, dev)
     m = args.m if args.m is not None else {"c2": 1, "c3": 1, "c4": 1, "c5": 4096, "c6": 1, "c7": 1}[cid]
     t_gen = time.time()
     wl = make_workload(cid, m, 0)
@@ -355,6 +358,176 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
+        "input_gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(out))
+
+
+def bench_gsi(args, dev):
+    """The gated subspace linear map ("Gated Subspace Inference for
+    Transformer Acceleration", sections 2.1-2.2) on the LoPA FFN's up
+    projection, d = 4096 -> 14336, k = 256, eps = 0.10: a step is one gated
+    forward call over the batch (projection, residual gate, image or full
+    product); the baseline is y = W x on the same tokens."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_amd as asg
+    from synth.gsi import make_gsi_config
+
+    m = args.m if args.m is not None else 1
+    t_gen = time.time()
+    wl = make_gsi_config("gsi", m=m, seed=0)
+    t_gen = time.time() - t_gen
+    note(f"inputs gsi m={m} generated in {t_gen:.1f}s")
+
+    def dev_bf16(a):
+        from synth import bf16_bits
+        return torch.from_numpy(bf16_bits(np.ascontiguousarray(a)).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w0, v0 = dev_bf16(wl.w), dev_bf16(wl.vk)
+    x = dev_bf16(wl.x)
+    layers = []
+    for _ in range(args.layers):
+        lin = asg.GsiLinear(w0.clone(), v0.clone(), max_m=m)
+        bufs = (lin.new_output(m), torch.empty(max(m, 1), dtype=torch.float32, device=dev),
+                torch.empty(max(m, 1), dtype=torch.int32, device=dev), torch.empty(4, dtype=torch.int32, device=dev),
+                lin.new_output(m))
+        layers.append((lin, bufs))
+    torch.cuda.synchronize()
+
+    def step(i):
+        lin, (y, rho, sl, ns, _) = layers[i % len(layers)]
+        lin.forward(x, wl.eps, y=y, rho=rho, slow_list=sl, n_slow=ns)
+
+    def dense_step(i):
+        lin, (_, _, _, _, yd) = layers[i % len(layers)]
+        lin.dense_forward(x, y=yd)
+
+    def timed(fn, n, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(warm + i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            step(i)
+        torch.cuda.synchronize()
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": f"{WORKLOADS['gsi']} m={m}",
+                          "copy_bytes": src.numel()}))
+        return
+
+    ms = timed(step, args.steps, args.warmup)
+    note(f"gsi step {ms * 1e3:.2f} us")
+    ms_dense = timed(dense_step, max(20, args.steps // 4), 5)
+    note(f"dense step {ms_dense * 1e3:.2f} us")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    dist = {"p10": round(float(np.percentile(us, 10)), 3), "p50": round(float(np.median(us)), 3),
+            "p90": round(float(np.percentile(us, 90)), 3), "steps": args.steps}
+
+    lin0, (y0, rho0, sl0, ns0, _) = layers[0]
+    step(0)
+    torch.cuda.synchronize()
+    n_slow = int(ns0[0])
+    d, dout, k = wl.d, wl.d_out, wl.k
+    alg = {
+        "proj": k * d * 2 + m * d * 2 + m * k * 4,
+        "resid": d * k * 2 + m * d * 2 + m * k * 4,
+        "out": (dout * k * 2 if n_slow < m else 0) + (dout * d * 2 + m * d * 2 if n_slow else 0)
+        + m * k * 4 + m * dout * 2,
+    }
+    touched = 2 * k * d * 2 + (dout * k * 2 if n_slow < m else 0) + (dout * d * 2 if n_slow else 0) \
+        + m * d * 2 + m * dout * 2
+    dense_bytes = dout * d * 2 + m * d * 2 + m * dout * 2
+
+    for lin, _ in layers:
+        lin.timing_enable(True, capacity=args.steps + 8)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kernels = {}
+    for kind in ("proj", "resid", "out"):
+        n_tot, ms_tot = 0, 0.0
+        for lin, _ in layers:
+            n, t = lin.timing_read(kind)
+            n_tot += n
+            ms_tot += t
+        if n_tot:
+            kernels[kind] = {"launches": n_tot, "avg_us": 1e3 * ms_tot / n_tot}
+    for lin, _ in layers:
+        lin.timing_enable(False)
+    dom = max(kernels, key=lambda kk: kernels[kk]["avg_us"])
+    achieved = alg[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            tinfo = json.load(fh).get(f"gsi-m{m}", {}).get(dom)
+        if tinfo and tinfo.get("source_sha") == src_hash():
+            traffic = tinfo.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": int(alg[dom]), "avg_us": round(kernels[dom]["avg_us"], 3)}
+
+    cpu = None
+    if not args.no_cpu:
+        from oracle import gsi_oracle as G
+        from threadpoolctl import threadpool_info
+        from synth import round_bf16
+        img = round_bf16(G.image(wl.w, wl.vk))          # the cached image: set-up, not timed
+        t0 = time.time()
+        reps = 0
+        while time.time() - t0 < args.cpu_seconds or reps == 0:
+            G.forward(wl.w, img, wl.vk, wl.x, wl.eps)
+            reps += 1
+        el = time.time() - t0
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        cpu = {"value": round(reps * m / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"{reps} oracle gated forward passes of the {m}-token batch ({el:.1f} s), image precomputed"}
+
+    out = {
+        "metric": "gated-subspace linear tokens/sec + effective HBM GB/s, d=4096 -> 14336, k=256 (1 GPU)",
+        "value": round(m * 1e3 / ms, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOADS['gsi']} m={m}", "d_in": d, "d_out": dout, "k": k, "m": m,
+                   "eps": wl.eps, "slow_tokens": n_slow, "layers_rotated": len(layers)},
+        "effective_hbm_GBps": round(touched / (ms * 1e-3) / 1e9, 1),
+        "touched_bytes": int(touched),
+        "weight_read_reduction": round(dense_bytes / touched, 2),
+        "dense_ms_per_step": round(ms_dense, 5),
+        "dense_effective_hbm_GBps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
+        "speedup_vs_dense": round(ms_dense / ms, 3),
+        "step_us_dist": dist,
+        "kernels_us": {kk: round(v["avg_us"], 3) for kk, v in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),
     }
     print(json.dumps(out))

@@ -13,7 +13,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ffn_sparse.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -25,8 +26,10 @@ def L():
 
 
 def declared_symbols():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(ffn_sparse_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        names |= set(re.findall(r"\b(ffn_(?:sparse|gsi)_[a-z_]+)\s*\(", open(h).read()))
+    return sorted(names)
 
 
 def cfg(L, **kw):
@@ -39,7 +42,8 @@ def cfg(L, **kw):
 def test_exports_every_declared_symbol(L):
     lib = L.load()
     names = declared_symbols()
-    assert len(names) >= 14
+    assert len(names) >= 28
+    assert any(n.startswith("ffn_gsi_") for n in names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
@@ -125,3 +129,53 @@ def test_calls_reject_null_handle(L):
     assert lib.ffn_sparse_device_status(None, None) == -1
     assert lib.ffn_sparse_debug_waits(None, 0, 1, None) == -1
     lib.ffn_sparse_destroy(None)
+
+
+# ---------------------------------------------------------------- GSI linear map
+def gcfg(L, **kw):
+    base = dict(d_in=4096, d_out=14336, k=256, max_m=16)
+    base.update(kw)
+    return L.GsiConfig(**base)
+
+
+@pytest.mark.parametrize("kw,ok", [
+    ({}, True),
+    (dict(d_in=64, d_out=40, k=16), True),
+    (dict(d_in=16384, k=512), True),
+    (dict(d_in=8, k=8, d_out=1), True),
+    (dict(k=12), False),               # k not a multiple of 8
+    (dict(k=520), False),              # k above 512
+    (dict(d_in=60), False),            # d_in not a multiple of 8
+    (dict(d_in=64, k=128), False),     # k > d_in
+    (dict(d_in=16392), False),
+    (dict(d_out=0), False),
+    (dict(max_m=0), False),
+])
+def test_gsi_check_config(L, kw, ok):
+    lib = L.load()
+    c = gcfg(L, **kw)
+    st = lib.ffn_gsi_check_config(ctypes.byref(c))
+    assert (st == 0) == ok
+    nb = lib.ffn_gsi_workspace_bytes(ctypes.byref(c))
+    assert (nb > 0) == ok
+    if ok:
+        # at least the transposed basis and the image, each bf16
+        assert nb >= 2 * c.k * c.d_in + 2 * c.d_out * c.k
+
+
+def test_gsi_bad_arguments_rejected_before_launch(L):
+    lib = L.load()
+    c = gcfg(L)
+    h = ctypes.c_void_p()
+    # null weights / workspace, misaligned workspace: FFN_E_INVALID, no handle
+    assert lib.ffn_gsi_init(ctypes.byref(c), None, None, None, 0, None, ctypes.byref(h)) == -1
+    assert not h.value
+    assert lib.ffn_gsi_init(ctypes.byref(c), 256, 256, 4096 + 16, 1 << 30, None, ctypes.byref(h)) == -1
+    assert lib.ffn_gsi_init(ctypes.byref(c), 256, 256, 4096, 16, None, ctypes.byref(h)) == -3
+    assert lib.ffn_gsi_init(None, 256, 256, 4096, 1 << 30, None, ctypes.byref(h)) == -1
+    assert lib.ffn_gsi_forward(None, None, 1, 0.1, None, None, None, None, None) == -1
+    assert lib.ffn_gsi_dense_forward(None, None, 1, None, None) == -1
+    assert lib.ffn_gsi_image(None) is None
+    n, ms = ctypes.c_int32(), ctypes.c_double()
+    assert lib.ffn_gsi_timing_read(None, 0, ctypes.byref(n), ctypes.byref(ms)) == -1
+    lib.ffn_gsi_destroy(None)
