@@ -26,13 +26,17 @@ Sources (page title, then section):
   section 3.1 (score = |hidden value| times the 2-norm of the weight column
   it multiplies) and section 3.2 (Lemma 3.1: optimal for column-orthogonal
   weights).
+* LoPA page, section "Model Casting and Quality at 90% Sparsity": the gating
+  carries over to mixture-of-experts layers whose experts are FFN blocks.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): y = W_down (a(z) * (W_up x)) with z = W_gate x + b and no
 up/down biases; "ReLU with threshold" passes z through (a = z when
 z > max(tau, 0)); the low-rank intermediate V x is kept unrounded; a cut is
 strict (z == cut is inactive); top-k orders by (score desc, index asc);
-a token is routed dense when any tile holds more than E active entries.
+a token is routed dense when any tile holds more than E active entries; in a
+mixture-of-experts layer each expert is one such FFN and a token's output is
+the routing-weighted sum of its chosen experts' outputs.
 
 Parity status: every function below is pinned by CPU tests (brute-force
 dense evaluation, closed forms, invariants, the hand-computed WINA example
@@ -330,3 +334,29 @@ def dense_forward(wl, bias=None, tau=None) -> np.ndarray:
         a = np.where(threshold_mask(z, np.maximum(t_in, 0.0)), a, 0.0)
     h = a * up_projection(x, wl.w_up)
     return h @ np.asarray(wl.w_down, dtype=np.float64).T
+
+
+# ---------------------------------------------------------------------------
+# mixture of experts
+# ---------------------------------------------------------------------------
+
+def moe_combine(expert_y, rows, slots, weights, m: int, d: int) -> np.ndarray:
+    """y_t = sum over token t's routing slots s of weights[t, s] times the
+    output of the expert of slot s on x_t. expert_y[e] holds expert e's
+    outputs for its tokens rows[e] (routing slots slots[e]). [LoPA page,
+    "Model Casting and Quality at 90% Sparsity": experts are FFN blocks; the
+    weighted sum is the usual combination of a routed layer.]"""
+    y = np.zeros((m, d))
+    w = np.asarray(weights, dtype=np.float64)
+    for ye, r_e, s_e in zip(expert_y, rows, slots):
+        for i, (t, s) in enumerate(zip(r_e, s_e)):
+            y[int(t)] += w[int(t), int(s)] * np.asarray(ye[i], dtype=np.float64)
+    return y
+
+
+def moe_forward(mw) -> dict:
+    """Each expert's sparse forward pass on the tokens routed to it, then the
+    weighted combination. Returns the per-expert results and y [m, d]."""
+    per = [forward(wl) if wl.m else None for wl in mw.experts]
+    ys = [p["y"] if p is not None else np.zeros((0, mw.d)) for p in per]
+    return {"experts": per, "y": moe_combine(ys, mw.rows, mw.slots, mw.weights, mw.m, mw.d)}
