@@ -5,7 +5,7 @@ include/ffn_sparse.h and include/ffn_gsi.h); this package only binds it. Importi
 GPU; calling an entry point needs the built library and a GPU.
 """
 from ._lib import FFNError, load  # noqa: F401
-from .ffn import SparseFFN, TwellPack  # noqa: F401
+from .ffn import SparseFFN, TwellPack, moe_forward  # noqa: F401
 from .gsi import GsiLinear  # noqa: F401
 
-__all__ = ["SparseFFN", "TwellPack", "GsiLinear", "FFNError", "load"]
+__all__ = ["SparseFFN", "TwellPack", "GsiLinear", "moe_forward", "FFNError", "load"]

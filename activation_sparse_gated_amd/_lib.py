@@ -21,7 +21,7 @@ EXPORTS = [
     "ffn_sparse_updown", "ffn_sparse_dense_fallback", "ffn_sparse_forward", "ffn_sparse_dense_forward",
     "ffn_sparse_forward_path", "ffn_sparse_timing_enable", "ffn_sparse_timing_read", "ffn_sparse_destroy",
     "ffn_sparse_device_status", "ffn_sparse_debug_waits", "ffn_sparse_forward_noalloc",
-    "ffn_sparse_noalloc_scratch_bytes",
+    "ffn_sparse_noalloc_scratch_bytes", "ffn_sparse_moe_workspace_bytes", "ffn_sparse_moe_forward",
     "ffn_gsi_check_config", "ffn_gsi_workspace_bytes", "ffn_gsi_init", "ffn_gsi_forward",
     "ffn_gsi_dense_forward", "ffn_gsi_image", "ffn_gsi_timing_enable", "ffn_gsi_timing_read",
     "ffn_gsi_destroy",
@@ -89,6 +89,10 @@ def load() -> ctypes.CDLL:
                                                  c_int32, P(Pack), c_void_p, c_void_p]),
         "ffn_sparse_noalloc_scratch_bytes": (c_size_t, []),
         "ffn_sparse_debug_waits": (c_int32, [c_void_p, ctypes.c_uint32, ctypes.c_uint32, c_void_p]),
+        "ffn_sparse_moe_workspace_bytes": (c_size_t, [P(Config), c_int32, c_int32]),
+        "ffn_sparse_moe_forward": (c_int32, [P(c_void_p), c_int32, c_void_p, c_int32, c_int32, P(c_int32),
+                                             P(c_float), c_void_p, c_float, c_void_p, c_int32, c_int32,
+                                             c_void_p, c_size_t, c_void_p, c_void_p]),
         "ffn_gsi_check_config": (c_int32, [P(GsiConfig)]),
         "ffn_gsi_workspace_bytes": (c_size_t, [P(GsiConfig)]),
         "ffn_gsi_init": (c_int32, [P(GsiConfig), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,

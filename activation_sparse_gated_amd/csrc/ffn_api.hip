@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -1465,6 +1466,102 @@ int32_t ffn_sparse_forward_path(const ffn_sparse_handle* h, int32_t m) {
   if (topk_down_kind(h, m) == 1) return 4;
   if (topk_down_kind(h, m) == 2) return 5;
   return 0;
+}
+
+size_t ffn_sparse_moe_workspace_bytes(const ffn_sparse_config* cfg, int32_t m, int32_t topk) {
+  if (ffn_sparse_check_config(cfg) != FFN_OK || m < 1 || topk < 1 || (size_t)m * topk > (size_t)kMoeMaxPairs)
+    return 0;
+  const size_t np = (size_t)m * topk, rowb = (size_t)cfg->d_model * esize_of(cfg->dtype);
+  return 2 * align_up(np * rowb) + 2 * align_up(np * 4) + ffn_sparse_pack_bytes(cfg, m);
+}
+
+ffn_status ffn_sparse_moe_forward(ffn_sparse_handle* const* experts, int32_t n_experts, const void* x, int32_t m,
+                                  int32_t topk, const int32_t* expert_ids, const float* weights, const float* bias,
+                                  float bias_scalar, const float* tau, int32_t k, int32_t dense, void* workspace,
+                                  size_t workspace_bytes, void* y, void* stream) {
+  if (!experts || n_experts < 1 || m < 0 || topk < 1 || topk > n_experts) return FFN_E_INVALID;
+  for (int e = 0; e < n_experts; ++e) {
+    if (!experts[e]) return FFN_E_INVALID;
+    if (experts[e]->failed) return FFN_E_HIP;
+    ffn_sparse_config a = experts[e]->cfg, b = experts[0]->cfg;
+    a.max_m = b.max_m = 0;
+    if (std::memcmp(&a, &b, sizeof(a)) != 0) return FFN_E_INVALID;    // one shape for every expert
+  }
+  if (m == 0) return FFN_OK;
+  const auto& c = experts[0]->cfg;
+  if ((size_t)m * topk > (size_t)kMoeMaxPairs || !expert_ids || !weights || !x || !y || !aligned16(x) ||
+      !aligned16(y) || !workspace || !aligned16(workspace))
+    return FFN_E_INVALID;
+  if (c.sel == FFN_SEL_THRESH && !tau) return FFN_E_INVALID;
+  if (workspace_bytes < ffn_sparse_moe_workspace_bytes(&c, m, topk)) return FFN_E_WORKSPACE;
+  // routing table (host): experts' rows contiguous, tokens in order
+  const int np = m * topk;
+  std::vector<int> cnt(n_experts, 0), off(n_experts + 1, 0);
+  for (int q = 0; q < np; ++q) {
+    const int e = expert_ids[q];
+    if (e < 0 || e >= n_experts || !std::isfinite(weights[q])) return FFN_E_INVALID;
+    for (int s2 = 0; s2 < q % topk; ++s2)
+      if (expert_ids[q - q % topk + s2] == e) return FFN_E_INVALID;     // one slot per expert and token
+    ++cnt[e];
+  }
+  for (int e = 0; e < n_experts; ++e) {
+    if (cnt[e] > experts[e]->cfg.max_m) return FFN_E_INVALID;
+    off[e + 1] = off[e] + cnt[e];
+  }
+  MoeDesc md{};
+  md.d = c.d_model;
+  md.m = m;
+  md.topk = topk;
+  md.npairs = np;
+  md.dtype = c.dtype == FFN_BF16 ? DT_BF16 : DT_F32;
+  {
+    std::vector<int> fill(off.begin(), off.end() - 1);
+    for (int t = 0; t < m; ++t)
+      for (int s2 = 0; s2 < topk; ++s2) {
+        const int q = t * topk + s2, e = expert_ids[q], r = fill[e]++;
+        md.tab.src[r] = q;
+        md.tab.pos[q] = r;
+        md.tab.w[q] = weights[q];
+      }
+  }
+  const size_t rowb = (size_t)c.d_model * esize_of(c.dtype);
+  char* p = static_cast<char*>(workspace);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    char* q = p + o;
+    o += align_up(bytes);
+    return q;
+  };
+  md.x = x;
+  md.xg = take((size_t)np * rowb);
+  md.yg = take((size_t)np * rowb);
+  md.tg = reinterpret_cast<float*>(take((size_t)np * 4));
+  md.bg = reinterpret_cast<float*>(take((size_t)np * 4));
+  md.tau = tau;
+  md.bias = bias;
+  md.y = y;
+  const size_t nt = c.d_ff / c.tile_w, E = c.ell_w;
+  ffn_twell_pack pk{};
+  pk.cnt = reinterpret_cast<int32_t*>(take((size_t)m * nt * 4));
+  pk.idx = reinterpret_cast<uint16_t*>(take((size_t)m * nt * E * 2));
+  pk.val = take((size_t)m * nt * E * esize_of(c.dtype));
+  pk.route = reinterpret_cast<uint8_t*>(take((size_t)m));
+  pk.dense_list = reinterpret_cast<int32_t*>(take((size_t)m * 4));
+  pk.n_dense = reinterpret_cast<int32_t*>(take(4));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (launch_moe_gather(md, s) != hipSuccess) return FFN_E_HIP;
+  // each expert's sparse forward pass on its rows, in expert order
+  for (int e = 0; e < n_experts; ++e) {
+    if (!cnt[e]) continue;
+    const char* xe = static_cast<const char*>(md.xg) + (size_t)off[e] * rowb;
+    void* ye = static_cast<char*>(const_cast<void*>(md.yg)) + (size_t)off[e] * rowb;
+    const float* be = bias ? md.bg + off[e] : nullptr;
+    const float* te = tau ? md.tg + off[e] : nullptr;
+    const ffn_status st = dense ? ffn_sparse_dense_forward(experts[e], xe, cnt[e], be, bias_scalar, te, ye, stream)
+                                : ffn_sparse_forward(experts[e], xe, cnt[e], be, bias_scalar, te, k, &pk, ye, stream);
+    if (st != FFN_OK) return st;
+  }
+  return hip_status(launch_moe_combine(md, s));
 }
 
 ffn_status ffn_sparse_timing_enable(ffn_sparse_handle* h, int32_t enable, int32_t capacity) {

@@ -292,6 +292,25 @@ int dec_down2_groups(int d_model, int d_ff);
 // width T and m tokens (0 when the decode shape does not apply).
 int dec_rows_per_wg(int K, int T, int m, int* ipw, int want_ipw = 0);
 int dec_gate_rows(int K, int T, int m, bool lowrank, int* ipw, int want_ipw = 0);
+
+// Mixture-of-experts layer: expert-grouped gather of x (and per-slot bias /
+// threshold) and the weighted combination of the experts' outputs.
+constexpr int kMoeMaxPairs = 256;   // (token, slot) pairs of one call
+struct MoeTable {
+  int32_t src[kMoeMaxPairs];        // grouped row r holds pair src[r] = token * topk + slot
+  int32_t pos[kMoeMaxPairs];        // pair q = token * topk + slot sits at grouped row pos[q]
+  float w[kMoeMaxPairs];            // combine weight of pair q
+};
+struct MoeDesc {
+  int d, m, topk, npairs, dtype;
+  const void* x; void* xg;          // [m x d], [npairs x d]
+  const float* tau; const float* bias;   // [m x topk] per pair, or null
+  float* tg; float* bg;             // [npairs] grouped
+  const void* yg; void* y;          // [npairs x d] expert outputs, [m x d]
+  MoeTable tab;
+};
+hipError_t launch_moe_gather(const MoeDesc& d, hipStream_t s);
+hipError_t launch_moe_combine(const MoeDesc& d, hipStream_t s);
 // Slices of d of the matrix-core first stage for m tokens (0: the VALU kernel).
 int dec_lowrank_slabs(int m, int d_model, int rank, int want);
 

@@ -199,3 +199,28 @@ class SparseFFN:
             self.close()
         except Exception:
             pass
+
+
+def moe_forward(experts, x, expert_ids, weights, *, tau=None, bias=None, bias_scalar=0.0, k=0, y=None,
+                workspace=None, dense=False, stream=None) -> torch.Tensor:
+    """Mixture-of-experts layer over SparseFFN experts of one shape
+    (ffn_sparse_moe_forward). expert_ids and weights are host arrays
+    [m, topk] (numpy or lists); tau / bias device tensors [m, topk] or None."""
+    import numpy as np
+    lib = experts[0].lib
+    ids = np.ascontiguousarray(np.asarray(expert_ids, dtype=np.int32))
+    wts = np.ascontiguousarray(np.asarray(weights, dtype=np.float32))
+    m, topk = ids.shape
+    cfg = experts[0].cfg
+    if y is None:
+        y = torch.empty((max(m, 1), cfg.d_model), dtype=experts[0].torch_dtype, device=experts[0].device)
+    nbytes = lib.ffn_sparse_moe_workspace_bytes(ctypes.byref(cfg), max(m, 1), topk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=experts[0].device)
+    hs = (ctypes.c_void_p * len(experts))(*[e.handle.value for e in experts])
+    check(lib.ffn_sparse_moe_forward(hs, len(experts), _ptr(x), m, topk,
+                                     ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     wts.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(bias),
+                                     float(bias_scalar), _ptr(tau), int(k), 1 if dense else 0, workspace.data_ptr(),
+                                     workspace.numel(), _ptr(y), _stream_ptr(stream)), "ffn_sparse_moe_forward")
+    return y

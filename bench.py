@@ -33,6 +33,7 @@ WORKLOADS = {
     "c6": "input-wina-gate-bf16-2048x8192",
     "c7": "lopa-input-wina-bf16-4096x14336-r512",
     "gsi": "gsi-linear-bf16-4096x14336-k256",
+    "moe": "moe-lopa-relu-thresh-bf16-8x4096x14336-r512-top2",
 }
 
 
@@ -88,6 +89,8 @@ def main():
     cid = args.workload
     if cid == "gsi":
         return bench_gsi(args, dev)
+    if cid == "moe":
+        return bench_moe(args, dev)
     m = args.m if args.m is not None else {"c2": 1, "c3": 1, "c4": 1, "c5": 4096, "c6": 1, "c7": 1}[cid]
     t_gen = time.time()
     wl = make_workload(cid, m, 0)
@@ -358,6 +361,169 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
+        "input_gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(out))
+
+
+def bench_moe(args, dev):
+    """A mixture-of-experts layer of 8 LoPA-gated experts of the LoPA shape
+    (d = 4096, d_ff = 14336, rank 512, 90% sparsity), top-2 routing: a step is
+    one layer call over the batch (gather, the chosen experts' sparse forward
+    passes, weighted combination); the baseline runs the same layer with the
+    experts' dense forward passes. Steps rotate over `--layers` copies of the
+    expert set and four routed batches, so the touched weights do not stay in
+    the last-level cache."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_amd as asg
+    from synth.moe import make_moe_config
+
+    m = args.m if args.m is not None else 1
+    nb = 4
+    t_gen = time.time()
+    mw = make_moe_config("moe", m=m * nb, seed=0)
+    t_gen = time.time() - t_gen
+    note(f"inputs moe m={m} x {nb} batches generated in {t_gen:.1f}s")
+    e0 = mw.experts[0]
+
+    def dev_bf16(a):
+        return torch.from_numpy(e0.storage(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = [{k: dev_bf16(getattr(wl, k)) for k in ("u", "v", "w_up", "w_down")} for wl in mw.experts]
+    n_sets = max(1, min(args.layers, 3))
+    sets = []
+    for li in range(n_sets):
+        ffns = []
+        for e, wl in enumerate(mw.experts):
+            w = {k: (v if li == 0 else v.clone()) for k, v in base[e].items()}
+            ffns.append(asg.SparseFFN(d_model=wl.d, d_ff=wl.f, rank=wl.rank, dtype="bf16", act=wl.act, sel=wl.sel,
+                                      tile_w=wl.T, ell_w=wl.E, max_m=m, u=w["u"], v=w["v"], w_up=w["w_up"],
+                                      w_down=w["w_down"], wdown_out_major=True))
+        sets.append(ffns)
+    x_all = dev_bf16(mw.x)
+    tau_all = torch.from_numpy(mw.tau.astype(np.float32)).to(dev)
+    batches = [(x_all[b * m:(b + 1) * m], mw.expert_ids[b * m:(b + 1) * m].copy(),
+                mw.weights[b * m:(b + 1) * m].copy(), tau_all[b * m:(b + 1) * m].contiguous()) for b in range(nb)]
+    lib = asg.load()
+    import ctypes
+    wsb = lib.ffn_sparse_moe_workspace_bytes(ctypes.byref(sets[0][0].cfg), m, mw.topk)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    y = torch.empty((m, mw.d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    combos = [(li, b) for li in range(n_sets) for b in range(nb)]
+
+    def step(i, dense=False):
+        li, b = combos[i % len(combos)]
+        xb, ids, wts, tb = batches[b]
+        asg.moe_forward(sets[li], xb, ids, wts, tau=tb, y=y, workspace=ws, dense=dense)
+
+    def timed(fn, n, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(warm + i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms = timed(step, args.steps, args.warmup)
+    note(f"moe step {ms * 1e3:.2f} us")
+    ms_dense = timed(lambda i: step(i, dense=True), max(20, args.steps // 4), 5)
+    note(f"dense moe step {ms_dense * 1e3:.2f} us")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    dist = {"p10": round(float(np.percentile(us, 10)), 3), "p50": round(float(np.median(us)), 3),
+            "p90": round(float(np.percentile(us, 90)), 3), "steps": args.steps}
+
+    # per-kernel durations of the experts' kernels (HIP events on the stream)
+    for ffns in sets:
+        for f in ffns:
+            f.timing_enable(True, capacity=2 * args.steps + 8)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kernels = {}
+    for kind in ("lowrank_v", "gate", "up", "updown", "reduce", "fallback"):
+        n_tot, ms_tot = 0, 0.0
+        for ffns in sets:
+            for f in ffns:
+                n, t = f.timing_read(kind)
+                n_tot += n
+                ms_tot += t
+        if n_tot:
+            kernels[kind] = {"launches": n_tot, "avg_us": 1e3 * ms_tot / n_tot}
+    for ffns in sets:
+        for f in ffns:
+            f.timing_enable(False)
+    d, F, r, T, E = e0.d, e0.f, e0.rank, e0.T, e0.E
+    k_act = e0.k
+    pairs = m * mw.topk
+    # touched bytes per step: each active expert's gate (U, V) once, its tokens'
+    # active up and down rows (union per expert), x gathered, y combined
+    ids0 = batches[0][1]
+    active_experts = len(set(ids0.ravel().tolist()))
+    touched = active_experts * (F * r + r * d) * 2 + pairs * k_act * 2 * d * 2 + 3 * pairs * d * 2 + m * d * 2
+    dense_bytes = active_experts * ((F * r + r * d) * 2 + 2 * F * d * 2) + 3 * pairs * d * 2 + m * d * 2
+    roofline = None
+    if m == 1 and "gate" in kernels:
+        ntiles = F // T
+        pack_bytes = ntiles * (4 + E * 4)
+        alg = F * r * 2 + r * 4 + pack_bytes + 9 + 2 * k_act * d * 2      # partial-row gate kernel of one expert
+        achieved = alg / (kernels["gate"]["avg_us"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "gate", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "alg_bytes_per_launch": int(alg), "avg_us": round(kernels["gate"]["avg_us"], 3)}
+    cpu = None
+    if not args.no_cpu:
+        from oracle import ffn_oracle as O
+        from threadpoolctl import threadpool_info
+        t0 = time.time()
+        reps = 0
+        while time.time() - t0 < args.cpu_seconds or reps == 0:
+            O.moe_forward(mw)
+            reps += 1
+        el = time.time() - t0
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        cpu = {"value": round(reps * mw.m / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"{reps} oracle passes of the layer over {mw.m} tokens ({el:.1f} s)"}
+    out = {
+        "metric": "MoE layer (8 LoPA-gated experts, top-2) tokens/sec + effective HBM GB/s, d=4096 (1 GPU)",
+        "value": round(m * 1e3 / ms, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOADS['moe']} m={m}", "experts": mw.n_experts, "topk": mw.topk,
+                   "d_model": d, "d_ff": F, "rank": r, "m": m, "active_experts_batch0": active_experts,
+                   "expert_sets_rotated": n_sets, "batches_rotated": nb},
+        # one token: exact; several: rows shared by an expert's tokens are
+        # counted once per token (an upper bound)
+        "effective_hbm_GBps": round(touched / (ms * 1e-3) / 1e9, 1) if m == 1 else None,
+        "touched_bytes": int(touched) if m == 1 else None,
+        "touched_bytes_upper": int(touched),
+        "dense_ms_per_step": round(ms_dense, 5),
+        "dense_effective_hbm_GBps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
+        "speedup_vs_dense": round(ms_dense / ms, 3),
+        "step_us_dist": dist,
+        "kernels_us": {kk: round(v["avg_us"], 3) for kk, v in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),
     }
     print(json.dumps(out))

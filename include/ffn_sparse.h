@@ -199,6 +199,38 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t
                                     const float *bias, float bias_scalar, const float *tau,
                                     void *y, void *stream);
 
+/* Bytes of the caller workspace ffn_sparse_moe_forward needs for m tokens
+ * routed to topk experts each (0 if invalid; m * topk <= 256). */
+size_t ffn_sparse_moe_workspace_bytes(const ffn_sparse_config *cfg, int32_t m, int32_t topk);
+
+/* Mixture-of-experts layer whose experts are sparse FFNs of one shape:
+ * y_t = sum over t's routing slots s of weights[t, s] * FFN_{e(t, s)}(x_t).
+ * Source: LoPA page, "Model Casting and Quality at 90% Sparsity" (the gating
+ * carries over to mixture-of-experts layers whose experts are FFN blocks);
+ * the weighted sum is the usual combination of a routed layer.
+ *   experts     n_experts handles (host array), all of one config except max_m
+ *   x           [m x d_model] device
+ *   expert_ids  HOST [m x topk]: the experts of each token, distinct per token
+ *               (the router has already run)
+ *   weights     HOST [m x topk] combine weights (finite)
+ *   bias, tau   NULL or DEVICE [m x topk]: the selection inputs of each
+ *               (token, slot) pair (tau required for THRESH), as for forward
+ *   k           kept neurons per (token, expert) for TOPK configs
+ *   dense       0: the experts' sparse forward passes; 1: their dense forward
+ *               passes (ffn_sparse_dense_forward, the comparison baseline)
+ *   workspace   DEVICE, 16-byte aligned, >= ffn_sparse_moe_workspace_bytes
+ *   y           [m x d_model] device, written in full
+ * One gather kernel builds the experts' contiguous token blocks, each expert
+ * with tokens runs its forward sequence on its block (expert
+ * order; each expert's max_m must cover its token count), one kernel adds the
+ * weighted outputs per token in slot order (fp32) and rounds once.
+ * 1 <= topk <= n_experts; 0 <= m with m * topk <= 256. */
+ffn_status ffn_sparse_moe_forward(ffn_sparse_handle *const *experts, int32_t n_experts, const void *x,
+                                  int32_t m, int32_t topk, const int32_t *expert_ids, const float *weights,
+                                  const float *bias, float bias_scalar, const float *tau, int32_t k,
+                                  int32_t dense, void *workspace, size_t workspace_bytes, void *y,
+                                  void *stream);
+
 /* Which kernel sequence ffn_sparse_forward runs for m tokens (host-only
  * query, no GPU work). The decode sequences (bf16, bias / threshold
  * selection, 1 <= m <= 16; modes 1 and 2 up to 8 tokens) run the low-rank

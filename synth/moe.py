@@ -6,7 +6,8 @@ are assumptions: Mixtral-like, 8 experts of the LoPA workload's shape
 (d = 4096, d_ff = 14336, rank 512, ReLU with a per-token threshold at 90%
 sparsity), each token routed to 2 of them.
 
-* expert e's weights: the LoPA workload's recipe with seed (seed * 64 + e);
+* expert e's weights: the LoPA workload's recipe with seed (s * 64 + e), s the
+  expert seed (the token seed unless given);
 * routing: per token, `topk` distinct experts uniformly at random (listed in
   ascending order), combine weights = softmax of N(0, 1) logits over the
   chosen experts, rounded to fp32;
@@ -64,10 +65,11 @@ class MoeWorkload:
 
 def make_moe(m: int, *, n_experts: int = 8, topk: int = 2, seed: int = 0, base: str = "c3",
              d: int | None = None, f: int | None = None, rank: int | None = None, T: int | None = None,
-             E: int | None = None, name: str = "moe") -> MoeWorkload:
+             E: int | None = None, name: str = "moe", expert_seed: int | None = None) -> MoeWorkload:
     if not (1 <= topk <= n_experts):
         raise ValueError("need 1 <= topk <= n_experts")
-    bases = [make_workload(base, 1, seed * 64 + e, d=d, f=f, rank=rank, T=T, E=E) for e in range(n_experts)]
+    es = seed if expert_seed is None else expert_seed
+    bases = [make_workload(base, 1, es * 64 + e, d=d, f=f, rank=rank, T=T, E=E) for e in range(n_experts)]
     b0 = bases[0]
     dd, ff = b0.d, b0.f
     k = ff - int(round(_SPARSITY_THRESH * ff))

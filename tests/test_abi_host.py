@@ -179,3 +179,17 @@ def test_gsi_bad_arguments_rejected_before_launch(L):
     n, ms = ctypes.c_int32(), ctypes.c_double()
     assert lib.ffn_gsi_timing_read(None, 0, ctypes.byref(n), ctypes.byref(ms)) == -1
     lib.ffn_gsi_destroy(None)
+
+
+def test_moe_host_checks(L):
+    lib = L.load()
+    c = cfg(L, rank=512, d_model=4096, d_ff=14336, sel=1, max_m=8)
+    assert lib.ffn_sparse_moe_workspace_bytes(ctypes.byref(c), 8, 2) > 0
+    assert lib.ffn_sparse_moe_workspace_bytes(ctypes.byref(c), 200, 2) == 0     # above 256 pairs
+    assert lib.ffn_sparse_moe_workspace_bytes(ctypes.byref(c), 0, 2) == 0
+    ids = (ctypes.c_int32 * 2)(0, 1)
+    w = (ctypes.c_float * 2)(0.5, 0.5)
+    assert lib.ffn_sparse_moe_forward(None, 2, None, 1, 2, ids, w, None, 0.0, None, 0, 0, None, 0, None, None) == -1
+    hs = (ctypes.c_void_p * 2)(None, None)
+    assert lib.ffn_sparse_moe_forward(hs, 2, None, 1, 2, ids, w, None, 0.0, None, 0, 0, None, 0, None, None) == -1
+    assert lib.ffn_sparse_moe_forward(hs, 2, None, 1, 3, ids, w, None, 0.0, None, 0, 0, None, 0, None, None) == -1
