@@ -28,6 +28,10 @@ Sources (page title, then section):
   weights).
 * LoPA page, section "Model Casting and Quality at 90% Sparsity": the gating
   carries over to mixture-of-experts layers whose experts are FFN blocks.
+* Sparser/Faster/Lighter page, section "Hybrid 應對非均勻稀疏": in training
+  the same hybrid (compact format for most tokens, dense backup for busy
+  ones) cuts dense work and stored activations; the backward pass here is
+  the gradient of the forward pass with its selection held fixed.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): y = W_down (a(z) * (W_up x)) with z = W_gate x + b and no
@@ -334,6 +338,46 @@ def dense_forward(wl, bias=None, tau=None) -> np.ndarray:
         a = np.where(threshold_mask(z, np.maximum(t_in, 0.0)), a, 0.0)
     h = a * up_projection(x, wl.w_up)
     return h @ np.asarray(wl.w_down, dtype=np.float64).T
+
+
+# ---------------------------------------------------------------------------
+# backward pass (training)
+# ---------------------------------------------------------------------------
+
+def backward(wl, dy, fwd: dict | None = None) -> dict:
+    """Gradients of L = sum_t <dy_t, y_t> through the sparse forward pass with
+    its selection held fixed (full-rank ReLU gate, bias or threshold rule).
+
+    With a = z on the active entries (0 elsewhere), u = W_up x, h = a * u and
+    y = W_down h: dh = W_down^T dy; du = dh * a; dz = dh * u on the active
+    entries; dW_down = dy h^T; dW_up = du x^T; dW_gate = dz x^T;
+    dx = W_up^T du + W_gate^T dz. Only the active neurons' rows and columns
+    are non-zero. [Sparser/Faster/Lighter page, "Hybrid 應對非均勻稀疏":
+    training with the hybrid format; the chain rule through the gated FFN
+    order of the LoPA page, "How LoPA Gating Restructures FFN Computation".]
+    Returns dx [m, d], dw_gate [f, d], dw_up [f, d], dw_down [d, f]
+    (output-major, as W_down) and the per-token du, dz, h [m, f].
+    """
+    if wl.sel == SEL_TOPK or wl.w_gate is None:
+        raise ValueError("the backward pass is defined here for a full-rank ReLU gate with a bias or threshold")
+    fwd = forward(wl) if fwd is None else fwd
+    x = np.asarray(wl.x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    w_down = np.asarray(wl.w_down, dtype=np.float64)
+    mask = fwd["mask"]
+    a = np.where(mask, fwd["z"], 0.0)
+    u = up_projection(x, wl.w_up)
+    h = a * u
+    dh = dy @ w_down                                 # row t: W_down^T dy_t
+    du = dh * a
+    dz = np.where(mask, dh * u, 0.0)
+    return {
+        "dx": du @ np.asarray(wl.w_up, dtype=np.float64) + dz @ np.asarray(wl.w_gate, dtype=np.float64),
+        "dw_gate": dz.T @ x,
+        "dw_up": du.T @ x,
+        "dw_down": dy.T @ h,
+        "du": du, "dz": dz, "h": h, "mask": mask,
+    }
 
 
 # ---------------------------------------------------------------------------

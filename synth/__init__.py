@@ -12,4 +12,5 @@ from .workloads import (  # noqa: F401
     round_bf16,
     round_f32,
     bf16_bits,
+    draw_dy,
 )

@@ -429,3 +429,10 @@ def make_workload(cid: str, m: int | None = None, seed: int = 0, *, d: int | Non
                     bias=bias if cid != "c1" else None, bias_scalar=bias_scalar,
                     tau=tau, delta=delta, attempts=attempts, info=dict(info, certified=certify),
                     in_keep=int(in_keep))
+
+
+def draw_dy(wl: Workload, seed: int = 0) -> np.ndarray:
+    """Seeded output gradient dy [m, d] ~ N(0, 1) in the workload's storage type
+    (the input of a backward pass)."""
+    rnd = round_f32 if wl.dtype == "f32" else round_bf16
+    return rnd(_rng(CONFIGS[wl.cid]["num"], wl.seed, 90, seed).standard_normal((wl.m, wl.d)))
