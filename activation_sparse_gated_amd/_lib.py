@@ -13,7 +13,7 @@ DTYPES = {"f32": 0, "bf16": 1}
 ACTS = {"relu": 0, "silu": 1}
 SELS = {"bias": 0, "thresh": 1, "topk": 2}
 KERNEL_KINDS = {"gate": 0, "lowrank_v": 1, "topk": 2, "updown": 3, "reduce": 4, "fallback": 5, "dense": 6,
-                "route": 7, "up": 8}
+                "route": 7, "up": 8, "bw_gate": 9, "bw_neuron": 10, "bw_dx": 11}
 
 EXPORTS = [
     "ffn_sparse_abi_version", "ffn_sparse_status_string", "ffn_sparse_check_config",
@@ -22,6 +22,7 @@ EXPORTS = [
     "ffn_sparse_forward_path", "ffn_sparse_timing_enable", "ffn_sparse_timing_read", "ffn_sparse_destroy",
     "ffn_sparse_device_status", "ffn_sparse_debug_waits", "ffn_sparse_forward_noalloc",
     "ffn_sparse_noalloc_scratch_bytes", "ffn_sparse_moe_workspace_bytes", "ffn_sparse_moe_forward",
+    "ffn_sparse_backward_workspace_bytes", "ffn_sparse_backward",
     "ffn_gsi_check_config", "ffn_gsi_workspace_bytes", "ffn_gsi_init", "ffn_gsi_forward",
     "ffn_gsi_dense_forward", "ffn_gsi_image", "ffn_gsi_timing_enable", "ffn_gsi_timing_read",
     "ffn_gsi_destroy",
@@ -90,6 +91,10 @@ def load() -> ctypes.CDLL:
         "ffn_sparse_noalloc_scratch_bytes": (c_size_t, []),
         "ffn_sparse_debug_waits": (c_int32, [c_void_p, ctypes.c_uint32, ctypes.c_uint32, c_void_p]),
         "ffn_sparse_moe_workspace_bytes": (c_size_t, [P(Config), c_int32, c_int32]),
+        "ffn_sparse_backward_workspace_bytes": (c_size_t, [P(Config), c_int32]),
+        "ffn_sparse_backward": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_float, c_void_p, P(Pack),
+                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                          c_void_p]),
         "ffn_sparse_moe_forward": (c_int32, [P(c_void_p), c_int32, c_void_p, c_int32, c_int32, P(c_int32),
                                              P(c_float), c_void_p, c_float, c_void_p, c_int32, c_int32,
                                              c_void_p, c_size_t, c_void_p, c_void_p]),

@@ -1468,6 +1468,146 @@ int32_t ffn_sparse_forward_path(const ffn_sparse_handle* h, int32_t m) {
   return 0;
 }
 
+// ------------------------------------------------------------------ backward pass
+namespace {
+// (the per-token input-gradient kernel lists a token's pack slots, or a routed
+// token's neurons, in 8192 LDS entries)
+bool bw_supported(const ffn_sparse_config& c) {
+  const long long slots = (long long)(c.d_ff / c.tile_w) * c.ell_w;
+  return c.rank == 0 && c.act == FFN_RELU && c.sel != FFN_SEL_TOPK_WINA && c.in_keep == 0 && c.d_model <= 4096 &&
+         c.tile_w <= 1024 && slots <= 8192 && (c.ell_w >= c.tile_w || c.d_ff <= 8192);
+}
+struct BwLayout {
+  size_t slot, zr, blk, colptr, ent_tok, ent_pos, du, dz, total;
+  long long pbase, pcap;
+  int nblk;
+};
+BwLayout bw_layout(const ffn_sparse_config& c, int m) {
+  BwLayout L{};
+  const long long ntiles = c.d_ff / c.tile_w;
+  const bool routing = c.ell_w < c.tile_w;
+  L.pbase = (long long)m * ntiles * c.ell_w;
+  L.pcap = L.pbase + (routing ? (long long)m * c.d_ff : 0);
+  L.nblk = (m + kBwBlock - 1) / kBwBlock;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  L.slot = take((size_t)m * 4);
+  L.zr = take(routing ? (size_t)m * c.d_ff * 4 : 4);
+  L.blk = take((size_t)L.nblk * c.d_ff * 4);
+  L.colptr = take((size_t)(c.d_ff + 1) * 4);
+  L.ent_tok = take((size_t)L.pcap * 4);
+  L.ent_pos = take((size_t)L.pcap * 4);
+  L.du = take((size_t)L.pcap * 4);
+  L.dz = take((size_t)L.pcap * 4);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+size_t ffn_sparse_backward_workspace_bytes(const ffn_sparse_config* cfg, int32_t m) {
+  if (ffn_sparse_check_config(cfg) != FFN_OK || !bw_supported(*cfg) || m < 1 || m > cfg->max_m) return 0;
+  const BwLayout L = bw_layout(*cfg, m);
+  if (L.pcap >= (1LL << 31)) return 0;
+  return L.total;
+}
+
+ffn_status ffn_sparse_backward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias, float bias_scalar,
+                               const float* tau, const ffn_twell_pack* pack, const void* dy, void* dx,
+                               float* dw_gate, float* dw_up, float* dw_down_nm, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return guarded(h, [&]() -> ffn_status {
+    ffn_status st = check_call(h, x, m, tau, 0);
+    if (st != FFN_OK) return st;
+    const auto& c = h->cfg;
+    if (!bw_supported(c)) return FFN_E_UNSUPPORTED;
+    if (m == 0) return FFN_OK;
+    if (!pack_ok(pack) || !dy || !aligned16(dy) || (dx && !aligned16(dx)) || (dw_gate && !aligned16(dw_gate)) ||
+        (dw_up && !aligned16(dw_up)) || (dw_down_nm && !aligned16(dw_down_nm)) || !workspace ||
+        !aligned16(workspace))
+      return FFN_E_INVALID;
+    if (workspace_bytes < ffn_sparse_backward_workspace_bytes(&c, m)) return FFN_E_WORKSPACE;
+    const BwLayout L = bw_layout(c, m);
+    char* w = static_cast<char*>(workspace);
+    BwDesc d{};
+    d.m = m;
+    d.d = c.d_model;
+    d.F = c.d_ff;
+    d.T = c.tile_w;
+    d.E = c.ell_w;
+    d.ntiles = c.d_ff / c.tile_w;
+    d.dtype = c.dtype == FFN_BF16 ? DT_BF16 : DT_F32;
+    d.sel = c.sel;
+    d.nblk = L.nblk;
+    d.routing = c.ell_w < c.tile_w;
+    d.x = x;
+    d.dy = dy;
+    d.dx = dx;
+    d.w_gate = h->w_gate;
+    d.w_up = h->w_up;
+    d.w_down_nm = h->w_down_nm;
+    d.bias = bias;
+    d.bias_scalar = bias_scalar;
+    d.tau = tau;
+    d.cnt = pack->cnt;
+    d.idx = pack->idx;
+    d.val = pack->val;
+    d.route = pack->route;
+    d.dense_list = pack->dense_list;
+    d.n_dense = pack->n_dense;
+    d.slot_of = reinterpret_cast<int32_t*>(w + L.slot);
+    d.zr = reinterpret_cast<float*>(w + L.zr);
+    d.blk = reinterpret_cast<int32_t*>(w + L.blk);
+    d.colptr = reinterpret_cast<int32_t*>(w + L.colptr);
+    d.ent_tok = reinterpret_cast<int32_t*>(w + L.ent_tok);
+    d.ent_pos = reinterpret_cast<int32_t*>(w + L.ent_pos);
+    d.du = reinterpret_cast<float*>(w + L.du);
+    d.dz = reinterpret_cast<float*>(w + L.dz);
+    d.pbase = L.pbase;
+    d.dw_gate = dw_gate;
+    d.dw_up = dw_up;
+    d.dw_down = dw_down_nm;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = launch_bw_slots(d, s);
+    if (e == hipSuccess && d.routing) {
+      // the routed tokens' gate rows, densely (dense-list slot order)
+      GemmDesc g = gemm_base(h);
+      g.A0 = h->w_gate;
+      g.nrows = c.d_ff;
+      g.lda = c.d_model;
+      g.K = c.d_model;
+      g.B = x;
+      g.ldb = c.d_model;
+      g.M = m;
+      g.gather = pack->dense_list;
+      g.m_dev = pack->n_dense;
+      EpiDesc ep = epi_base(h, nullptr, 0.f, nullptr);
+      ep.kind = EPI_STORE_F32;
+      ep.out = reinterpret_cast<float*>(w + L.zr);
+      ep.ldo = c.d_ff;
+      ep.out_slab = 0;
+      if (!plan_plain(g, h) || g.ks != 1) return FFN_E_UNSUPPORTED;
+      Timed tm(h, FFN_K_BW_GATE, s);
+      e = launch_gemm(g, ep, s);
+    }
+    if (e == hipSuccess) e = launch_bw_count(d, s);
+    if (e == hipSuccess) e = launch_bw_scan(d, s);
+    if (e == hipSuccess) e = launch_bw_fill(d, s);
+    if (e == hipSuccess) {
+      Timed tm(h, FFN_K_BW_NEURON, s);
+      e = launch_bw_neuron(d, s);
+    }
+    if (e == hipSuccess && dx) {
+      Timed tm(h, FFN_K_BW_DX, s);
+      e = launch_bw_dx(d, s);
+    }
+    return hip_status(e);
+  });
+}
+
 size_t ffn_sparse_moe_workspace_bytes(const ffn_sparse_config* cfg, int32_t m, int32_t topk) {
   if (ffn_sparse_check_config(cfg) != FFN_OK || m < 1 || topk < 1 || (size_t)m * topk > (size_t)kMoeMaxPairs)
     return 0;

@@ -309,6 +309,33 @@ struct MoeDesc {
   const void* yg; void* y;          // [npairs x d] expert outputs, [m x d]
   MoeTable tab;
 };
+// Backward pass of the sparse FFN (full ReLU gate, selection held fixed).
+// Pair positions: a non-routed token's pack slot (t, tile j, slot s) sits at
+// (t * ntiles + j) * E + s; a routed token (dense-list slot r) and neuron i at
+// pbase + r * F + i (pbase = m * ntiles * E).
+constexpr int kBwBlock = 64;        // tokens per block of the neuron-major index build
+struct BwDesc {
+  int m, d, F, T, E, ntiles, dtype, sel, nblk, routing;
+  const void* x; const void* dy; void* dx;
+  const void* w_gate; const void* w_up; const void* w_down_nm;
+  const float* bias; float bias_scalar; const float* tau;
+  const int32_t* cnt; const uint16_t* idx; const void* val; const uint8_t* route;
+  const int32_t* dense_list; const int32_t* n_dense;
+  int32_t* slot_of;                 // [m] dense-list slot of a routed token, -1 otherwise
+  const float* zr;                  // [m x F] gate g of the routed tokens (slot order), before bias
+  int32_t* blk;                     // [nblk x F] pairs per (token block, neuron), then their offsets
+  int32_t* colptr;                  // [F + 1] neuron-major start of each neuron's pairs
+  int32_t* ent_tok; int32_t* ent_pos;   // neuron-major pairs: token, pair position
+  float* du; float* dz;             // per pair position
+  long long pbase;
+  float* dw_gate; float* dw_up; float* dw_down;   // [F x d] fp32, accumulated
+};
+hipError_t launch_bw_slots(const BwDesc& d, hipStream_t s);
+hipError_t launch_bw_count(const BwDesc& d, hipStream_t s);
+hipError_t launch_bw_scan(const BwDesc& d, hipStream_t s);
+hipError_t launch_bw_fill(const BwDesc& d, hipStream_t s);
+hipError_t launch_bw_neuron(const BwDesc& d, hipStream_t s);
+hipError_t launch_bw_dx(const BwDesc& d, hipStream_t s);
 hipError_t launch_moe_gather(const MoeDesc& d, hipStream_t s);
 hipError_t launch_moe_combine(const MoeDesc& d, hipStream_t s);
 // Slices of d of the matrix-core first stage for m tokens (0: the VALU kernel).

@@ -116,6 +116,24 @@ class SparseFFN:
                                                  _stream_ptr(stream)), "ffn_sparse_dense_fallback")
         return y
 
+    def backward(self, x, dy, pack: TwellPack, m=None, *, bias=None, bias_scalar=0.0, tau=None, dx=None,
+                 dw_gate=None, dw_up=None, dw_down_nm=None, workspace=None, stream=None):
+        """Gradients of <dy, y> through the forward pass that wrote `pack`
+        (ffn_sparse_backward). dx is written (allocated here unless given);
+        the fp32 weight-gradient buffers [d_ff, d_model] are added to when given."""
+        m = x.shape[0] if m is None else m
+        if dx is None:
+            dx = torch.empty((max(m, 1), self.cfg.d_model), dtype=self.torch_dtype, device=self.device)
+        if workspace is None:
+            nb = self.lib.ffn_sparse_backward_workspace_bytes(ctypes.byref(self.cfg), max(m, 1))
+            workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        ps = pack.c_struct()
+        check(self.lib.ffn_sparse_backward(self.handle, _ptr(x), m, _ptr(bias), float(bias_scalar), _ptr(tau),
+                                           ctypes.byref(ps), _ptr(dy), _ptr(dx), _ptr(dw_gate), _ptr(dw_up),
+                                           _ptr(dw_down_nm), workspace.data_ptr(), workspace.numel(),
+                                           _stream_ptr(stream)), "ffn_sparse_backward")
+        return dx
+
     def forward(self, x, m=None, *, bias=None, bias_scalar=0.0, tau=None, k=0, pack=None, y=None,
                 stream=None):
         m = x.shape[0] if m is None else m

@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (full-gate workloads: c2, c5) after one forward pass")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="profiling mode: run this many sparse steps and one 256 MiB device copy "
                          "(counter calibration), print nothing else")
@@ -91,6 +93,8 @@ def main():
         return bench_gsi(args, dev)
     if cid == "moe":
         return bench_moe(args, dev)
+    if args.backward:
+        return bench_backward(args, dev)
     m = args.m if args.m is not None else {"c2": 1, "c3": 1, "c4": 1, "c5": 4096, "c6": 1, "c7": 1}[cid]
     t_gen = time.time()
     wl = make_workload(cid, m, 0)
@@ -361,6 +365,147 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
+        "input_gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(out))
+
+
+def bench_backward(args, dev):
+    """Backward pass of one FFN layer (Sparser/Faster/Lighter page, "Hybrid
+    應對非均勻稀疏": training with the compact format and a dense backup):
+    a step is one ffn_sparse_backward call (dx and the three fp32 weight
+    gradients) for the batch, after one forward pass wrote the pack; steps
+    rotate over `--layers` copies of the weights."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_amd as asg
+    from synth import draw_dy, make_workload
+
+    cid = args.workload
+    if cid not in ("c2", "c5"):
+        raise SystemExit("--backward: full-gate workloads c2 and c5 only")
+    m = args.m if args.m is not None else {"c2": 16, "c5": 4096}[cid]
+    t_gen = time.time()
+    wl = make_workload(cid, m, 0)
+    dyh = draw_dy(wl, 1)
+    t_gen = time.time() - t_gen
+    note(f"inputs {cid} m={m} generated in {t_gen:.1f}s")
+
+    def dev_bf16(a):
+        return torch.from_numpy(wl.storage(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = {k: dev_bf16(getattr(wl, k)) for k in ("w_gate", "w_up", "w_down")}
+    x, dy = dev_bf16(wl.x), dev_bf16(dyh)
+    bias = torch.from_numpy(wl.bias.astype(np.float32)).to(dev)
+    nl = max(1, min(args.layers, 4))
+    layers = []
+    for li in range(nl):
+        w = {k: (v if li == 0 else v.clone()) for k, v in base.items()}
+        ffn = asg.SparseFFN(d_model=wl.d, d_ff=wl.f, rank=0, dtype="bf16", act=wl.act, sel=wl.sel, tile_w=wl.T,
+                            ell_w=wl.E, max_m=m, w_gate=w["w_gate"], w_up=w["w_up"], w_down=w["w_down"],
+                            wdown_out_major=True)
+        pack = ffn.new_pack(m)
+        ffn.forward(x, pack=pack, bias=bias)
+        grads = [torch.zeros((wl.f, wl.d), dtype=torch.float32, device=dev) for _ in range(3)]
+        layers.append((ffn, pack, grads))
+    import ctypes
+    lib = asg.load()
+    wsb = lib.ffn_sparse_backward_workspace_bytes(ctypes.byref(layers[0][0].cfg), m)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    dx = torch.empty((m, wl.d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        ffn, pack, (gg, gu, gd) = layers[i % nl]
+        ffn.backward(x, dy, pack, bias=bias, dx=dx, dw_gate=gg, dw_up=gu, dw_down_nm=gd, workspace=ws)
+
+    steps = max(5, min(args.steps, 40 if m > 256 else args.steps))
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    note(f"backward step {ms * 1e3:.2f} us")
+    e0.record()
+    for i in range(steps):
+        ffn, pack, _ = layers[i % nl]
+        ffn.forward(x, pack=pack, bias=bias)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_fwd = e0.elapsed_time(e1) / steps
+
+    for ffn, *_ in layers:
+        ffn.timing_enable(True, capacity=steps + 8)
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    kernels = {}
+    for kind in ("bw_gate", "bw_neuron", "bw_dx"):
+        n_tot, ms_tot = 0, 0.0
+        for ffn, *_ in layers:
+            n, t = ffn.timing_read(kind)
+            n_tot += n
+            ms_tot += t
+        if n_tot:
+            kernels[kind] = {"launches": n_tot, "avg_us": 1e3 * ms_tot / n_tot}
+    for ffn, *_ in layers:
+        ffn.timing_enable(False)
+    fwd = None
+    from oracle import ffn_oracle as O
+    fwd = O.forward(wl)
+    mask = fwd["mask"]
+    pairs = int(mask.sum())
+    n_act = int(mask.any(axis=0).sum())
+    d, F = wl.d, wl.f
+    # HBM bytes the neuron kernel cannot avoid: each active neuron's W_up and
+    # W_down rows, its three fp32 gradient rows read and written, x and dy once,
+    # and du, dz of every pair
+    alg = {"bw_neuron": n_act * (2 * d * 2 + 3 * d * 8) + 2 * m * d * 2 + pairs * 8,
+           "bw_dx": n_act * 2 * d * 2 + pairs * 8 + m * d * 2,
+           "bw_gate": F * d * 2 + int(fwd["n_dense"]) * (d * 2 + F * 4)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    achieved = alg[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "alg_bytes_per_launch": int(alg[dom]),
+                "avg_us": round(kernels[dom]["avg_us"], 3)}
+    cpu = None
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_info
+        t0 = time.time()
+        reps = 0
+        while time.time() - t0 < args.cpu_seconds or reps == 0:
+            O.backward(wl, dyh, fwd)
+            reps += 1
+        el = time.time() - t0
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        cpu = {"value": round(reps * m / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"{reps} oracle backward passes of the {m}-token batch ({el:.1f} s)"}
+    out = {
+        "metric": "sparse-FFN backward tokens/sec (dx + fp32 weight gradients), one layer (1 GPU)",
+        "value": round(m * 1e3 / ms, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 3,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOADS[cid]} m={m} backward", "d_model": d, "d_ff": F, "m": m,
+                   "active_pairs": pairs, "active_neurons": n_act, "routed_tokens": int(fwd["n_dense"]),
+                   "layers_rotated": nl},
+        "forward_ms_per_step": round(ms_fwd, 5),
+        "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),
     }
     print(json.dumps(out))

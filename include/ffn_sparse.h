@@ -199,6 +199,40 @@ ffn_status ffn_sparse_dense_forward(ffn_sparse_handle *h, const void *x, int32_t
                                     const float *bias, float bias_scalar, const float *tau,
                                     void *y, void *stream);
 
+/* Bytes of the caller workspace ffn_sparse_backward needs for m tokens (0 if
+ * the config has no backward pass here: it is defined for a full-rank ReLU
+ * gate with bias or threshold selection, d_model <= 4096, in_keep = 0,
+ * (d_ff / tile_w) * ell_w <= 8192 and, when tokens can be routed
+ * (ell_w < tile_w), d_ff <= 8192). */
+size_t ffn_sparse_backward_workspace_bytes(const ffn_sparse_config *cfg, int32_t m);
+
+/* Backward pass of ffn_sparse_forward with its selection held fixed: the
+ * gradients of L = sum_t <dy_t, y_t>. With a = z on the active entries,
+ * u = W_up x, h = a u and dh = W_down^T dy:
+ *   du = dh a, dz = dh u (active entries only),
+ *   dW_down[:, i] += sum_t h_ti dy_t, dW_up[i, :] += sum_t du_ti x_t,
+ *   dW_gate[i, :] += sum_t dz_ti x_t, dx_t = sum_i du_ti W_up[i, :] + dz_ti W_gate[i, :].
+ * Source: Sparser/Faster/Lighter page, "Hybrid 應對非均勻稀疏" (training with
+ * the compact format for most tokens and a dense backup for busy ones): the
+ * compact tokens' activations come from `pack` (the forward pass's TwELL
+ * pack, values a as stored: bf16 in bf16 configs), a routed token's gate row
+ * is recomputed densely on matrix cores and its active neurons read from it.
+ *   x, m, bias, bias_scalar, tau, pack: as passed to (and written by) the
+ *               forward call on this handle
+ *   dy          [m x d_model] device, config dtype
+ *   dx          NULL or [m x d_model] device, config dtype: written
+ *   dw_gate, dw_up  NULL or [d_ff x d_model] fp32 device: ADDED TO; only the
+ *               rows of neurons active for some token change
+ *   dw_down_nm  NULL or [d_ff x d_model] fp32 device: the gradient of W_down
+ *               in neuron-major layout (row i = dW_down[:, i]), added to
+ *   workspace   >= ffn_sparse_backward_workspace_bytes(cfg, m), 16-byte aligned
+ * Every sum runs in a fixed order (tokens ascending per neuron), so the
+ * result is reproducible run to run. FFN_E_UNSUPPORTED for other configs. */
+ffn_status ffn_sparse_backward(ffn_sparse_handle *h, const void *x, int32_t m, const float *bias,
+                               float bias_scalar, const float *tau, const ffn_twell_pack *pack,
+                               const void *dy, void *dx, float *dw_gate, float *dw_up, float *dw_down_nm,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of the caller workspace ffn_sparse_moe_forward needs for m tokens
  * routed to topk experts each (0 if invalid; m * topk <= 256). */
 size_t ffn_sparse_moe_workspace_bytes(const ffn_sparse_config *cfg, int32_t m, int32_t topk);
@@ -274,7 +308,10 @@ typedef enum {
   FFN_K_DENSE = 6,     /* dense baseline kernels                               */
   FFN_K_ROUTE = 7,     /* routing pass of a standalone gate_pack               */
   FFN_K_UP = 8,        /* decode: up products of the union neurons (split mode) */
-  FFN_K_COUNT = 9
+  FFN_K_BW_GATE = 9,   /* backward: the routed tokens' gate rows recomputed    */
+  FFN_K_BW_NEURON = 10,/* backward: per-neuron du, dz and weight gradients     */
+  FFN_K_BW_DX = 11,    /* backward: per-token input gradient                   */
+  FFN_K_COUNT = 12
 } ffn_kernel_kind;
 ffn_status ffn_sparse_timing_enable(ffn_sparse_handle *h, int32_t enable, int32_t capacity);
 ffn_status ffn_sparse_timing_read(ffn_sparse_handle *h, int32_t kind, int32_t *launches,
