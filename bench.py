@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_BF16_TFLOPS = 2500.0     # dense bf16 matrix cores
 WORKLOADS = {
     "c2": "decode-relu-bf16-2048x8192",
     "c3": "lopa-relu-thresh-bf16-4096x14336-r512",
@@ -272,6 +273,10 @@ def main():
     elif path == "general" and "up" in kernels:                 # prefill: XCD-sliced up, then down
         alg["up"] = entries * d * 2 + m * d * 2
         alg["updown"] = entries * d * 2 + m * d * 2
+    elif path == "general":
+        # HBM minimum of the sparse pass: each union neuron's up and down rows
+        # once (the per-entry re-reads are cache traffic)
+        alg["updown"] = n_union * row_bytes + m * d * 2 + m * d * 2 + pack_bytes
     elif path == "topk-masked-dense":
         alg["updown"] = F * d * 2 + m * F * 2 + m * d * 2      # all of W_down, the masked h rows, y
     if wl.sel == "topk":
@@ -294,6 +299,13 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": int(alg[dom]), "avg_us": round(kernels[dom]["avg_us"], 3)}
+    if m >= 128 and dom == "gate":
+        # prefill: the gate GEMM is a dense contraction on matrix cores
+        flops = 2.0 * m * F * (r if r else d) + (2.0 * m * r * d if r else 0.0)
+        tf = flops / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(tf, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "flops_per_launch": int(flops), "avg_us": round(kernels[dom]["avg_us"], 3)}
 
     # ---- CPU oracle on a bounded sample of the same workload ----
     # (all the host threads BLAS uses here, then one thread; the oracle is
@@ -419,6 +431,13 @@ def bench_backward(args, dev):
     def step(i):
         ffn, pack, (gg, gu, gd) = layers[i % nl]
         ffn.backward(x, dy, pack, bias=bias, dx=dx, dw_gate=gg, dw_up=gu, dw_down_nm=gd, workspace=ws)
+
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": f"{WORKLOADS[cid]} m={m} backward"}))
+        return
 
     steps = max(5, min(args.steps, 40 if m > 256 else args.steps))
     for i in range(3):
@@ -563,6 +582,13 @@ def bench_moe(args, dev):
         li, b = combos[i % len(combos)]
         xb, ids, wts, tb = batches[b]
         asg.moe_forward(sets[li], xb, ids, wts, tau=tb, y=y, workspace=ws, dense=dense)
+
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": f"{WORKLOADS['moe']} m={m}"}))
+        return
 
     def timed(fn, n, warm):
         for i in range(warm):
