@@ -1612,7 +1612,9 @@ size_t ffn_sparse_moe_workspace_bytes(const ffn_sparse_config* cfg, int32_t m, i
   if (ffn_sparse_check_config(cfg) != FFN_OK || m < 1 || topk < 1 || (size_t)m * topk > (size_t)kMoeMaxPairs)
     return 0;
   const size_t np = (size_t)m * topk, rowb = (size_t)cfg->d_model * esize_of(cfg->dtype);
-  return 2 * align_up(np * rowb) + 2 * align_up(np * 4) + ffn_sparse_pack_bytes(cfg, m);
+  // + one single-token pack per pair for the grouped one-token launches
+  return 2 * align_up(np * rowb) + 2 * align_up(np * 4) + ffn_sparse_pack_bytes(cfg, m) +
+         np * ffn_sparse_pack_bytes(cfg, 1);
 }
 
 ffn_status ffn_sparse_moe_forward(ffn_sparse_handle* const* experts, int32_t n_experts, const void* x, int32_t m,
@@ -1690,6 +1692,69 @@ ffn_status ffn_sparse_moe_forward(ffn_sparse_handle* const* experts, int32_t n_e
   pk.n_dense = reinterpret_cast<int32_t*>(take(4));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (launch_moe_gather(md, s) != hipSuccess) return FFN_E_HIP;
+  // one token per active expert (decode): the experts' one-token kernels run
+  // as one launch each for all of them (grid.y = expert), each expert with its
+  // own pack; otherwise each expert runs its own sequence below
+  std::vector<int> act;
+  for (int e = 0; e < n_experts; ++e)
+    if (cnt[e]) act.push_back(e);
+  bool grouped = !dense;
+  std::vector<DecodeDesc> dds(act.size());
+  for (size_t a = 0; a < act.size() && grouped; ++a) {
+    const int e = act[a];
+    grouped = cnt[e] == 1 && plan_decode(experts[e], 1, &dds[a]) && dds[a].mode == DEC_PART;
+  }
+  if (grouped) {
+    const size_t pb1 = ffn_sparse_pack_bytes(&c, 1);
+    for (size_t a = 0; a < act.size(); ++a) {
+      const int e = act[a];
+      char* pbase = take(pb1);
+      ffn_twell_pack p1{};
+      p1.cnt = reinterpret_cast<int32_t*>(pbase);
+      p1.idx = reinterpret_cast<uint16_t*>(pbase + align_up(nt * 4));
+      p1.val = pbase + align_up(nt * 4) + align_up(nt * E * 2);
+      p1.route = reinterpret_cast<uint8_t*>(pbase + align_up(nt * 4) + align_up(nt * E * 2) + align_up(nt * E * esize_of(c.dtype)));
+      p1.dense_list = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p1.route) + align_up(1));
+      p1.n_dense = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p1.dense_list) + align_up(4));
+      DecodeDesc& d = dds[a];
+      d.x = static_cast<const char*>(md.xg) + (size_t)off[e] * rowb;
+      d.bias = bias ? md.bg + off[e] : nullptr;
+      d.bias_scalar = bias_scalar;
+      d.tau = tau ? md.tg + off[e] : nullptr;
+      d.cnt = p1.cnt;
+      d.idx = p1.idx;
+      d.val = p1.val;
+      d.g_debug = nullptr;
+      d.up = 1;
+      d.y = static_cast<char*>(const_cast<void*>(md.yg)) + (size_t)off[e] * rowb;
+      d.route_pass = 1;
+      d.route = route_desc(experts[e], 1, &p1);
+    }
+    ffn_sparse_handle* h0 = experts[act[0]];
+    for (size_t a0 = 0; a0 < act.size(); a0 += kDecGroupMax) {
+      const int n = (int)std::min<size_t>(kDecGroupMax, act.size() - a0);
+      DecGroup g{};
+      for (int i = 0; i < n; ++i) g.d[i] = dds[a0 + i];
+      hipError_t err = hipSuccess;
+      if (c.rank) {
+        Timed tm(h0, FFN_K_LOWRANK_V, s);
+        err = launch_dec_lowrank_group(g, n, s);
+      }
+      if (err == hipSuccess) {
+        Timed tm(h0, FFN_K_GATE, s);
+        err = launch_dec_gate_group(g, n, s);
+      }
+      if (err == hipSuccess) {
+        Timed tm(h0, FFN_K_UPDOWN, s);
+        err = launch_dec_reduce_group(g, n, s);
+      }
+      if (err != hipSuccess) {
+        for (int i = 0; i < n; ++i) experts[act[a0 + i]]->failed = true;
+        return FFN_E_HIP;
+      }
+    }
+    return hip_status(launch_moe_combine(md, s));
+  }
   // each expert's sparse forward pass on its rows, in expert order
   for (int e = 0; e < n_experts; ++e) {
     if (!cnt[e]) continue;

@@ -259,7 +259,7 @@ __device__ __forceinline__ void stage_rows(uint4* dst, const uint4* src, int row
 
 // ------------------------------------------------------------------ k_dec_lowrank
 template <int IPW, int MAXM>
-__global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank(const DecodeDesc d) {
+__device__ __forceinline__ void dec_lowrank_body(const DecodeDesc& d) {
   extern __shared__ uint4 s_dyn[];
   __shared__ float s_part[kDecVWaves * IPW * MAXM];
   __shared__ float s_g[kDecVWaves * IPW * MAXM];
@@ -277,6 +277,10 @@ __global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank(const DecodeDes
     if (m < d.M && row0 + r < d.rank) d.t[(size_t)m * d.rank + row0 + r] = s_g[r * MAXM + m];
   }
 }
+template <int IPW, int MAXM>
+__global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank(const DecodeDesc d) { dec_lowrank_body<IPW, MAXM>(d); }
+template <int IPW, int MAXM>
+__global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank_grp(const DecGroup g) { dec_lowrank_body<IPW, MAXM>(g.d[blockIdx.y]); }
 
 // ------------------------------------------------------------------ k_dec_lowrank_mf
 // t = V x for 2..16 tokens on matrix cores (bf16 inputs, exact products): a
@@ -370,7 +374,7 @@ __device__ __forceinline__ int lb_count(const uint64_t* p, const WaitCtl& wc, ui
 }
 
 template <int NW, int IPW, int MAXM, bool LOWRANK, int MODE>
-__global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
+__device__ __forceinline__ void dec_gate_body(const DecodeDesc& d) {
   constexpr bool PART = MODE == DEC_PART;
   extern __shared__ uint4 s_dyn[];
   __shared__ float s_part[NW * IPW * MAXM];
@@ -667,6 +671,10 @@ __global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) {
     }
   }
 }
+template <int NW, int IPW, int MAXM, bool LOWRANK, int MODE>
+__global__ __launch_bounds__(64 * NW) void k_dec_gate(const DecodeDesc d) { dec_gate_body<NW, IPW, MAXM, LOWRANK, MODE>(d); }
+template <int NW, int IPW, int MAXM, bool LOWRANK, int MODE>
+__global__ __launch_bounds__(64 * NW) void k_dec_gate_grp(const DecGroup g) { dec_gate_body<NW, IPW, MAXM, LOWRANK, MODE>(g.d[blockIdx.y]); }
 
 // ------------------------------------------------------------------ k_dec_down
 constexpr int kDownThreads = 256;
@@ -792,7 +800,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(const DecodeDesc d) {
 constexpr int kRedThreads = 256;
 
 template <int MAXM>
-__global__ __launch_bounds__(kRedThreads) void k_dec_reduce(const DecodeDesc d) {
+__device__ __forceinline__ void dec_reduce_body(const DecodeDesc& d) {
   constexpr int B = 16 / MAXM;                          // sub-tiles in flight per thread
   __shared__ float s_red[MAXM][32][33];
   const int nsl = d.d / 32;
@@ -847,6 +855,10 @@ __global__ __launch_bounds__(kRedThreads) void k_dec_reduce(const DecodeDesc d) 
     if (m < M) reinterpret_cast<uint16_t*>(d.y)[(size_t)m * dm + (size_t)sl * 32 + c] = (uint16_t)f2bf(sum);
   }
 }
+template <int MAXM>
+__global__ __launch_bounds__(kRedThreads) void k_dec_reduce(const DecodeDesc d) { dec_reduce_body<MAXM>(d); }
+template <int MAXM>
+__global__ __launch_bounds__(kRedThreads) void k_dec_reduce_grp(const DecGroup g) { dec_reduce_body<MAXM>(g.d[blockIdx.y]); }
 
 // ------------------------------------------------------------------ k_dec_up (split mode)
 // The union neurons (set bits of the sub-tile masks, ascending) form the list;
@@ -1399,6 +1411,61 @@ hipError_t launch_dec_down(const DecodeDesc& d, hipStream_t s) {
     case 4: ffn_launch((k_dec_down<4>), grid, blk, 0, s, d); break;
     default: ffn_launch((k_dec_down<8>), grid, blk, 0, s, d); break;
   }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ grouped one-token launches
+// One launch of each one-token kernel for several FFNs of one shape (a
+// mixture-of-experts layer's active experts): grid.y picks the FFN's
+// descriptor, so each expert's workgroups run exactly its own kernel's work.
+hipError_t launch_dec_lowrank_group(const DecGroup& g, int n, hipStream_t s) {
+  const DecodeDesc& d = g.d[0];
+  if (n < 1 || n > kDecGroupMax || d.M != 1 || d.rank <= 0 || d.nslab > 0) return hipErrorInvalidValue;
+  const int P = pow2_pieces(d.d);
+  if (P > 8) return hipErrorInvalidValue;
+  DecGroup gl = g;                                   // ipw carries the pieces per V row here
+  for (int i = 0; i < n; ++i) gl.d[i].ipw = P;
+  auto go = [&](auto kern, int IPW) -> hipError_t {
+    const int R = kDecVWaves * IPW / P;
+    const size_t lds = dec_lowrank_lds(d);
+    hipError_t e = lds_attr(kern, lds);
+    if (e != hipSuccess) return e;
+    ffn_launch(kern, dim3((d.rank + R - 1) / R, n), dim3(64 * kDecVWaves), lds, s, gl);
+    return hipGetLastError();
+  };
+  if (P >= 8) return go(k_dec_lowrank_grp<4, 1>, 4);
+  return go(k_dec_lowrank_grp<2, 1>, 2);
+}
+
+hipError_t launch_dec_gate_group(const DecGroup& g, int n, hipStream_t s) {
+  const DecodeDesc& d = g.d[0];
+  if (n < 1 || n > kDecGroupMax || d.M != 1 || d.mode != DEC_PART || !d.up) return hipErrorInvalidValue;
+  constexpr int NW = dec_gate_waves(1);
+  const int P = pow2_pieces(d.K);
+  if (NW * d.ipw != d.R * P || d.R > 64 || d.R < 2 || d.T % d.R != 0 || d.F % d.R != 0 || d.T / d.R > 64)
+    return hipErrorInvalidValue;
+  const size_t lds = dec_gate_lds(d);
+  auto go = [&](auto kern) -> hipError_t {
+    hipError_t e = lds_attr(kern, lds);
+    if (e != hipSuccess) return e;
+    ffn_launch(kern, dim3(d.F / d.R, n), dim3(64 * NW), lds, s, g);
+    return hipGetLastError();
+  };
+  const bool lr = d.rank > 0;
+  switch (d.ipw) {
+    case 1: return lr ? go(k_dec_gate_grp<NW, 1, 1, true, DEC_PART>) : go(k_dec_gate_grp<NW, 1, 1, false, DEC_PART>);
+    case 2: return lr ? go(k_dec_gate_grp<NW, 2, 1, true, DEC_PART>) : go(k_dec_gate_grp<NW, 2, 1, false, DEC_PART>);
+    case 4: return lr ? go(k_dec_gate_grp<NW, 4, 1, true, DEC_PART>) : go(k_dec_gate_grp<NW, 4, 1, false, DEC_PART>);
+    case 8: return lr ? go(k_dec_gate_grp<NW, 8, 1, true, DEC_PART>) : go(k_dec_gate_grp<NW, 8, 1, false, DEC_PART>);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dec_reduce_group(const DecGroup& g, int n, hipStream_t s) {
+  const DecodeDesc& d = g.d[0];
+  if (n < 1 || n > kDecGroupMax || d.M != 1 || d.d % 32 != 0 || d.F / d.R > kDecMaxSub || !d.part)
+    return hipErrorInvalidValue;
+  ffn_launch(k_dec_reduce_grp<1>, dim3(d.d / 32 + (d.route_pass ? 1 : 0), n), dim3(kRedThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -266,6 +266,16 @@ struct DecodeDesc {
   float* tslab;
   RouteDesc route;
 };
+// Descriptors of several FFNs of one shape for the grouped one-token launches
+// (grid.y selects the FFN).
+constexpr int kDecGroupMax = 8;
+struct DecGroup {
+  DecodeDesc d[kDecGroupMax];
+};
+static_assert(sizeof(DecGroup) <= 4096, "kernel arguments are limited to 4 KiB");
+hipError_t launch_dec_lowrank_group(const DecGroup& g, int n, hipStream_t s);
+hipError_t launch_dec_gate_group(const DecGroup& g, int n, hipStream_t s);
+hipError_t launch_dec_reduce_group(const DecGroup& g, int n, hipStream_t s);
 constexpr int kDecMaxM = 16;       // split sequence; the chunk and partial-row modes stop at 8
 // waves of the gate workgroup: 16 for one token; 8 (twice the registers per
 // thread) when the up / down accumulators hold several tokens
