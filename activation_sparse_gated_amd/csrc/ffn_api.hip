@@ -1478,7 +1478,7 @@ bool bw_supported(const ffn_sparse_config& c) {
          c.tile_w <= 1024 && slots <= 8192 && (c.ell_w >= c.tile_w || c.d_ff <= 8192);
 }
 struct BwLayout {
-  size_t slot, zr, blk, colptr, ent_tok, ent_pos, du, dz, total;
+  size_t slot, zr, blk, colptr, ent_tok, ent_pos, du, dz, dxp, total;
   long long pbase, pcap;
   int nblk;
 };
@@ -1503,6 +1503,8 @@ BwLayout bw_layout(const ffn_sparse_config& c, int m) {
   L.ent_pos = take((size_t)L.pcap * 4);
   L.du = take((size_t)L.pcap * 4);
   L.dz = take((size_t)L.pcap * 4);
+  const int S = bw_dx_splits(m);
+  L.dxp = take(S > 1 ? (size_t)S * m * c.d_model * 4 : 4);
   L.total = o;
   return L;
 }
@@ -1566,6 +1568,7 @@ ffn_status ffn_sparse_backward(ffn_sparse_handle* h, const void* x, int32_t m, c
     d.ent_pos = reinterpret_cast<int32_t*>(w + L.ent_pos);
     d.du = reinterpret_cast<float*>(w + L.du);
     d.dz = reinterpret_cast<float*>(w + L.dz);
+    d.dxp = reinterpret_cast<float*>(w + L.dxp);
     d.pbase = L.pbase;
     d.dw_gate = dw_gate;
     d.dw_up = dw_up;

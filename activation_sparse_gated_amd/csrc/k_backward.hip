@@ -24,6 +24,8 @@
 //                token order and added to the fp32 accumulators.
 //   k_bw_dx      one workgroup per token: dx from its active neurons' W_up and
 //                W_gate rows and their du, dz.
+#include <algorithm>
+
 #include "common.cuh"
 #include "kernels.cuh"
 #include "wave.cuh"
@@ -327,7 +329,9 @@ __global__ __launch_bounds__(kBwThreads) void k_bw_dx(const BwDesc d) {
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-  for (int s0 = 0; s0 < n; s0 += kBwDxBatch) {
+  // split S = gridDim.y of this token's list: batch b goes to split b mod S
+  const int S = gridDim.y;
+  for (int s0 = blockIdx.y * kBwDxBatch; s0 < n; s0 += S * kBwDxBatch) {
     Raw8<BF> wu[kBwDxBatch][CH], wg[kBwDxBatch][CH];
     float du[kBwDxBatch], dz[kBwDxBatch];
 #pragma unroll
@@ -366,6 +370,18 @@ __global__ __launch_bounds__(kBwThreads) void k_bw_dx(const BwDesc d) {
         for (int e = 0; e < 8; ++e) acc[c][e] = fmaf(dz[bb], g8[e], fmaf(du[bb], a8[e], acc[c][e]));
       }
   }
+  if (S > 1) {
+    // fp32 partial row of this split; k_bw_dxsum adds the splits in order
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int col = (threadIdx.x + c * kBwThreads) * 8;
+      if (col >= d.d) continue;
+      float* o = d.dxp + ((size_t)blockIdx.y * d.m + t) * d.d + col;
+      *reinterpret_cast<float4*>(o) = float4{acc[c][0], acc[c][1], acc[c][2], acc[c][3]};
+      *reinterpret_cast<float4*>(o + 4) = float4{acc[c][4], acc[c][5], acc[c][6], acc[c][7]};
+    }
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int col = (threadIdx.x + c * kBwThreads) * 8;
@@ -382,6 +398,33 @@ __global__ __launch_bounds__(kBwThreads) void k_bw_dx(const BwDesc d) {
       *reinterpret_cast<float4*>(o) = float4{acc[c][0], acc[c][1], acc[c][2], acc[c][3]};
       *reinterpret_cast<float4*>(o + 4) = float4{acc[c][4], acc[c][5], acc[c][6], acc[c][7]};
     }
+  }
+}
+
+// dx of token blockIdx.x from its splits' fp32 partial rows, added in split order
+__global__ __launch_bounds__(kBwThreads) void k_bw_dxsum(const BwDesc d, int S) {
+  const int t = blockIdx.x;
+  const int col = (blockIdx.y * kBwThreads + threadIdx.x) * 8;
+  if (col >= d.d) return;
+  float a[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    const float* p = d.dxp + ((size_t)sp * d.m + t) * d.d + col;
+    const float4 u = *reinterpret_cast<const float4*>(p), v = *reinterpret_cast<const float4*>(p + 4);
+    a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w; a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
+  }
+  if (d.dtype == DT_BF16) {
+    uint4 o;
+    o.x = f2bf(a[0]) | (f2bf(a[1]) << 16);
+    o.y = f2bf(a[2]) | (f2bf(a[3]) << 16);
+    o.z = f2bf(a[4]) | (f2bf(a[5]) << 16);
+    o.w = f2bf(a[6]) | (f2bf(a[7]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.dx) + (size_t)t * d.d + col) = o;
+  } else {
+    float* o = static_cast<float*>(d.dx) + (size_t)t * d.d + col;
+    *reinterpret_cast<float4*>(o) = float4{a[0], a[1], a[2], a[3]};
+    *reinterpret_cast<float4*>(o + 4) = float4{a[4], a[5], a[6], a[7]};
   }
 }
 
@@ -427,16 +470,22 @@ hipError_t launch_bw_neuron(const BwDesc& d, hipStream_t s) {
   }
   return hipGetLastError();
 }
+int bw_dx_splits(int m) { return std::max(1, std::min(kBwDxMaxSplit, kBwDxPartRows / std::max(m, 1))); }
+
 hipError_t launch_bw_dx(const BwDesc& d, hipStream_t s) {
   if (!bw_shape_ok(d) || !d.dx) return hipErrorInvalidValue;
+  const int S = bw_dx_splits(d.m);
+  if (S > 1 && !d.dxp) return hipErrorInvalidValue;
   const bool two = d.d > 8 * kBwThreads;
+  const dim3 grid(d.m, S);
   if (d.dtype == DT_BF16) {
-    if (two) ffn_launch((k_bw_dx<true, 2>), dim3(d.m), dim3(kBwThreads), 0, s, d);
-    else ffn_launch((k_bw_dx<true, 1>), dim3(d.m), dim3(kBwThreads), 0, s, d);
+    if (two) ffn_launch((k_bw_dx<true, 2>), grid, dim3(kBwThreads), 0, s, d);
+    else ffn_launch((k_bw_dx<true, 1>), grid, dim3(kBwThreads), 0, s, d);
   } else {
-    if (two) ffn_launch((k_bw_dx<false, 2>), dim3(d.m), dim3(kBwThreads), 0, s, d);
-    else ffn_launch((k_bw_dx<false, 1>), dim3(d.m), dim3(kBwThreads), 0, s, d);
+    if (two) ffn_launch((k_bw_dx<false, 2>), grid, dim3(kBwThreads), 0, s, d);
+    else ffn_launch((k_bw_dx<false, 1>), grid, dim3(kBwThreads), 0, s, d);
   }
+  if (S > 1) ffn_launch(k_bw_dxsum, dim3(d.m, (d.d + 8 * kBwThreads - 1) / (8 * kBwThreads)), dim3(kBwThreads), 0, s, d, S);
   return hipGetLastError();
 }
 

@@ -337,6 +337,7 @@ struct BwDesc {
   int32_t* colptr;                  // [F + 1] neuron-major start of each neuron's pairs
   int32_t* ent_tok; int32_t* ent_pos;   // neuron-major pairs: token, pair position
   float* du; float* dz;             // per pair position
+  float* dxp;                       // [splits x m x d] fp32 partial dx rows (few tokens), or null
   long long pbase;
   float* dw_gate; float* dw_up; float* dw_down;   // [F x d] fp32, accumulated
 };
@@ -346,6 +347,11 @@ hipError_t launch_bw_scan(const BwDesc& d, hipStream_t s);
 hipError_t launch_bw_fill(const BwDesc& d, hipStream_t s);
 hipError_t launch_bw_neuron(const BwDesc& d, hipStream_t s);
 hipError_t launch_bw_dx(const BwDesc& d, hipStream_t s);
+// Splits of each token's neuron list in the dx kernel (more workgroups for
+// few tokens; at most kBwDxPartRows partial rows).
+constexpr int kBwDxMaxSplit = 16;
+constexpr int kBwDxPartRows = 512;
+int bw_dx_splits(int m);
 hipError_t launch_moe_gather(const MoeDesc& d, hipStream_t s);
 hipError_t launch_moe_combine(const MoeDesc& d, hipStream_t s);
 // Slices of d of the matrix-core first stage for m tokens (0: the VALU kernel).
