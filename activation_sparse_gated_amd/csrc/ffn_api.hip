@@ -626,6 +626,32 @@ hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const in
 }
 
 // y rows = W_down h for `m` slots of hbuf (scattered through `list`).
+// y = A x for m tokens through the library's dense GEMM kernels (bf16, K a
+// multiple of 32), for entry points that hold no FFN handle (the GSI linear
+// map's dense baseline): a handle with the default launch shapes plans it.
+hipError_t dense_rows_impl(const void* A, int nrows, int K, const void* x, int m, void* y, int ldy, int cus,
+                           hipStream_t s) {
+  ffn_sparse_handle h{};
+  h.cfg.dtype = FFN_BF16;
+  h.cus = cus;
+  GemmDesc g = gemm_base(&h);
+  g.A0 = A;
+  g.nrows = nrows;
+  g.lda = K;
+  g.K = K;
+  g.B = x;
+  g.ldb = K;
+  g.M = m;
+  if (K % 32 != 0 || !plan_plain(g, &h) || g.ks != 1) return hipErrorInvalidValue;
+  EpiDesc e{};
+  e.kind = EPI_Y;
+  e.F = nrows;
+  e.out_f32 = 0;
+  e.y = y;
+  e.ldy = ldy;
+  return launch_gemm(g, e, s);
+}
+
 hipError_t run_dense_down(ffn_sparse_handle* h, int m, const int32_t* list, const int32_t* m_dev,
                           void* y, int kind, hipStream_t s) {
   const auto& c = h->cfg;
@@ -1067,6 +1093,13 @@ ffn_status guarded(ffn_sparse_handle* h, Fn fn) {
 }
 
 }  // namespace
+
+namespace ffn {
+hipError_t dense_rows_bf16(const void* A, int nrows, int K, const void* x, int m, void* y, int ldy, int cus,
+                           hipStream_t s) {
+  return dense_rows_impl(A, nrows, K, x, m, y, ldy, cus, s);
+}
+}  // namespace ffn
 
 extern "C" {
 

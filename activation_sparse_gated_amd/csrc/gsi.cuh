@@ -35,6 +35,7 @@ struct GsiDesc {
   int lpr;                            // lanes per k-row (power of two, 8 elements each)
   int res_nl, nres;                   // k-rows per lane and workgroups of the residual kernel
   int out_nl, nout;                   // the same for the output kernel
+  int lpr4, out_nl4, nout4;           // the output kernel with several tokens: 4 chunks a lane
 };
 
 bool gsi_plan(GsiDesc& d, int cus);

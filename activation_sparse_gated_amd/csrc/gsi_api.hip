@@ -206,6 +206,12 @@ ffn_status ffn_gsi_dense_forward(ffn_gsi_handle* h, const void* x, int32_t m, vo
       return launch_sgemv1(d, s) == hipSuccess ? FFN_OK : fail(h);
     }
   }
+  if (c.d_in % 32 == 0) {
+    // several tokens: the library's dense GEMM kernels (VALU GEMV up to 8
+    // tokens, matrix-core tiles beyond)
+    GsiTimed tm(h, FFN_GSI_K_DENSE);
+    return dense_rows_bf16(h->w, c.d_out, c.d_in, x, m, y, c.d_out, h->cus, s) == hipSuccess ? FFN_OK : fail(h);
+  }
   for (int t0 = 0; t0 < m; t0 += kGsiMaxM) {
     GsiDesc d = h->plan;
     d.M = std::min(kGsiMaxM, m - t0);

@@ -200,25 +200,34 @@ __global__ __launch_bounds__(64 * kGsiResWaves) void k_gsi_resid(const GsiDesc d
 // Every workgroup takes the same decision from the residual parts (the same
 // loads and sums in the same order); workgroup 0 also writes rho, the slow
 // list and its count. Tokens are taken TQ at a time, as in the residual kernel.
-template <int TQ>
+// NC: 16-byte chunks of an image row per lane (1, or 4 with several tokens:
+// fewer lanes per row, so each token's row sum takes fewer butterfly levels
+// per multiply-add).
+template <int TQ, int NC>
 __global__ __launch_bounds__(256) void k_gsi_out(const GsiDesc d) {
   extern __shared__ float4 s_dyn4[];
   const float* s_g = reinterpret_cast<const float*>(s_dyn4);     // [M x k]
   __shared__ float s_parts[2 * kGsiMaxM * kGsiResParts];
   __shared__ float s_rho[kGsiMaxM];
   __shared__ float s_yacc[4][kGsiMaxM];
+  constexpr int NLMAX = NC == 1 ? kGsiMaxNl : 2;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int lpr = d.lpr, rpi = 64 / lpr, c8 = lane & (lpr - 1), rsub = lane / lpr;
-  const int col = c8 * 8;
-  const int rows_wg = 4 * rpi * d.out_nl;
+  const int lpr = NC == 1 ? d.lpr : d.lpr4, rpi = 64 / lpr, c8 = lane & (lpr - 1), rsub = lane / lpr;
+  const int nl = NC == 1 ? d.out_nl : d.out_nl4;
+  const int col = c8 * 8;             // chunk c of a lane: elements (c * lpr + c8) * 8 ...
+  const int rows_wg = 4 * rpi * nl;
   const int o0 = blockIdx.x * rows_wg;
   // image rows first: they are needed unless every token is slow
-  uint4 a[kGsiMaxNl];
+  uint4 a[NLMAX][NC];
 #pragma unroll
-  for (int i = 0; i < kGsiMaxNl; ++i) {
+  for (int i = 0; i < NLMAX; ++i) {
     const int o = o0 + (i * 4 + wave) * rpi + rsub;
-    a[i] = (!d.force_slow && i < d.out_nl && o < d.dout && col < d.k) ? ldg16(d.img + (size_t)o * d.k + col)
-                                                                       : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int cc = col + c * lpr * 8;
+      a[i][c] = (!d.force_slow && i < nl && o < d.dout && cc < d.k) ? ldg16(d.img + (size_t)o * d.k + cc)
+                                                                     : uint4{0, 0, 0, 0};
+    }
   }
   const uint32_t all = (1u << d.M) - 1u;
   uint32_t fast = 0;
@@ -274,18 +283,24 @@ __global__ __launch_bounds__(256) void k_gsi_out(const GsiDesc d) {
     for (int m0 = 0; m0 < d.M; m0 += TQ) {
       if (!((fast >> m0) & ((1u << TQ) - 1u))) continue;
 #pragma unroll
-      for (int i = 0; i < kGsiMaxNl; ++i) {
-        if (i < d.out_nl) {
+      for (int i = 0; i < NLMAX; ++i) {
+        if (i < nl) {
           const int o = o0 + (i * 4 + wave) * rpi + rsub;
           float p[TQ];
 #pragma unroll
           for (int t = 0; t < TQ; ++t) {
             const int m = m0 + t;
             p[t] = 0.f;
-            if (((fast >> m) & 1u) && col < d.k) {
-              const float4 b0 = *reinterpret_cast<const float4*>(s_g + m * d.k + col);
-              const float4 b1 = *reinterpret_cast<const float4*>(s_g + m * d.k + col + 4);
-              p[t] = dot8_f32(a[i], b0, b1, 0.f);
+            if ((fast >> m) & 1u) {
+#pragma unroll
+              for (int c = 0; c < NC; ++c) {
+                const int cc = col + c * lpr * 8;
+                if (cc < d.k) {
+                  const float4 b0 = *reinterpret_cast<const float4*>(s_g + m * d.k + cc);
+                  const float4 b1 = *reinterpret_cast<const float4*>(s_g + m * d.k + cc + 4);
+                  p[t] = dot8_f32(a[i][c], b0, b1, p[t]);
+                }
+              }
             }
           }
           group_sum(p, lpr);
@@ -419,6 +434,11 @@ bool gsi_plan(GsiDesc& d, int cus) {
     }
   }
   d.nout = (d.dout + 4 * rpi * d.out_nl - 1) / (4 * rpi * d.out_nl);
+  // several tokens: 4 chunks (32 elements) of an image row per lane
+  d.lpr4 = pow2ceil((d.k + 31) / 32);
+  const int rpi4 = 64 / d.lpr4;
+  d.out_nl4 = (d.dout + 4 * rpi4 * 2 - 1) / (4 * rpi4 * 2) >= 2 * cus ? 2 : 1;
+  d.nout4 = (d.dout + 4 * rpi4 * d.out_nl4 - 1) / (4 * rpi4 * d.out_nl4);
   return true;
 }
 
@@ -456,13 +476,15 @@ hipError_t launch_gsi_resid(const GsiDesc& d, hipStream_t s) {
 }
 
 hipError_t launch_gsi_out(const GsiDesc& d, hipStream_t s) {
-  if (d.M < 1 || d.M > kGsiMaxM || d.out_nl < 1 || d.out_nl > kGsiMaxNl || d.nout < 1) return hipErrorInvalidValue;
+  if (d.M < 1 || d.M > kGsiMaxM || d.out_nl < 1 || d.out_nl > kGsiMaxNl || d.nout < 1 || d.out_nl4 < 1 ||
+      d.out_nl4 > 2 || d.nout4 < 1)
+    return hipErrorInvalidValue;
   const size_t lds = (size_t)d.M * d.k * 4;
-  const dim3 grid(d.nout), blk(256);
+  const dim3 blk(256);
   switch (std::min(group_maxm(d.M), 4)) {
-    case 1: ffn_launch(k_gsi_out<1>, grid, blk, lds, s, d); break;
-    case 2: ffn_launch(k_gsi_out<2>, grid, blk, lds, s, d); break;
-    default: ffn_launch(k_gsi_out<4>, grid, blk, lds, s, d); break;
+    case 1: ffn_launch((k_gsi_out<1, 1>), dim3(d.nout), blk, lds, s, d); break;
+    case 2: ffn_launch((k_gsi_out<2, 1>), dim3(d.nout), blk, lds, s, d); break;
+    default: ffn_launch((k_gsi_out<4, 4>), dim3(d.nout4), blk, lds, s, d); break;
   }
   return hipGetLastError();
 }

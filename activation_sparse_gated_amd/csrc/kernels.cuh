@@ -87,6 +87,9 @@ struct EpiDesc {
 };
 
 hipError_t launch_gemm(const GemmDesc& g, const EpiDesc& e, hipStream_t s);
+// y [m x ldy] = A [nrows x K] x for m tokens (bf16) with the dense GEMM kernels.
+hipError_t dense_rows_bf16(const void* A, int nrows, int K, const void* x, int m, void* y, int ldy, int cus,
+                           hipStream_t s);
 
 // Transpose rows x cols (row-major) -> cols x rows, element size 2 or 4 bytes.
 hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int esize, hipStream_t s);
