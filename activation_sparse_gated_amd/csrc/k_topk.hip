@@ -1,4 +1,4 @@
-// WINA top-k selection and TwELL pack, one workgroup per token.
+// WINA top-k selection and TwELL pack, G workgroups per token.
 //
 // Scores s_i = |h_i| * ||W_down[:, i]||_2 (WINA page, section 3.1) are
 // non-negative, so their fp32 bit patterns order like the values. A three-pass
@@ -9,10 +9,16 @@
 // one block-wide scan (of the counts above and equal to the cut, packed in one
 // word) gives every kept neuron its rank in index order. The ranks go to LDS,
 // and one wave per TwELL tile writes the tile's slots from them (slot = rank
-// minus the kept count before the tile) with coalesced stores. Optionally the
+// minus the kept count before the tile) with coalesced stores. The G
+// workgroups of a token each take the selection in full (the same loads and
+// passes, so the same cut) and then rank and pack only their own run of
+// tiles: the ranking and the pack stores, which bound one workgroup on its
+// CU, are spread over G CUs. Optionally the
 // kernel also writes the kept neurons as a neuron-ordered list with bf16 h (the
 // input of the list-driven down kernel) or h rows with the other neurons
 // zeroed (the input of a dense down product).
+#include <algorithm>
+
 #include "common.cuh"
 #include "kernels.cuh"
 
@@ -28,7 +34,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   __shared__ int s_scan[16];
   __shared__ int s_wtot[2][TOPK_THREADS / 64];   // per-wave histogram sums, alternating by pass
   __shared__ uint32_t s_digit[3], s_above[3];
-  const int tok = blockIdx.x, F = d.F, tid = threadIdx.x;
+  const int G = d.G, tok = blockIdx.x / G, wg = blockIdx.x - tok * G, F = d.F, tid = threadIdx.x;
+  const int T = d.T, ntiles = F / T;
+  const int tlo = wg * ntiles / G, thi = (wg + 1) * ntiles / G;   // this workgroup's tiles
+  const int lo = tlo * T, hi = thi * T;
   const float* srow = d.s_buf + (size_t)tok * F;
   float* s_hv = reinterpret_cast<float*>(s_keys + F);
   const float* hrow = d.h_buf + (size_t)tok * F;
@@ -38,16 +47,16 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
     float sv[CW], hv[CW];
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
-      const int i = min(tid + c * TOPK_THREADS, F - 1);  // past the end: a re-read, not stored
+      const int iu = tid + c * TOPK_THREADS, i = min(iu, F - 1);   // past the end: a re-read, not stored
       sv[c] = srow[i];
-      hv[c] = HLDS ? hrow[i] : 0.f;
+      hv[c] = (HLDS && iu >= lo && iu < hi) ? hrow[i] : 0.f;       // h of the own tiles only
     }
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
       const int i = tid + c * TOPK_THREADS;
       if (i < F) {
         s_keys[i] = __float_as_uint(sv[c]);
-        if (HLDS) s_hv[i] = hv[c];
+        if (HLDS && i >= lo && i < hi) s_hv[i] = hv[c];
       }
     }
     for (int i = tid; i < 2048; i += TOPK_THREADS) s_hist[0][i] = 0u;   // the first pass's histogram
@@ -118,8 +127,11 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   const int eqb = pre2 & 0xFFFF, gtb = pre2 >> 16;
   int er = eqb;
   uint32_t cm = 0u;                                // kept elements of the run, bit c
+  // runs that meet the own tiles: the others need only their prefix
+  const bool mine = n > 0 && i0 < hi && i0 + n > lo;
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
+    if (!mine) break;
     bool sel;
     if (k == 0) sel = false;
     else if (k >= F) sel = true;
@@ -134,12 +146,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   }
   const int pb = k == 0 ? 0 : (k >= F ? i0 : gtb + min(need, eqb));
   const int nsel_tot = k == 0 ? 0 : (k >= F ? F : (tot >> 16) + min(need, tot & 0xFFFF));
-  // kept count before each tile start that falls in this run; each thread
-  // then overwrites its own keys with the kept neurons' ranks (or ~0)
-  const int T = d.T, ntiles = F / T;
-  for (int j = (i0 + T - 1) / T; j * T < i0 + n; ++j) s_tstart[j] = pb + __popc(cm & ((1u << (j * T - i0)) - 1u));
+  // kept count before each start of an own tile (or of the tile after them)
+  // that falls in this run; a start at the run's first element is the prefix
+  // itself. The runs that meet the own tiles then overwrite their keys with
+  // the kept neurons' ranks (or ~0)
+  for (int j = (i0 + T - 1) / T; j * T < i0 + n; ++j)
+    if (j >= tlo && j <= thi && (mine || j * T == i0)) s_tstart[j] = pb + __popc(cm & ((1u << (j * T - i0)) - 1u));
   if (tid == 0) s_tstart[ntiles] = nsel_tot;
-  {
+  if (mine) {
     int p = pb;
 #pragma unroll
     for (int c = 0; c < CW; ++c)
@@ -151,7 +165,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   // the masked h row, from the ranks in LDS
   const int lane = tid & 63, wave = tid >> 6;
   uint16_t* hm = d.hmask ? reinterpret_cast<uint16_t*>(d.hmask) + (size_t)tok * d.ldhm : nullptr;
-  for (int j = wave; j < ntiles; j += TOPK_THREADS / 64) {
+  for (int j = tlo + wave; j < thi; j += TOPK_THREADS / 64) {
     const int base = s_tstart[j], cntj = s_tstart[j + 1] - base;
     const size_t slot0 = ((size_t)tok * ntiles + j) * T;   // E == T
     if (lane == 0) d.cnt[(size_t)tok * ntiles + j] = cntj;
@@ -178,6 +192,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
       }
     }
   }
+  if (wg != 0) return;
   if (d.ul_nrn) {
     // list length and the zero pad up to the next multiple of 32
     const int pad = (nsel_tot + 31) / 32 * 32;
@@ -194,8 +209,13 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(const TopkDesc d) {
   }
 }
 
-hipError_t launch_topk(const TopkDesc& d, hipStream_t s) {
-  if (d.M <= 0) return hipSuccess;
+hipError_t launch_topk(const TopkDesc& desc, hipStream_t s) {
+  if (desc.M <= 0) return hipSuccess;
+  TopkDesc d = desc;
+  // workgroups per token: up to 16 (and at most one per tile), about one
+  // workgroup per CU over all tokens
+  const int ntiles = d.T > 0 ? d.F / d.T : 0;
+  d.G = std::max(1, std::min({16, ntiles, 256 / d.M}));
   if (d.F > 32 * TOPK_THREADS || d.T <= 0 || d.F % d.T != 0 || d.F / d.T > 1024 || (d.ul_nrn && d.M != 1) ||
       (d.hmask && d.ldhm < d.F))
     return hipErrorInvalidValue;
@@ -208,8 +228,8 @@ hipError_t launch_topk(const TopkDesc& d, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if (wide) ffn_launch(k_topk<32, false>, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
-  else ffn_launch(k_topk<16, true>, dim3(d.M), dim3(TOPK_THREADS), lds, s, d);
+  if (wide) ffn_launch(k_topk<32, false>, dim3(d.M * d.G), dim3(TOPK_THREADS), lds, s, d);
+  else ffn_launch(k_topk<16, true>, dim3(d.M * d.G), dim3(TOPK_THREADS), lds, s, d);
   return hipGetLastError();
 }
 

@@ -107,6 +107,7 @@ struct TopkDesc {
   // optional outputs (null: not written)
   int32_t* ul_nrn; uint16_t* ul_hT; int32_t* ul_total;   // one token: kept neurons ascending, bf16 h, count
   void* hmask; int ldhm;                                  // bf16 h rows, unselected neurons zero
+  int G;                                                  // workgroups per token (set by the launcher)
 };
 hipError_t launch_topk(const TopkDesc& d, hipStream_t s);
 
