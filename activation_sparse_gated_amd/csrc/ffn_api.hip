@@ -1510,8 +1510,12 @@ bool bw_supported(const ffn_sparse_config& c) {
   return c.rank == 0 && c.act == FFN_RELU && c.sel != FFN_SEL_TOPK_WINA && c.in_keep == 0 && c.d_model <= 4096 &&
          c.tile_w <= 1024 && slots <= 8192 && (c.ell_w >= c.tile_w || c.d_ff <= 8192);
 }
+// dx on matrix cores (bf16, training batch sizes): see k_bw_duz
+bool bw_dx_dense(const ffn_sparse_config& c, int m) {
+  return c.dtype == FFN_BF16 && m >= kBwDxDenseMin && c.d_ff % 32 == 0 && c.d_model % 64 == 0;
+}
 struct BwLayout {
-  size_t slot, zr, blk, colptr, ent_tok, ent_pos, du, dz, dxp, total;
+  size_t slot, zr, blk, colptr, ent_tok, ent_pos, du, dz, dxp, wt, duz, total;
   long long pbase, pcap;
   int nblk;
 };
@@ -1538,6 +1542,10 @@ BwLayout bw_layout(const ffn_sparse_config& c, int m) {
   L.dz = take((size_t)L.pcap * 4);
   const int S = bw_dx_splits(m);
   L.dxp = take(S > 1 ? (size_t)S * m * c.d_model * 4 : 4);
+  // matrix-core dx: [W_up; W_gate] transposed, [d x 2F], and the (du | dz) rows
+  const bool dense_dx = bw_dx_dense(c, m);
+  L.wt = take(dense_dx ? (size_t)c.d_model * 2 * c.d_ff * 2 : 4);
+  L.duz = take(dense_dx ? (size_t)m * 2 * c.d_ff * 2 : 4);
   L.total = o;
   return L;
 }
@@ -1637,8 +1645,35 @@ ffn_status ffn_sparse_backward(ffn_sparse_handle* h, const void* x, int32_t m, c
       e = launch_bw_neuron(d, s);
     }
     if (e == hipSuccess && dx) {
-      Timed tm(h, FFN_K_BW_DX, s);
-      e = launch_bw_dx(d, s);
+      if (bw_dx_dense(c, m)) {
+        // dx = (du | dz) [W_up; W_gate] on matrix cores: both weights
+        // transposed side by side into [d x 2F], the dense rows, one GEMM
+        uint16_t* wt = reinterpret_cast<uint16_t*>(w + L.wt);
+        d.duz = reinterpret_cast<uint16_t*>(w + L.duz);
+        GemmDesc g = gemm_base(h);
+        g.A0 = wt;
+        g.nrows = c.d_model;
+        g.lda = 2 * c.d_ff;
+        g.K = 2 * c.d_ff;
+        g.B = d.duz;
+        g.ldb = 2 * c.d_ff;
+        g.M = m;
+        EpiDesc ep{};
+        ep.kind = EPI_Y;
+        ep.F = c.d_model;
+        ep.out_f32 = false;
+        ep.y = dx;
+        ep.ldy = c.d_model;
+        if (!plan_plain(g, h)) return FFN_E_UNSUPPORTED;
+        Timed tm(h, FFN_K_BW_DX, s);
+        e = launch_transpose_ld(h->w_up, wt, c.d_ff, c.d_model, 2 * c.d_ff, 2, s);
+        if (e == hipSuccess) e = launch_transpose_ld(h->w_gate, wt + c.d_ff, c.d_ff, c.d_model, 2 * c.d_ff, 2, s);
+        if (e == hipSuccess) e = launch_bw_duz(d, s);
+        if (e == hipSuccess) e = launch_gemm(g, ep, s);
+      } else {
+        Timed tm(h, FFN_K_BW_DX, s);
+        e = launch_bw_dx(d, s);
+      }
     }
     return hip_status(e);
   });

@@ -24,6 +24,11 @@
 //                token order and added to the fp32 accumulators.
 //   k_bw_dx      one workgroup per token: dx from its active neurons' W_up and
 //                W_gate rows and their du, dz.
+//   k_bw_duz     training batch sizes: each token's du and dz as one dense bf16
+//                row (du over the neurons, then dz), so that dx is a
+//                matrix-core GEMM with [W_up; W_gate] transposed: at 10%
+//                density the per-token row gathers cost more than the dense
+//                product.
 #include <algorithm>
 
 #include "common.cuh"
@@ -435,6 +440,49 @@ static bool bw_shape_ok(const BwDesc& d) {
   return d.m >= 1 && d.d % 8 == 0 && d.d <= 8 * kBwChunks * kBwThreads && d.T <= 1024 && d.F % d.T == 0 &&
          d.nblk == (d.m + kBwBlock - 1) / kBwBlock && (long long)d.ntiles * d.E <= kBwDxList &&
          (!d.routing || d.F <= kBwDxList);
+}
+
+// Row t of (du | dz): zero, then the token's active neurons (the same list
+// as k_bw_dx), staged in LDS and written with 16-byte stores.
+__global__ __launch_bounds__(kBwThreads) void k_bw_duz(const BwDesc d) {
+  extern __shared__ uint4 s_dz4[];
+  uint16_t* s_row = reinterpret_cast<uint16_t*>(s_dz4);      // [2F]
+  const int t = blockIdx.x, F = d.F, n16 = 2 * F / 8;
+  const int r = d.slot_of[t];
+  for (int c = threadIdx.x; c < n16; c += kBwThreads) s_dz4[c] = uint4{0, 0, 0, 0};
+  __syncthreads();
+  if (r < 0) {
+    const int nslots = d.ntiles * d.E;
+    for (int q0 = threadIdx.x; q0 < nslots; q0 += kBwThreads) {
+      const int j = q0 / d.E, q = q0 - j * d.E;
+      const size_t pk = (size_t)t * d.ntiles + j;
+      if (q < min(d.cnt[pk], d.E)) {
+        const long long p = (long long)pk * d.E + q;
+        const int i = j * d.T + d.idx[p];
+        s_row[i] = (uint16_t)f2bf(d.du[p]);
+        s_row[F + i] = (uint16_t)f2bf(d.dz[p]);
+      }
+    }
+  } else {
+    const float b = bw_bias(d, t), cut = bw_cut(d, t);
+    for (int i = threadIdx.x; i < F; i += kBwThreads)
+      if (d.zr[(size_t)r * F + i] + b > cut) {
+        const long long p = d.pbase + (long long)r * F + i;
+        s_row[i] = (uint16_t)f2bf(d.du[p]);
+        s_row[F + i] = (uint16_t)f2bf(d.dz[p]);
+      }
+  }
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(d.duz + (size_t)t * 2 * F);
+  for (int c = threadIdx.x; c < n16; c += kBwThreads) dst[c] = s_dz4[c];
+}
+
+hipError_t launch_bw_duz(const BwDesc& d, hipStream_t s) {
+  if (!bw_shape_ok(d) || !d.duz || d.dtype != DT_BF16 || d.F % 8 != 0) return hipErrorInvalidValue;
+  const size_t lds = (size_t)d.F * 2 * sizeof(uint16_t);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  ffn_launch(k_bw_duz, dim3(d.m), dim3(kBwThreads), lds, s, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_bw_slots(const BwDesc& d, hipStream_t s) {

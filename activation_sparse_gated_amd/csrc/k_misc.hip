@@ -4,10 +4,11 @@
 
 namespace ffn {
 
-// dst[c][r] = src[r][c] through a 64 x 64 LDS tile (coalesced on both sides).
+// dst[c][r] = src[r][c] through a 64 x 64 LDS tile (coalesced on both sides);
+// dst rows are ldd elements apart.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T* __restrict__ dst,
-                                                  int rows, int cols) {
+                                                  int rows, int cols, int ldd) {
   __shared__ T buf[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -18,17 +19,21 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T*
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) dst[(size_t)c * rows + r] = buf[tx][i];
+    if (c < cols && r < rows) dst[(size_t)c * ldd + r] = buf[tx][i];
   }
 }
 
-hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int esize, hipStream_t s) {
+hipError_t launch_transpose_ld(const void* src, void* dst, int rows, int cols, int ldd, int esize, hipStream_t s) {
+  if (ldd < rows) return hipErrorInvalidValue;
   dim3 grid((cols + 63) / 64, (rows + 63) / 64);
   if (esize == 2)
-    ffn_launch(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src, (uint16_t*)dst, rows, cols);
+    ffn_launch(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src, (uint16_t*)dst, rows, cols, ldd);
   else
-    ffn_launch(k_transpose<float>, grid, dim3(256), 0, s, (const float*)src, (float*)dst, rows, cols);
+    ffn_launch(k_transpose<float>, grid, dim3(256), 0, s, (const float*)src, (float*)dst, rows, cols, ldd);
   return hipGetLastError();
+}
+hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int esize, hipStream_t s) {
+  return launch_transpose_ld(src, dst, rows, cols, rows, esize, s);
 }
 
 // One wave per neuron row of the neuron-major W_down^T [F x d]: the column

@@ -93,6 +93,7 @@ hipError_t dense_rows_bf16(const void* A, int nrows, int K, const void* x, int m
 
 // Transpose rows x cols (row-major) -> cols x rows, element size 2 or 4 bytes.
 hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int esize, hipStream_t s);
+hipError_t launch_transpose_ld(const void* src, void* dst, int rows, int cols, int ldd, int esize, hipStream_t s);
 // c[i] = || row i of the neuron-major matrix [F x d] ||_2 (fp32, correctly rounded sqrt).
 hipError_t launch_rownorm(const void* w, float* c, int F, int d, int dtype, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
@@ -342,6 +343,7 @@ struct BwDesc {
   int32_t* ent_tok; int32_t* ent_pos;   // neuron-major pairs: token, pair position
   float* du; float* dz;             // per pair position
   float* dxp;                       // [splits x m x d] fp32 partial dx rows (few tokens), or null
+  uint16_t* duz;                    // [m x 2F] bf16 rows (du | dz) for the matrix-core dx, or null
   long long pbase;
   float* dw_gate; float* dw_up; float* dw_down;   // [F x d] fp32, accumulated
 };
@@ -351,6 +353,10 @@ hipError_t launch_bw_scan(const BwDesc& d, hipStream_t s);
 hipError_t launch_bw_fill(const BwDesc& d, hipStream_t s);
 hipError_t launch_bw_neuron(const BwDesc& d, hipStream_t s);
 hipError_t launch_bw_dx(const BwDesc& d, hipStream_t s);
+hipError_t launch_bw_duz(const BwDesc& d, hipStream_t s);
+// From this many tokens (bf16) dx is a matrix-core GEMM of the dense (du | dz)
+// rows with [W_up; W_gate] instead of per-token row gathers.
+constexpr int kBwDxDenseMin = 512;
 // Splits of each token's neuron list in the dx kernel (more workgroups for
 // few tokens; at most kBwDxPartRows partial rows).
 constexpr int kBwDxMaxSplit = 16;

@@ -472,7 +472,7 @@ def bench_backward(args, dev):
             n_tot += n
             ms_tot += t
         if n_tot:
-            kernels[kind] = {"launches": n_tot, "avg_us": 1e3 * ms_tot / n_tot}
+            kernels[kind] = {"launches": n_tot, "avg_us": 1e3 * ms_tot / n_tot, "step_us": 1e3 * ms_tot / steps}
     for ffn, *_ in layers:
         ffn.timing_enable(False)
     fwd = None
@@ -522,7 +522,10 @@ def bench_backward(args, dev):
                    "active_pairs": pairs, "active_neurons": n_act, "routed_tokens": int(fwd["n_dense"]),
                    "layers_rotated": nl},
         "forward_ms_per_step": round(ms_fwd, 5),
-        "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
+        # per step: from 512 bf16 tokens the dx role is four launches (two
+        # weight transposes, the (du | dz) rows, the matrix-core GEMM)
+        "kernels_us": {k: round(v["step_us"], 3) for k, v in kernels.items()},
+        "launches_per_step": {k: round(v["launches"] / steps, 2) for k, v in kernels.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),

@@ -225,7 +225,11 @@ size_t ffn_sparse_backward_workspace_bytes(const ffn_sparse_config *cfg, int32_t
  *               rows of neurons active for some token change
  *   dw_down_nm  NULL or [d_ff x d_model] fp32 device: the gradient of W_down
  *               in neuron-major layout (row i = dW_down[:, i]), added to
- *   workspace   >= ffn_sparse_backward_workspace_bytes(cfg, m), 16-byte aligned
+ *   workspace   >= ffn_sparse_backward_workspace_bytes(cfg, m), 16-byte aligned;
+ *               from 512 tokens in bf16 it also holds [W_up; W_gate]
+ *               transposed (d_model x 2 d_ff) and the dense (du | dz) rows
+ *               (m x 2 d_ff), both bf16, for dx as one matrix-core GEMM
+ *               (du and dz rounded to bf16 there)
  * Every sum runs in a fixed order (tokens ascending per neuron), so the
  * result is reproducible run to run. FFN_E_UNSUPPORTED for other configs. */
 ffn_status ffn_sparse_backward(ffn_sparse_handle *h, const void *x, int32_t m, const float *bias,

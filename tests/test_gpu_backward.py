@@ -7,7 +7,9 @@ configs, a relative rounding of 2^-9 that enters du = dh a) and recomputes
 routed tokens' gate rows. Checked: dx per token, and every gradient row of
 W_up, W_gate and W_down (neuron-major) within the workload's relative L2
 bound of 5e-3; rows of neurons no token activates stay exactly zero; a
-second call adds the same values again (exact doubling).
+second call adds the same values again (exact doubling). From 512 tokens dx
+is a bf16 GEMM of the dense (du | dz) rows: du and dz rounded to bf16 add a
+relative error of about 2^-9 / sqrt(3) per token, inside the same bound.
 """
 from __future__ import annotations
 
@@ -41,7 +43,9 @@ def check_rows(got, ref, what):
 
 CASES = [("c1", 4, {}), ("c2", 5, dict(d=256, f=1024)), ("c2", 70, dict(d=256, f=1024)),
          ("c5", 40, dict(d=256, f=1024, T=256, E=16)), ("c2", 16, {}), ("c5", 200, dict(d=512, f=2048)),
-         ("c5", 256, {})]                                  # full width: d 2048, d_ff 8192, T 1024, E 128
+         ("c5", 256, {}),                                  # full width: d 2048, d_ff 8192, T 1024, E 128
+         # 512+ tokens: dx as a matrix-core GEMM of the dense (du | dz) rows
+         ("c2", 520, dict(d=256, f=1024)), ("c5", 600, dict(d=512, f=2048, T=256, E=32))]
 
 
 @pytest.mark.parametrize("cid,m,kw", CASES, ids=[f"{c}-m{m}-{i}" for i, (c, m, _) in enumerate(CASES)])

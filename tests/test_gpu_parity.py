@@ -70,6 +70,12 @@ REDUCED = [
     ("c3", 37, dict(d=256, f=1024, rank=32, T=64, E=8)),
     ("c4", 3, dict(d=512, f=1024, T=128, E=128)),
     ("c4", 18, dict(d=256, f=768, T=64, E=64)),
+    # top-k workgroups per token: 3 tiles (3 workgroups), 17 tiles over 16,
+    # 2 workgroups a token, 1 workgroup a token
+    ("c4", 1, dict(d=256, f=384, T=128, E=128)),
+    ("c4", 1, dict(d=256, f=1088, T=64, E=64)),
+    ("c4", 100, dict(d=256, f=640, T=64, E=64)),
+    ("c4", 300, dict(d=128, f=512, T=64, E=64)),
     ("c5", 67, dict(d=256, f=2048, T=256, E=32)),
     ("c5", 40, dict(d=128, f=1024, T=1024, E=128)),
 ]
