@@ -1665,11 +1665,23 @@ ffn_status ffn_sparse_backward(ffn_sparse_handle* h, const void* x, int32_t m, c
         ep.y = dx;
         ep.ldy = c.d_model;
         if (!plan_plain(g, h)) return FFN_E_UNSUPPORTED;
-        Timed tm(h, FFN_K_BW_DX, s);
-        e = launch_transpose_ld(h->w_up, wt, c.d_ff, c.d_model, 2 * c.d_ff, 2, s);
-        if (e == hipSuccess) e = launch_transpose_ld(h->w_gate, wt + c.d_ff, c.d_ff, c.d_model, 2 * c.d_ff, 2, s);
-        if (e == hipSuccess) e = launch_bw_duz(d, s);
-        if (e == hipSuccess) e = launch_gemm(g, ep, s);
+        // four launches, each timed under the dx role
+        {
+          Timed tm(h, FFN_K_BW_DX, s);
+          e = launch_transpose_ld(h->w_up, wt, c.d_ff, c.d_model, 2 * c.d_ff, 2, s);
+        }
+        if (e == hipSuccess) {
+          Timed tm(h, FFN_K_BW_DX, s);
+          e = launch_transpose_ld(h->w_gate, wt + c.d_ff, c.d_ff, c.d_model, 2 * c.d_ff, 2, s);
+        }
+        if (e == hipSuccess) {
+          Timed tm(h, FFN_K_BW_DX, s);
+          e = launch_bw_duz(d, s);
+        }
+        if (e == hipSuccess) {
+          Timed tm(h, FFN_K_BW_DX, s);
+          e = launch_gemm(g, ep, s);
+        }
       } else {
         Timed tm(h, FFN_K_BW_DX, s);
         e = launch_bw_dx(d, s);

@@ -460,7 +460,7 @@ def bench_backward(args, dev):
     ms_fwd = e0.elapsed_time(e1) / steps
 
     for ffn, *_ in layers:
-        ffn.timing_enable(True, capacity=steps + 8)
+        ffn.timing_enable(True, capacity=4 * steps + 8)   # up to four dx launches a step
     for i in range(steps):
         step(i)
     torch.cuda.synchronize()
