@@ -1644,27 +1644,29 @@ ffn_status ffn_sparse_backward(ffn_sparse_handle* h, const void* x, int32_t m, c
       Timed tm(h, FFN_K_BW_NEURON, s);
       e = launch_bw_neuron(d, s);
     }
+    GemmDesc gdx = gemm_base(h);
+    const bool dense_dx = dx && bw_dx_dense(c, m) && [&] {
+      gdx.A0 = w + L.wt;
+      gdx.nrows = c.d_model;
+      gdx.lda = 2 * c.d_ff;
+      gdx.K = 2 * c.d_ff;
+      gdx.B = w + L.duz;
+      gdx.ldb = 2 * c.d_ff;
+      gdx.M = m;
+      return plan_plain(gdx, h);
+    }();
     if (e == hipSuccess && dx) {
-      if (bw_dx_dense(c, m)) {
+      if (dense_dx) {
         // dx = (du | dz) [W_up; W_gate] on matrix cores: both weights
         // transposed side by side into [d x 2F], the dense rows, one GEMM
         uint16_t* wt = reinterpret_cast<uint16_t*>(w + L.wt);
         d.duz = reinterpret_cast<uint16_t*>(w + L.duz);
-        GemmDesc g = gemm_base(h);
-        g.A0 = wt;
-        g.nrows = c.d_model;
-        g.lda = 2 * c.d_ff;
-        g.K = 2 * c.d_ff;
-        g.B = d.duz;
-        g.ldb = 2 * c.d_ff;
-        g.M = m;
         EpiDesc ep{};
         ep.kind = EPI_Y;
         ep.F = c.d_model;
         ep.out_f32 = false;
         ep.y = dx;
         ep.ldy = c.d_model;
-        if (!plan_plain(g, h)) return FFN_E_UNSUPPORTED;
         // four launches, each timed under the dx role
         {
           Timed tm(h, FFN_K_BW_DX, s);
@@ -1680,7 +1682,7 @@ ffn_status ffn_sparse_backward(ffn_sparse_handle* h, const void* x, int32_t m, c
         }
         if (e == hipSuccess) {
           Timed tm(h, FFN_K_BW_DX, s);
-          e = launch_gemm(g, ep, s);
+          e = launch_gemm(gdx, ep, s);
         }
       } else {
         Timed tm(h, FFN_K_BW_DX, s);

@@ -380,6 +380,50 @@ def backward(wl, dy, fwd: dict | None = None) -> dict:
     }
 
 
+def backward_sampled(wl, dy, tokens, neurons) -> dict:
+    """The outputs of `backward` for a sample, by the same definitions: dx of
+    the given tokens, and the gradient rows of the given neurons. A token's
+    dx needs its own z, mask, u and dh over every neuron; a neuron's gradient
+    rows need that neuron's z, mask, u and dh over every token. The mask is
+    the bias / threshold rule on z (a routed token keeps the same mask: its
+    dense gate evaluates the same selection). [Sources as for `backward`.]
+    Returns dx [len(tokens), d], and for the neurons dw_gate, dw_up and
+    dw_down_nm (row i = dW_down[:, i]), each [len(neurons), d]."""
+    if wl.sel == SEL_TOPK or wl.w_gate is None or wl.act != RELU:
+        raise ValueError("the backward pass is defined here for a full-rank ReLU gate with a bias or threshold")
+    x = np.asarray(wl.x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    w_gate = np.asarray(wl.w_gate, dtype=np.float64)
+    w_up = np.asarray(wl.w_up, dtype=np.float64)
+    w_down = np.asarray(wl.w_down, dtype=np.float64)
+    b = wl.bias_per_token()
+    cut = np.zeros(wl.m) if wl.sel == SEL_BIAS else np.maximum(np.asarray(wl.tau, dtype=np.float64), 0.0)
+    tk = np.asarray(tokens, dtype=np.int64)
+    nr = np.asarray(neurons, dtype=np.int64)
+    # the sampled tokens over every neuron
+    z_t = gate_preactivation(x[tk], w_gate) + b[tk].reshape(-1, 1)
+    m_t = threshold_mask(z_t, cut[tk])
+    a_t = np.where(m_t, z_t, 0.0)
+    u_t = up_projection(x[tk], w_up)
+    dh_t = dy[tk] @ w_down
+    du_t = dh_t * a_t
+    dz_t = np.where(m_t, dh_t * u_t, 0.0)
+    # the sampled neurons over every token
+    z_n = gate_preactivation(x, w_gate[nr]) + b.reshape(-1, 1)
+    m_n = threshold_mask(z_n, cut)
+    a_n = np.where(m_n, z_n, 0.0)
+    u_n = up_projection(x, w_up[nr])
+    dh_n = dy @ w_down[:, nr]
+    du_n = dh_n * a_n
+    dz_n = np.where(m_n, dh_n * u_n, 0.0)
+    return {
+        "dx": du_t @ w_up + dz_t @ w_gate,
+        "dw_gate": dz_n.T @ x,
+        "dw_up": du_n.T @ x,
+        "dw_down_nm": (a_n * u_n).T @ dy,
+    }
+
+
 # ---------------------------------------------------------------------------
 # mixture of experts
 # ---------------------------------------------------------------------------

@@ -143,3 +143,24 @@ def test_backward_mutations_caught(monkeypatch, kind):
     assert _pins_pass()
     monkeypatch.setattr(O, "backward", _variant(kind))
     assert not _pins_pass()
+
+
+@pytest.mark.parametrize("cid,m,kw", SMALL)
+def test_backward_sampled_matches_autograd_and_full(cid, m, kw):
+    """The sampled evaluation used at full size equals autograd's rows (an
+    independent evaluation) and the full oracle's rows."""
+    wl = make_workload(cid, m, 0, **kw)
+    dy = draw_dy(wl, 3)
+    fwd = O.forward(wl)
+    ref = _autograd(wl, dy, fwd["mask"])
+    full = O.backward(wl, dy, fwd)
+    rng = np.random.default_rng(11)
+    tokens = np.sort(rng.choice(m, min(m, 3), replace=False))
+    neurons = np.sort(rng.choice(wl.f, 9, replace=False))
+    sm = O.backward_sampled(wl, dy, tokens, neurons)
+    assert _rel(sm["dx"], ref["dx"][tokens]) < 1e-12
+    assert _rel(sm["dw_gate"], ref["dw_gate"][neurons]) < 1e-12
+    assert _rel(sm["dw_up"], ref["dw_up"][neurons]) < 1e-12
+    assert _rel(sm["dw_down_nm"], ref["dw_down"][:, neurons].T) < 1e-12
+    assert _rel(sm["dx"], full["dx"][tokens]) < 1e-12
+    assert _rel(sm["dw_down_nm"], full["dw_down"][:, neurons].T) < 1e-12

@@ -7,7 +7,9 @@ configs, a relative rounding of 2^-9 that enters du = dh a) and recomputes
 routed tokens' gate rows. Checked: dx per token, and every gradient row of
 W_up, W_gate and W_down (neuron-major) within the workload's relative L2
 bound of 5e-3; rows of neurons no token activates stay exactly zero; a
-second call adds the same values again (exact doubling). From 512 tokens dx
+second call adds the same values again (exact doubling). At 4096 tokens the
+oracle evaluates a sample of tokens (routed ones among them) and neurons on
+its own (`backward_sampled`). From 512 tokens dx
 is a bf16 GEMM of the dense (du | dz) rows: du and dz rounded to bf16 add a
 relative error of about 2^-9 / sqrt(3) per token, inside the same bound.
 """
@@ -45,7 +47,8 @@ CASES = [("c1", 4, {}), ("c2", 5, dict(d=256, f=1024)), ("c2", 70, dict(d=256, f
          ("c5", 40, dict(d=256, f=1024, T=256, E=16)), ("c2", 16, {}), ("c5", 200, dict(d=512, f=2048)),
          ("c5", 256, {}),                                  # full width: d 2048, d_ff 8192, T 1024, E 128
          # 512+ tokens: dx as a matrix-core GEMM of the dense (du | dz) rows
-         ("c2", 520, dict(d=256, f=1024)), ("c5", 600, dict(d=512, f=2048, T=256, E=32))]
+         ("c2", 520, dict(d=256, f=1024)), ("c5", 600, dict(d=512, f=2048, T=256, E=32)),
+         ("c5", 4096, {})]                                 # the timed configuration: 4096 tokens, full width
 
 
 @pytest.mark.parametrize("cid,m,kw", CASES, ids=[f"{c}-m{m}-{i}" for i, (c, m, _) in enumerate(CASES)])
@@ -64,13 +67,27 @@ def test_backward_parity(cid, m, kw):
     kw2 = {k: v for k, v in sa.items() if k in ("bias", "bias_scalar", "tau")}
     dx = ffn.backward(x, to_dev(wl, dy), pack, dw_gate=dw["gate"], dw_up=dw["up"], dw_down_nm=dw["down"], **kw2)
     torch.cuda.synchronize()
-    ref = O.backward(wl, dy)
     if cid == "c5":
         assert int(pack.n_dense[0]) > 0                   # routed tokens take part
-    check_y(y_to_f64(wl, dx[:m]), ref["dx"], tol=TOL)
-    check_rows(dw["up"].cpu().numpy().astype(np.float64), ref["dw_up"], "dW_up")
-    check_rows(dw["gate"].cpu().numpy().astype(np.float64), ref["dw_gate"], "dW_gate")
-    check_rows(dw["down"].cpu().numpy().astype(np.float64), ref["dw_down"].T, "dW_down")
+    if m >= 2048:
+        # full size: sampled tokens (routed ones among them) and neurons, each
+        # output evaluated on its own by the oracle
+        rng = np.random.default_rng(5)
+        routed = pack.dense_list[:int(pack.n_dense[0])].cpu().numpy()
+        tokens = np.unique(np.concatenate([rng.choice(m, 56, replace=False), routed[:8]]))
+        neurons = np.sort(rng.choice(f, 192, replace=False))
+        ref = O.backward_sampled(wl, dy, tokens, neurons)
+        check_y(y_to_f64(wl, dx[:m])[tokens], ref["dx"], tol=TOL)
+        nt = torch.from_numpy(neurons).cuda()
+        check_rows(dw["up"][nt].cpu().numpy().astype(np.float64), ref["dw_up"], "dW_up")
+        check_rows(dw["gate"][nt].cpu().numpy().astype(np.float64), ref["dw_gate"], "dW_gate")
+        check_rows(dw["down"][nt].cpu().numpy().astype(np.float64), ref["dw_down_nm"], "dW_down")
+    else:
+        ref = O.backward(wl, dy)
+        check_y(y_to_f64(wl, dx[:m]), ref["dx"], tol=TOL)
+        check_rows(dw["up"].cpu().numpy().astype(np.float64), ref["dw_up"], "dW_up")
+        check_rows(dw["gate"].cpu().numpy().astype(np.float64), ref["dw_gate"], "dW_gate")
+        check_rows(dw["down"].cpu().numpy().astype(np.float64), ref["dw_down"].T, "dW_down")
     # accumulation: a second call adds the same values (exactly doubles them)
     first = {k: v.clone() for k, v in dw.items()}
     ffn.backward(x, to_dev(wl, dy), pack, dw_gate=dw["gate"], dw_up=dw["up"], dw_down_nm=dw["down"], **kw2)

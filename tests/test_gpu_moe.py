@@ -70,7 +70,7 @@ def test_moe_argument_errors():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("m,ne", [(1, 2), (4, 4)])
+@pytest.mark.parametrize("m,ne", [(1, 2), (4, 4), (8, 8)])   # (8, 8): the timed 8-token configuration
 def test_moe_full_size(m, ne):
     """Experts of the LoPA shape (d = 4096, d_ff = 14336, rank 512), top-2."""
     say("moe full size", m, ne)
