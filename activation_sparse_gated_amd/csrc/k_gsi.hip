@@ -196,6 +196,103 @@ __global__ __launch_bounds__(64 * kGsiResWaves) void k_gsi_resid(const GsiDesc d
   }
 }
 
+// The per-token gate, taken the same way by every workgroup of the output
+// kernel: the residual parts of every token (in LDS when they fit, else read
+// in place), each token's sums in a fixed order (lane order within a chunk of
+// 64 parts, chunks in order, the wave butterfly; one wave per token), then
+// rho = sqrt(rr) / sqrt(xx) and fast <=> rho < eps. Workgroup 0 also writes
+// rho, the slow-token list and its count. Returns the fast-token mask.
+__device__ __forceinline__ uint32_t gsi_decide(const GsiDesc& d, float* s_parts, float* s_rho) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int half = d.M * d.nres;                   // parts of the group's tokens, per kind
+  const bool in_lds = d.nres <= kGsiResParts;
+  if (in_lds) {
+    for (int q = threadIdx.x; q < 2 * half; q += blockDim.x) {
+      const int which = q >= half ? 1 : 0, off = which * (kGsiMaxM * d.nres) + (q - which * half);
+      s_parts[off] = d.part[off];
+    }
+    __syncthreads();
+  }
+  const float* src = in_lds ? s_parts : d.part;
+  for (int m = wave; m < d.M; m += nw) {
+    float ra = 0.f, xa = 0.f;
+    for (int p0 = 0; p0 < d.nres; p0 += 64) {
+      const int p = p0 + lane;
+      if (p < d.nres) {
+        ra += src[(size_t)m * d.nres + p];
+        xa += src[((size_t)kGsiMaxM + m) * d.nres + p];
+      }
+    }
+    ra = wave_sum(ra);
+    xa = wave_sum(xa);
+    if (lane == 0) s_rho[m] = xa > 0.f ? sqrtf(ra) / sqrtf(xa) : 0.f;     // x = 0: rho = 0
+  }
+  __syncthreads();
+  uint32_t fast = 0;
+  for (int m = 0; m < d.M; ++m)
+    if (s_rho[m] < d.eps) fast |= 1u << m;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    int n = d.tok0 > 0 ? *d.counter : 0;
+    for (int m = 0; m < d.M; ++m) {
+      if (d.rho) d.rho[d.tok0 + m] = s_rho[m];
+      if (!((fast >> m) & 1u)) {
+        if (d.slow_list) d.slow_list[n] = d.tok0 + m;
+        ++n;
+      }
+    }
+    *d.counter = n;
+    if (d.n_slow) *d.n_slow = n;
+  }
+  return fast;
+}
+
+// Slow tokens of the output kernel: y = W x, one wave per W row (rows
+// o0 + wave * rpw .. + rpw - 1): its chunks of 4096 inputs (8 x 16 bytes per
+// lane in flight), each chunk's dot with every slow token, the chunk totals
+// added in order into the wave's fp32 accumulators in LDS.
+template <int TQ>
+__device__ __forceinline__ void gsi_slow_rows(const GsiDesc& d, uint32_t slow, int o0, int rpw, float* yacc) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int P = (d.d + 511) / 512;
+  constexpr int SH = 6 - Log2<TQ>::value;
+  for (int q = 0; q < rpw; ++q) {
+    const int o = o0 + wave * rpw + q;
+    if (o >= d.dout) break;
+    const uint16_t* wr = d.w + (size_t)o * d.d;
+    if (lane < kGsiMaxM) yacc[lane] = 0.f;
+    for (int c0 = 0; c0 < P; c0 += 8) {
+      uint4 wv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int cc = (c0 + i) * 512 + lane * 8;
+        wv[i] = cc < d.d ? ldg16(wr + cc) : uint4{0, 0, 0, 0};
+      }
+      for (int m0 = 0; m0 < d.M; m0 += TQ) {
+        if (!((slow >> m0) & ((1u << TQ) - 1u))) continue;
+        float acc[TQ];
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) acc[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int cc = (c0 + i) * 512 + lane * 8;
+          if (cc < d.d) {
+#pragma unroll
+            for (int t = 0; t < TQ; ++t)
+              if ((slow >> (m0 + t)) & 1u)
+                acc[t] = dot8_bf(wv[i], ldg16(d.x + (size_t)(m0 + t) * d.d + cc), acc[t]);
+          }
+        }
+        WaveTRed<TQ, 32>::run(acc, lane);
+        if ((lane & ((1 << SH) - 1)) == 0) {
+          const int m = m0 + (lane >> SH);
+          if (m < kGsiMaxM) yacc[m] += acc[0];
+        }
+      }
+    }
+    if (lane < d.M && ((slow >> lane) & 1u)) d.y[(size_t)lane * d.dout + o] = (uint16_t)f2bf(yacc[lane]);
+  }
+}
+
 // ------------------------------------------------------------------ gate, then y = M g or W x
 // Every workgroup takes the same decision from the residual parts (the same
 // loads and sums in the same order); workgroup 0 also writes rho, the slow
@@ -230,50 +327,7 @@ __global__ __launch_bounds__(256) void k_gsi_out(const GsiDesc d) {
     }
   }
   const uint32_t all = (1u << d.M) - 1u;
-  uint32_t fast = 0;
-  if (!d.force_slow) {
-    // the parts of every token (in LDS when they fit, else read in place),
-    // then each token's sum: lane order within a chunk of 64 parts, chunks
-    // in order, the wave butterfly; one wave per token
-    const int half = d.M * d.nres;                 // parts of the group's tokens, per kind
-    const bool in_lds = d.nres <= kGsiResParts;
-    if (in_lds) {
-      for (int q = threadIdx.x; q < 2 * half; q += 256) {
-        const int which = q >= half ? 1 : 0, off = which * (kGsiMaxM * d.nres) + (q - which * half);
-        s_parts[off] = d.part[off];
-      }
-      __syncthreads();
-    }
-    const float* src = in_lds ? s_parts : d.part;
-    for (int m = wave; m < d.M; m += 4) {
-      float ra = 0.f, xa = 0.f;
-      for (int p0 = 0; p0 < d.nres; p0 += 64) {
-        const int p = p0 + lane;
-        if (p < d.nres) {
-          ra += src[(size_t)m * d.nres + p];
-          xa += src[((size_t)kGsiMaxM + m) * d.nres + p];
-        }
-      }
-      ra = wave_sum(ra);
-      xa = wave_sum(xa);
-      if (lane == 0) s_rho[m] = xa > 0.f ? sqrtf(ra) / sqrtf(xa) : 0.f;     // x = 0: rho = 0
-    }
-    __syncthreads();
-    for (int m = 0; m < d.M; ++m)
-      if (s_rho[m] < d.eps) fast |= 1u << m;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      int n = d.tok0 > 0 ? *d.counter : 0;
-      for (int m = 0; m < d.M; ++m) {
-        if (d.rho) d.rho[d.tok0 + m] = s_rho[m];
-        if (!((fast >> m) & 1u)) {
-          if (d.slow_list) d.slow_list[n] = d.tok0 + m;
-          ++n;
-        }
-      }
-      *d.counter = n;
-      if (d.n_slow) *d.n_slow = n;
-    }
-  }
+  const uint32_t fast = d.force_slow ? 0u : gsi_decide(d, s_parts, s_rho);
   const uint32_t slow = all & ~fast;
 
   if (fast) {
@@ -314,51 +368,86 @@ __global__ __launch_bounds__(256) void k_gsi_out(const GsiDesc d) {
     }
   }
 
-  if (slow) {
-    // one wave per W row: its chunks of 4096 inputs (8 x 16 bytes per lane in
-    // flight), each chunk's dot with every slow token, the chunk totals added
-    // in order into the wave's fp32 accumulators in LDS
-    const int rpw = rows_wg / 4;
-    const int P = (d.d + 511) / 512;
-    constexpr int SH = 6 - Log2<TQ>::value;
-    float* yacc = s_yacc[wave];
-    for (int q = 0; q < rpw; ++q) {
-      const int o = o0 + wave * rpw + q;
-      if (o >= d.dout) break;
-      const uint16_t* wr = d.w + (size_t)o * d.d;
-      if (lane < kGsiMaxM) yacc[lane] = 0.f;
-      for (int c0 = 0; c0 < P; c0 += 8) {
-        uint4 wv[8];
+  if (slow) gsi_slow_rows<TQ>(d, slow, o0, rows_wg / 4, s_yacc[wave]);
+}
+
+// The output kernel with 8..16 tokens on matrix cores: wave w owns 16 image
+// rows, one 16 x 16 tile of y over the tokens, y[o][m] = sum_c M[o][c] g[m][c]
+// as v_mfma_f32_16x16x32_bf16 steps over c with g split into bf16 hi + lo (two
+// products a step; the products are exact and summed in fp32). Operand lane
+// l holds image row l % 16 (A) or token l % 16 (B), elements 8 (l / 16) .. +7
+// of the step's 32; the image rows and g are loaded before the gate is taken.
+// g sits in LDS with rows padded by 4 floats, so the 16 tokens of a read fall
+// in distinct banks. Slow tokens take the same path as in k_gsi_out.
+__global__ __launch_bounds__(256) void k_gsi_out_mf(const GsiDesc d) {
+  extern __shared__ float4 s_dyn4[];
+  float* s_g = reinterpret_cast<float*>(s_dyn4);                 // [M x (k + 4)]
+  __shared__ float s_parts[2 * kGsiMaxM * kGsiResParts];
+  __shared__ float s_rho[kGsiMaxM];
+  __shared__ float s_yacc[4][kGsiMaxM];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int o0 = blockIdx.x * 64, ob = o0 + wave * 16;
+  const int steps = d.k / 32, ldg = d.k + 4;
+  uint4 aw[kGsiMaxK / 32];
+  {
+    const int orow = ob + r16;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int cc = (c0 + i) * 512 + lane * 8;
-          wv[i] = cc < d.d ? ldg16(wr + cc) : uint4{0, 0, 0, 0};
+    for (int j = 0; j < kGsiMaxK / 32; ++j)
+      aw[j] = (!d.force_slow && j < steps && orow < d.dout) ? ldg16(d.img + (size_t)orow * d.k + 32 * j + 8 * q)
+                                                             : uint4{0, 0, 0, 0};
+  }
+  // g of the group too, in the same round as the image rows (it does not
+  // depend on the gate): at most 16 x 512 floats, 8 float4 a thread
+  const int k4 = d.k / 4, n4 = d.M * k4;
+  float4 gq[kGsiMaxM * kGsiMaxK / 4 / 256];
+#pragma unroll
+  for (int u = 0; u < kGsiMaxM * kGsiMaxK / 4 / 256; ++u) {
+    const int p = threadIdx.x + 256 * u;
+    gq[u] = (!d.force_slow && p < n4) ? reinterpret_cast<const float4*>(d.g)[p] : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint32_t all = (1u << d.M) - 1u;
+  const uint32_t fast = d.force_slow ? 0u : gsi_decide(d, s_parts, s_rho);
+  const uint32_t slow = all & ~fast;
+
+  if (fast) {
+#pragma unroll
+    for (int u = 0; u < kGsiMaxM * kGsiMaxK / 4 / 256; ++u) {
+      const int p = threadIdx.x + 256 * u, m = p / k4, c = p - m * k4;
+      if (p < n4) *reinterpret_cast<float4*>(s_g + (size_t)m * ldg + 4 * c) = gq[u];
+    }
+    __syncthreads();
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float* gr = s_g + (size_t)min(r16, d.M - 1) * ldg + 8 * q;
+#pragma unroll
+    for (int j = 0; j < kGsiMaxK / 32; ++j) {
+      if (j < steps) {
+        const float4 g0 = *reinterpret_cast<const float4*>(gr + 32 * j);
+        const float4 g1 = *reinterpret_cast<const float4*>(gr + 32 * j + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = r16 < d.M ? gv[e] : 0.f;
+          hi[e] = f2bf(v);
+          lo[e] = f2bf(v - bf2f(hi[e]));
         }
-        for (int m0 = 0; m0 < d.M; m0 += TQ) {
-          if (!((slow >> m0) & ((1u << TQ) - 1u))) continue;
-          float acc[TQ];
-#pragma unroll
-          for (int t = 0; t < TQ; ++t) acc[t] = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int cc = (c0 + i) * 512 + lane * 8;
-            if (cc < d.d) {
-#pragma unroll
-              for (int t = 0; t < TQ; ++t)
-                if ((slow >> (m0 + t)) & 1u)
-                  acc[t] = dot8_bf(wv[i], ldg16(d.x + (size_t)(m0 + t) * d.d + cc), acc[t]);
-            }
-          }
-          WaveTRed<TQ, 32>::run(acc, lane);
-          if ((lane & ((1 << SH) - 1)) == 0) {
-            const int m = m0 + (lane >> SH);
-            if (m < kGsiMaxM) yacc[m] += acc[0];
-          }
-        }
+        const uint4 bh{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+        const uint4 bl{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw[j]), as_bf16x8(bh), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aw[j]), as_bf16x8(bl), acc, 0, 0, 0);
       }
-      if (lane < d.M && ((slow >> lane) & 1u)) d.y[(size_t)lane * d.dout + o] = (uint16_t)f2bf(yacc[lane]);
+    }
+    // lane l: rows ob + 4 (l / 16) + v, token l % 16
+    if (r16 < d.M && ((fast >> r16) & 1u)) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = ob + 4 * q + v;
+        if (o < d.dout) d.y[(size_t)r16 * d.dout + o] = (uint16_t)f2bf(acc[v]);
+      }
     }
   }
+  if (slow) gsi_slow_rows<4>(d, slow, o0, 16, s_yacc[wave]);
 }
 
 // ------------------------------------------------------------------ image M = W V_k (set-up)
@@ -479,8 +568,13 @@ hipError_t launch_gsi_out(const GsiDesc& d, hipStream_t s) {
   if (d.M < 1 || d.M > kGsiMaxM || d.out_nl < 1 || d.out_nl > kGsiMaxNl || d.nout < 1 || d.out_nl4 < 1 ||
       d.out_nl4 > 2 || d.nout4 < 1)
     return hipErrorInvalidValue;
-  const size_t lds = (size_t)d.M * d.k * 4;
   const dim3 blk(256);
+  if (group_maxm(d.M) >= 8 && d.k % 32 == 0) {
+    // 8..16 tokens: the matrix-core output kernel, 64 image rows a workgroup
+    ffn_launch(k_gsi_out_mf, dim3((d.dout + 63) / 64), blk, (size_t)d.M * (d.k + 4) * 4, s, d);
+    return hipGetLastError();
+  }
+  const size_t lds = (size_t)d.M * d.k * 4;
   switch (std::min(group_maxm(d.M), 4)) {
     case 1: ffn_launch((k_gsi_out<1, 1>), dim3(d.nout), blk, lds, s, d); break;
     case 2: ffn_launch((k_gsi_out<2, 1>), dim3(d.nout), blk, lds, s, d); break;
