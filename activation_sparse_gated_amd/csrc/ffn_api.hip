@@ -1693,11 +1693,33 @@ ffn_status ffn_sparse_backward(ffn_sparse_handle* h, const void* x, int32_t m, c
   });
 }
 
+namespace {
+// A TwELL pack for m tokens in `base` (the layout ffn_sparse_pack_bytes sizes).
+ffn_twell_pack carve_pack(char* base, const ffn_sparse_config& c, int m) {
+  const size_t nt = c.d_ff / c.tile_w, E = c.ell_w, es = esize_of(c.dtype);
+  ffn_twell_pack p{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    char* q = base + o;
+    o += align_up(bytes);
+    return q;
+  };
+  p.cnt = reinterpret_cast<int32_t*>(take((size_t)m * nt * 4));
+  p.idx = reinterpret_cast<uint16_t*>(take((size_t)m * nt * E * 2));
+  p.val = take((size_t)m * nt * E * es);
+  p.route = reinterpret_cast<uint8_t*>(take((size_t)m));
+  p.dense_list = reinterpret_cast<int32_t*>(take((size_t)m * 4));
+  p.n_dense = reinterpret_cast<int32_t*>(take(4));
+  return p;
+}
+}  // namespace
+
 size_t ffn_sparse_moe_workspace_bytes(const ffn_sparse_config* cfg, int32_t m, int32_t topk) {
   if (ffn_sparse_check_config(cfg) != FFN_OK || m < 1 || topk < 1 || (size_t)m * topk > (size_t)kMoeMaxPairs)
     return 0;
   const size_t np = (size_t)m * topk, rowb = (size_t)cfg->d_model * esize_of(cfg->dtype);
-  // + one single-token pack per pair for the grouped one-token launches
+  // + the grouped experts' own packs: one single-token pack per pair covers
+  // them (the pack size is subadditive in the token count)
   return 2 * align_up(np * rowb) + 2 * align_up(np * 4) + ffn_sparse_pack_bytes(cfg, m) +
          np * ffn_sparse_pack_bytes(cfg, 1);
 }
@@ -1777,49 +1799,76 @@ ffn_status ffn_sparse_moe_forward(ffn_sparse_handle* const* experts, int32_t n_e
   pk.n_dense = reinterpret_cast<int32_t*>(take(4));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (launch_moe_gather(md, s) != hipSuccess) return FFN_E_HIP;
-  // one token per active expert (decode): the experts' one-token kernels run
-  // as one launch each for all of them (grid.y = expert), each expert with its
-  // own pack; otherwise each expert runs its own sequence below
-  std::vector<int> act;
-  for (int e = 0; e < n_experts; ++e)
-    if (cnt[e]) act.push_back(e);
-  bool grouped = !dense;
-  std::vector<DecodeDesc> dds(act.size());
-  for (size_t a = 0; a < act.size() && grouped; ++a) {
-    const int e = act[a];
-    grouped = cnt[e] == 1 && plan_decode(experts[e], 1, &dds[a]) && dds[a].mode == DEC_PART;
-  }
-  if (grouped) {
-    const size_t pb1 = ffn_sparse_pack_bytes(&c, 1);
-    for (size_t a = 0; a < act.size(); ++a) {
-      const int e = act[a];
-      char* pbase = take(pb1);
-      ffn_twell_pack p1{};
-      p1.cnt = reinterpret_cast<int32_t*>(pbase);
-      p1.idx = reinterpret_cast<uint16_t*>(pbase + align_up(nt * 4));
-      p1.val = pbase + align_up(nt * 4) + align_up(nt * E * 2);
-      p1.route = reinterpret_cast<uint8_t*>(pbase + align_up(nt * 4) + align_up(nt * E * 2) + align_up(nt * E * esize_of(c.dtype)));
-      p1.dense_list = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p1.route) + align_up(1));
-      p1.n_dense = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p1.dense_list) + align_up(4));
-      DecodeDesc& d = dds[a];
-      d.x = static_cast<const char*>(md.xg) + (size_t)off[e] * rowb;
-      d.bias = bias ? md.bg + off[e] : nullptr;
-      d.bias_scalar = bias_scalar;
-      d.tau = tau ? md.tg + off[e] : nullptr;
-      d.cnt = p1.cnt;
-      d.idx = p1.idx;
-      d.val = p1.val;
-      d.g_debug = nullptr;
-      d.up = 1;
-      d.y = static_cast<char*>(const_cast<void*>(md.yg)) + (size_t)off[e] * rowb;
-      d.route_pass = 1;
-      d.route = route_desc(experts[e], 1, &p1);
+  // The active experts, grouped by their decode sequence: one-token experts
+  // (partial rows) and 2..8-token experts (the split sequence, planned for
+  // the group's largest count) run one launch per kernel for the whole group
+  // (grid.y or grid.z picks the expert), each expert with its own pack; any
+  // other expert runs its own sequence.
+  std::vector<int> one, multi, rest;
+  int mmax = 0;
+  for (int e = 0; e < n_experts; ++e) {
+    if (!cnt[e]) continue;
+    if (dense) rest.push_back(e);
+    else if (cnt[e] == 1) one.push_back(e);
+    else if (cnt[e] <= 8 && c.rank > 0) {
+      multi.push_back(e);
+      mmax = std::max(mmax, cnt[e]);
+    } else {
+      rest.push_back(e);
     }
-    ffn_sparse_handle* h0 = experts[act[0]];
-    for (size_t a0 = 0; a0 < act.size(); a0 += kDecGroupMax) {
-      const int n = (int)std::min<size_t>(kDecGroupMax, act.size() - a0);
+  }
+  std::vector<DecodeDesc> d1(one.size()), dm(multi.size());
+  bool g1 = !one.empty();
+  for (size_t a = 0; a < one.size() && g1; ++a)
+    g1 = plan_decode(experts[one[a]], 1, &d1[a]) && d1[a].mode == DEC_PART;
+  if (!g1) rest.insert(rest.end(), one.begin(), one.end());
+  bool gm = !multi.empty();
+  for (size_t a = 0; a < multi.size() && gm; ++a)
+    gm = experts[multi[a]]->cfg.max_m >= mmax && plan_decode(experts[multi[a]], mmax, &dm[a]) &&
+         dm[a].mode == DEC_SPLIT && dec_split_group_shape(dm[a]);
+  if (!gm) rest.insert(rest.end(), multi.begin(), multi.end());
+  // the expert's rows, selection inputs, own pack and output rows
+  auto bind = [&](DecodeDesc& d, int e) {
+    const ffn_twell_pack pe = carve_pack(take(ffn_sparse_pack_bytes(&c, cnt[e])), c, cnt[e]);
+    d.M = cnt[e];
+    d.x = static_cast<const char*>(md.xg) + (size_t)off[e] * rowb;
+    d.bias = bias ? md.bg + off[e] : nullptr;
+    d.bias_scalar = bias_scalar;
+    d.tau = tau ? md.tg + off[e] : nullptr;
+    d.cnt = pe.cnt;
+    d.idx = pe.idx;
+    d.val = pe.val;
+    d.g_debug = nullptr;
+    d.up = 1;
+    d.y = static_cast<char*>(const_cast<void*>(md.yg)) + (size_t)off[e] * rowb;
+    d.route_pass = 1;
+    d.route = route_desc(experts[e], cnt[e], &pe);
+  };
+  auto fail = [&](const std::vector<int>& ids, size_t a0, int n) {
+    for (int i = 0; i < n; ++i) experts[ids[a0 + i]]->failed = true;
+    return FFN_E_HIP;
+  };
+  if (gm) {
+    for (size_t a = 0; a < multi.size(); ++a) bind(dm[a], multi[a]);
+    ffn_sparse_handle* h0 = experts[multi[0]];
+    for (size_t a0 = 0; a0 < multi.size(); a0 += kDecGroupMax) {
+      const int n = (int)std::min<size_t>(kDecGroupMax, multi.size() - a0);
       DecGroup g{};
-      for (int i = 0; i < n; ++i) g.d[i] = dds[a0 + i];
+      for (int i = 0; i < n; ++i) g.d[i] = dm[a0 + i];
+      static const int kind[4] = {FFN_K_LOWRANK_V, FFN_K_GATE, FFN_K_UP, FFN_K_UPDOWN};
+      for (int stage = 0; stage < 4; ++stage) {
+        Timed tm(h0, kind[stage], s);
+        if (launch_dec_split_group(g, n, stage, s) != hipSuccess) return fail(multi, a0, n);
+      }
+    }
+  }
+  if (g1) {
+    for (size_t a = 0; a < one.size(); ++a) bind(d1[a], one[a]);
+    ffn_sparse_handle* h0 = experts[one[0]];
+    for (size_t a0 = 0; a0 < one.size(); a0 += kDecGroupMax) {
+      const int n = (int)std::min<size_t>(kDecGroupMax, one.size() - a0);
+      DecGroup g{};
+      for (int i = 0; i < n; ++i) g.d[i] = d1[a0 + i];
       hipError_t err = hipSuccess;
       if (c.rank) {
         Timed tm(h0, FFN_K_LOWRANK_V, s);
@@ -1833,16 +1882,13 @@ ffn_status ffn_sparse_moe_forward(ffn_sparse_handle* const* experts, int32_t n_e
         Timed tm(h0, FFN_K_UPDOWN, s);
         err = launch_dec_reduce_group(g, n, s);
       }
-      if (err != hipSuccess) {
-        for (int i = 0; i < n; ++i) experts[act[a0 + i]]->failed = true;
-        return FFN_E_HIP;
-      }
+      if (err != hipSuccess) return fail(one, a0, n);
     }
-    return hip_status(launch_moe_combine(md, s));
   }
-  // each expert's sparse forward pass on its rows, in expert order
-  for (int e = 0; e < n_experts; ++e) {
-    if (!cnt[e]) continue;
+  // every other expert's forward pass on its rows, in expert order, with the
+  // shared pack
+  std::sort(rest.begin(), rest.end());
+  for (const int e : rest) {
     const char* xe = static_cast<const char*>(md.xg) + (size_t)off[e] * rowb;
     void* ye = static_cast<char*>(const_cast<void*>(md.yg)) + (size_t)off[e] * rowb;
     const float* be = bias ? md.bg + off[e] : nullptr;

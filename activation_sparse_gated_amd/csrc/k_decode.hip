@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * kDecVWaves) void k_dec_lowrank_grp(const DecGr
 constexpr int kLrMaxWaves = 16;
 constexpr int kLrMaxSteps = 8;                        // 32-element steps per wave
 
-__global__ __launch_bounds__(64 * kLrMaxWaves) void k_dec_lowrank_mf(const DecodeDesc d) {
+__device__ __forceinline__ void dec_lowrank_mf_body(const DecodeDesc& d) {
   __shared__ f32x4_t s_acc[kLrMaxWaves][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15, M = d.M, dm = d.d, z = blockIdx.y;
@@ -337,6 +337,8 @@ __global__ __launch_bounds__(64 * kLrMaxWaves) void k_dec_lowrank_mf(const Decod
           float4{t[0], t[1], t[2], t[3]};
   }
 }
+__global__ __launch_bounds__(64 * kLrMaxWaves) void k_dec_lowrank_mf(const DecodeDesc d) { dec_lowrank_mf_body(d); }
+__global__ __launch_bounds__(64 * kLrMaxWaves) void k_dec_lowrank_mf_grp(const DecGroup g) { dec_lowrank_mf_body(g.d[blockIdx.z]); }
 
 // Waves per workgroup of the matrix-core first stage for S slices of d (0: no
 // shape fits): the fewest of 4, 8, 16 whose wave slices take at most
@@ -887,7 +889,7 @@ constexpr int kUpMaxEnt = 128;                         // entries per workgroup 
 // count on hold -1 (no row)
 constexpr int kUpNrnSlots = (kUpMaxEnt + 16 * kUpNB - 1) / (16 * kUpNB) * (16 * kUpNB);
 
-__global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
+__device__ __forceinline__ void dec_up_body(const DecodeDesc& d) {
   extern __shared__ uint4 s_dyn[];                     // x: M rows of d + 8 bf16; masks; prefixes
   __shared__ int s_scan[kUpWaves];
   __shared__ int s_nrn[kUpNrnSlots];
@@ -1036,6 +1038,8 @@ __global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) {
     __syncthreads();
   }
 }
+__global__ __launch_bounds__(64 * kUpWaves) void k_dec_up(const DecodeDesc d) { dec_up_body(d); }
+__global__ __launch_bounds__(64 * kUpWaves) void k_dec_up_grp(const DecGroup g) { dec_up_body(g.d[blockIdx.y]); }
 
 // ------------------------------------------------------------------ k_dec_down2 (split mode)
 // y[token, :] = sum over the list of h[token, e] W_down[:, n_e], as MFMA tiles
@@ -1060,7 +1064,7 @@ constexpr int kDown2MaxIds = 2048;                     // list entries per workg
 __device__ __forceinline__ int dn_slot(int row, int c) { return row * 8 + (c ^ ((row & 3) << 1)); }
 typedef short dn_v4s __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kDown2Threads) void k_dec_down2(const DecodeDesc d) {
+__device__ __forceinline__ void dec_down2_body(const DecodeDesc& d) {
   constexpr int NW = kDown2Threads / 64;
   __shared__ uint4 s_w[NW][2][32 * 8];                 // per wave: two blocks of 32 rows x 128 bytes
   __shared__ int s_ids[kDown2MaxIds];
@@ -1146,10 +1150,12 @@ __global__ __launch_bounds__(kDown2Threads) void k_dec_down2(const DecodeDesc d)
           float4{s[0], s[1], s[2], s[3]};
   }
 }
+__global__ __launch_bounds__(kDown2Threads) void k_dec_down2(const DecodeDesc d) { dec_down2_body(d); }
+__global__ __launch_bounds__(kDown2Threads) void k_dec_down2_grp(const DecGroup g) { dec_down2_body(g.d[blockIdx.y]); }
 
 // y = sum of the S group partials in group order; the extra last workgroup
 // routes the pack.
-__global__ __launch_bounds__(256) void k_dec_reduce2(const DecodeDesc d) {
+__device__ __forceinline__ void dec_reduce2_body(const DecodeDesc& d) {
   const int n = d.M * d.d;
   if (d.route_pass && (int)blockIdx.x == (n + 1023) / 1024) {
     route_pass(d.route);
@@ -1168,6 +1174,8 @@ __global__ __launch_bounds__(256) void k_dec_reduce2(const DecodeDesc d) {
   uint16_t* y = reinterpret_cast<uint16_t*>(d.y) + i0;
   *reinterpret_cast<uint2*>(y) = uint2{f2bf(acc.x) | (f2bf(acc.y) << 16), f2bf(acc.z) | (f2bf(acc.w) << 16)};
 }
+__global__ __launch_bounds__(256) void k_dec_reduce2(const DecodeDesc d) { dec_reduce2_body(d); }
+__global__ __launch_bounds__(256) void k_dec_reduce2_grp(const DecGroup g) { dec_reduce2_body(g.d[blockIdx.y]); }
 
 // ------------------------------------------------------------------ launches
 static int pow2_pieces(int K) {
@@ -1467,6 +1475,89 @@ hipError_t launch_dec_reduce_group(const DecGroup& g, int n, hipStream_t s) {
     return hipErrorInvalidValue;
   ffn_launch(k_dec_reduce_grp<1>, dim3(d.d / 32 + (d.route_pass ? 1 : 0), n), dim3(kRedThreads), 0, s, g);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ grouped split-sequence launches
+// The same for FFNs of one shape with 2..8 tokens each, planned for the
+// group's largest token count (so every descriptor shares the launch shape:
+// sub-tile rows, pieces, slabs, entry groups) and each carrying its own count.
+// Whether a split-sequence plan has the one shape the grouped gate is built
+// for (low rank 512, 64-row sub-tiles of 8 pieces) and the other stages fit.
+bool dec_split_group_shape(const DecodeDesc& d) {
+  return d.rank > 0 && d.K == 512 && d.ipw == 8 && d.R == 64 && d.nslab > 0 && d.rank % 16 == 0 &&
+         lowrank_mf_waves(d.d, d.nslab) != 0 && d.d % 64 == 0 && d.T % d.R == 0 && d.F % d.R == 0 &&
+         d.T / d.R <= 64 && dec_split_ok(d);
+}
+
+static bool split_group_ok(const DecGroup& g, int n) {
+  if (n < 1 || n > kDecGroupMax) return false;
+  const DecodeDesc& a = g.d[0];
+  for (int i = 0; i < n; ++i) {
+    const DecodeDesc& b = g.d[i];
+    if (b.M < 2 || b.M > 8 || b.mode != DEC_SPLIT || !b.up || b.d != a.d || b.F != a.F || b.T != a.T ||
+        b.K != a.K || b.rank != a.rank || b.R != a.R || b.ipw != a.ipw || b.nslab != a.nslab ||
+        b.ngroups != a.ngroups || b.ldh != a.ldh || !dec_split_ok(b))
+      return false;
+  }
+  return dec_split_group_shape(a);
+}
+static int group_maxm_of(const DecGroup& g, int n) {
+  int mx = 1;
+  for (int i = 0; i < n; ++i) mx = std::max(mx, g.d[i].M);
+  return dec_maxm(mx);
+}
+
+hipError_t launch_dec_split_group(const DecGroup& g, int n, int stage, hipStream_t s) {
+  if (!split_group_ok(g, n)) return hipErrorInvalidValue;
+  const DecodeDesc& d = g.d[0];
+  const int maxm = group_maxm_of(g, n);
+  if (stage == 0) {                                    // t = V x on matrix cores, nslab slabs each
+    const int nwv = lowrank_mf_waves(d.d, d.nslab);
+    if (nwv == 0 || d.rank % 16 != 0) return hipErrorInvalidValue;
+    ffn_launch(k_dec_lowrank_mf_grp, dim3(d.rank / 16, d.nslab, n), dim3(64 * nwv), 0, s, g);
+    return hipGetLastError();
+  }
+  if (stage == 1) {                                    // gate, selection, pack, union activations
+    if (d.ipw != 8 || d.K != 512 || d.R != 64 || d.T % d.R != 0 || d.F % d.R != 0 || d.T / d.R > 64)
+      return hipErrorInvalidValue;
+    size_t lds = 0;
+    for (int i = 0; i < n; ++i) {
+      DecodeDesc t = g.d[i];
+      t.M = maxm;
+      lds = std::max(lds, dec_gate_lds(t));
+    }
+    auto go = [&](auto kern) -> hipError_t {
+      hipError_t e = lds_attr(kern, lds);
+      if (e != hipSuccess) return e;
+      ffn_launch(kern, dim3(d.F / d.R, n), dim3(64 * dec_gate_waves(maxm)), lds, s, g);
+      return hipGetLastError();
+    };
+    switch (maxm) {
+      case 2: return go(k_dec_gate_grp<dec_gate_waves(2), 8, 2, true, DEC_SPLIT>);
+      case 4: return go(k_dec_gate_grp<dec_gate_waves(4), 8, 4, true, DEC_SPLIT>);
+      case 8: return go(k_dec_gate_grp<dec_gate_waves(8), 8, 8, true, DEC_SPLIT>);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (stage == 2) {                                    // up products of the union list
+    size_t lds = 0;
+    for (int i = 0; i < n; ++i) lds = std::max(lds, dec_up_lds(g.d[i]));
+    hipError_t e = lds_attr(k_dec_up_grp, lds);
+    if (e != hipSuccess) return e;
+    ffn_launch(k_dec_up_grp, dim3(kUpGrid, n), dim3(64 * kUpWaves), lds, s, g);
+    return hipGetLastError();
+  }
+  if (stage == 3) {                                    // down products, then the ordered group sum
+    if (d.d % 64 != 0) return hipErrorInvalidValue;
+    ffn_launch(k_dec_down2_grp, dim3(d.d / 64 * d.ngroups, n), dim3(kDown2Threads), 0, s, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int nmax = 0;
+    for (int i = 0; i < n; ++i) nmax = std::max(nmax, g.d[i].M * g.d[i].d);
+    ffn_launch(k_dec_reduce2_grp, dim3((nmax + 1023) / 1024 + 1, n), dim3(256), 0, s, g);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ffn

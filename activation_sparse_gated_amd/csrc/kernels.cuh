@@ -278,6 +278,11 @@ struct DecGroup {
   DecodeDesc d[kDecGroupMax];
 };
 static_assert(sizeof(DecGroup) <= 4096, "kernel arguments are limited to 4 KiB");
+// The split sequence for a group of FFNs of one shape with 2..8 tokens each
+// (stage 0: t = V x; 1: the gate; 2: the up products; 3: the down products
+// and the ordered sum, whose extra workgroup routes each FFN's pack).
+hipError_t launch_dec_split_group(const DecGroup& g, int n, int stage, hipStream_t s);
+bool dec_split_group_shape(const DecodeDesc& d);
 hipError_t launch_dec_lowrank_group(const DecGroup& g, int n, hipStream_t s);
 hipError_t launch_dec_gate_group(const DecGroup& g, int n, hipStream_t s);
 hipError_t launch_dec_reduce_group(const DecGroup& g, int n, hipStream_t s);

@@ -40,6 +40,23 @@ SMALL = dict(d=256, f=1024, rank=32, T=64, E=64)
 CASES = [(6, 4, 2, 0), (9, 3, 3, 1), (5, 1, 1, 2), (16, 8, 2, 3), (40, 4, 1, 4)]
 
 
+# experts of rank 512 (the shape the grouped split sequence is built for):
+# 2..8 tokens per expert run as one group, one-token experts as another, and
+# experts with more tokens alone
+LR512 = dict(d=1024, f=2048, rank=512, T=128, E=64)
+CASES512 = [(8, 8, 2, 5), (12, 4, 2, 6), (20, 4, 2, 7), (3, 8, 2, 8)]
+
+
+@pytest.mark.parametrize("m,ne,k,seed", CASES512, ids=[f"r512-m{c[0]}-e{c[1]}-top{c[2]}" for c in CASES512])
+def test_moe_grouped_sequences(m, ne, k, seed):
+    say("moe grouped", m, ne, k, seed)
+    mw = make_moe(m, n_experts=ne, topk=k, seed=seed, **LR512)
+    counts = [wl.m for wl in mw.experts]
+    say("tokens per expert", counts)
+    _, _, _, y = run_moe(mw)
+    check_y(y, O.moe_forward(mw)["y"])
+
+
 @pytest.mark.parametrize("m,ne,k,seed", CASES, ids=[f"m{c[0]}-e{c[1]}-top{c[2]}" for c in CASES])
 def test_moe_parity_small(m, ne, k, seed):
     say("moe small", m, ne, k, seed)
