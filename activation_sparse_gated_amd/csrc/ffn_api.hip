@@ -1005,7 +1005,13 @@ UpdownDesc updown_desc(const ffn_sparse_handle* h, const void* x, int m, const f
       if (!fit && wg <= 2LL * h->cus) fit = g;
       if (!aligned && groups(g) % 8 == 0 && wg <= 2LL * h->cus) aligned = g;
     }
+    // Beyond two workgroups per CU, eight groups (one per XCD) still win up to
+    // three per CU, against the finest fitting grouping whose groups spread
+    // over every XCD (LoPA, 72 tokens: 281 against 320 us, 96 tokens: 299
+    // against 380 us; at 112 and 128 tokens four groups, which fit, are faster)
+    const int g8 = (ntiles + 7) / 8;
     if (aligned && (long long)m * groups(aligned) * 2 >= 3LL * h->cus) G = aligned;
+    else if (!aligned && g8 <= gcap && groups(g8) == 8 && 8LL * m <= 3LL * h->cus && 16LL * m >= 3LL * h->cus) G = g8;
     else G = fit ? fit : gcap;
   }
   if (h->tune.ud_group > 0) G = std::min(gcap, h->tune.ud_group);

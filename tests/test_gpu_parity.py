@@ -76,6 +76,10 @@ REDUCED = [
     ("c4", 1, dict(d=256, f=1088, T=64, E=64)),
     ("c4", 100, dict(d=256, f=640, T=64, E=64)),
     ("c4", 300, dict(d=128, f=512, T=64, E=64)),
+    # the general path past two workgroups per CU: eight XCD-aligned tile
+    # groups (90 tokens), then four (110 tokens)
+    ("c3", 90, dict(d=512, f=2048, rank=64, T=128, E=64)),
+    ("c3", 110, dict(d=512, f=2048, rank=64, T=128, E=64)),
     ("c5", 67, dict(d=256, f=2048, T=256, E=32)),
     ("c5", 40, dict(d=128, f=1024, T=1024, E=128)),
 ]
