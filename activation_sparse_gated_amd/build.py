@@ -9,7 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libffn_sparse.so")
-SOURCES = ["ffn_api.hip", "k_gate.hip", "k_dense.hip", "k_updown.hip", "k_topk.hip", "k_misc.hip", "k_decode.hip", "k_prefill.hip", "k_xcd.hip", "k_sgemv.hip", "k_input.hip", "k_gsi.hip", "gsi_api.hip", "k_moe.hip", "k_backward.hip"]
+SOURCES = ["ffn_api.hip", "k_gate.hip", "k_dense.hip", "k_updown.hip", "k_topk.hip", "k_misc.hip", "k_decode.hip", "k_prefill.hip", "k_xcd.hip", "k_sgemv.hip", "k_input.hip", "k_gsi.hip", "gsi_api.hip", "k_moe.hip", "k_backward.hip", "k_skinny.hip"]
 # -packed-fp32-ops off: no v_pk_*_f32 in generated code
 HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -678,6 +678,10 @@ hipError_t run_dense_down(ffn_sparse_handle* h, int m, const int32_t* list, cons
   g.M = m;
   g.m_dev = m_dev;
   if (!plan_plain(g, h)) return hipErrorInvalidValue;
+  // K-split partial slabs of the skinny kernel: the sparse kernel's partial-row
+  // buffer, which no kernel of a dense down product's call uses
+  g.skpart = h->ws.ud_partial;
+  g.skpart_rows = (int)std::min<size_t>(h->ws.ud_rows, 1 << 20);
   EpiDesc e{};
   e.kind = EPI_Y;
   e.F = c.d_model;

@@ -642,6 +642,10 @@ inline dim3 gemm_grid(const GemmDesc& g) {
 bool pf_ok(const GemmDesc& g, const EpiDesc& e);
 hipError_t launch_gemm_pf(const GemmDesc& g, const EpiDesc& e, hipStream_t s);
 
+// skinny GEMM (k_skinny.hip): 16..64-token blocks, the token tile in LDS
+bool sk_ok(const GemmDesc& g, const EpiDesc& e);
+hipError_t launch_gemm_sk(const GemmDesc& g, const EpiDesc& e, hipStream_t s);
+
 // entry points per epilogue group (each in its own translation unit)
 hipError_t launch_gemm_pack(const GemmDesc& g, const EpiDesc& e, hipStream_t s);    // STORE_F32, TWELL
 hipError_t launch_gemm_dense(const GemmDesc& g, const EpiDesc& e, hipStream_t s);   // WINA, DENSE_H, Y

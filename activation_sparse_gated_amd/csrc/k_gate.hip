@@ -22,6 +22,7 @@ hipError_t launch_gemm_pack(const GemmDesc& g, const EpiDesc& e, hipStream_t s) 
 hipError_t launch_gemm(const GemmDesc& g, const EpiDesc& e, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   if (pf_ok(g, e) && !g.no_pf) return launch_gemm_pf(g, e, s);
+  if (sk_ok(g, e)) return launch_gemm_sk(g, e, s);
   if (g.nwaves != 4 && g.nwaves != 16) return hipErrorInvalidValue;
   if (e.kind == EPI_STORE_F32 || e.kind == EPI_TWELL) return launch_gemm_pack(g, e, s);
   return launch_gemm_dense(g, e, s);

@@ -57,6 +57,11 @@ struct GemmDesc {
   // slice z of K writes fp32 partials kpart[(z * kpart_m + m) * nrows + n]
   float* kpart;
   int kpart_m;
+  // skinny kernel (9..127 tokens, output rows y): K may be split over
+  // workgroups whose fp32 partial slabs [ks x M x nrows] go here, at most
+  // skpart_rows = ks * M rows; null: no K split
+  float* skpart;
+  int skpart_rows;
 };
 
 struct EpiDesc {
