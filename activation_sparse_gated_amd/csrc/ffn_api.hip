@@ -119,6 +119,13 @@ int pick_mt(int m) { return m <= 16 ? 16 : (m <= 32 ? 32 : 64); }
 // routed tokens (no extra launches); larger counts use the dense backup GEMMs.
 constexpr int kDecodeMaxM = 64;
 
+// Token counts of the masked dense sequence: above the decode kernels' 16
+// tokens the union of the tokens' active neurons covers most rows (at 10%
+// density, 1 - 0.9^17 = 83%; 97% at 32 tokens), so a sparse pass cannot read
+// fewer weight bytes than the dense products, and below the prefill shapes
+// (128 tokens) the products are weight streams.
+constexpr int kMaskedDenseMaxM = 127;
+
 struct Workspace {
   uint32_t* ctrl;       // kCtrlWords control words + kTicketWords tickets
   void* wdown_alt;      // the W_down layout the caller did not pass
@@ -177,7 +184,10 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
   w.colnorm = (float*)take(F * sizeof(float));
   w.lr_slabs = (float*)take(std::max<size_t>(1, kMaxSlabs * M * r) * sizeof(float));
   w.lr_t = (float*)take(std::max<size_t>(1, M * r) * sizeof(float));
-  w.g_ext = (float*)take(r ? M * F * sizeof(float) : 16);
+  // gate values [tokens x F] fp32: the dense paths of a low-rank gate, and
+  // the masked dense sequence (17..127 tokens; see masked_dense_ok)
+  const bool md = c.dtype == FFN_BF16 && c.sel != FFN_SEL_TOPK_WINA && c.in_keep == 0 && M > (size_t)kDecMaxM;
+  w.g_ext = (float*)take(r ? M * F * sizeof(float) : (md ? std::min<size_t>(M, kMaskedDenseMaxM) * F * sizeof(float) : 16));
   const bool topk = c.sel == FFN_SEL_TOPK_WINA;
   w.wina_s = (float*)take(topk ? M * F * sizeof(float) : 16);
   w.wina_h = (float*)take(topk ? M * F * sizeof(float) : 16);
@@ -253,7 +263,8 @@ int device_cus() {
 // organisation), FFN_SPARSE_NO_PREFILL_GEMM (1: the decode-shaped MFMA kernel
 // for 128+ tokens as well), FFN_SPARSE_NO_TOPK_DOWN (1: top-k selection's down
 // product through the per-token TwELL kernel), FFN_SPARSE_NO_XCD (1: the
-// per-token sparse kernel at prefill token counts too).
+// per-token sparse kernel at prefill token counts too),
+// FFN_SPARSE_NO_MASKED_DENSE (1: the general sequence at 17..127 tokens).
 // Launch-shape overrides for tuning exist only in a library compiled with
 // -DFFN_SPARSE_TUNING (FFN_SPARSE_GATE_NT, _GATE_WAVES, _UD_SPLIT, _UD_GROUP,
 // _UD_WAVES, _V_KS, _NO_GEMV, _LR_SLABS, _DEC_IPW, _UD_ORDER); the product
@@ -262,7 +273,7 @@ int device_cus() {
 // summation order.
 struct Tuning {
   int gate_nt = 0, gate_waves = 0, ud_split = 0, ud_group = 0, ud_waves = 0, v_ks = 0, no_gemv = 0, no_decode = 0, dec_mode = 0, no_pf = 0,
-      no_topk_down = 0, no_xcd = 0, lr_slabs = 0, dec_ipw = 0, ud_order = 0;
+      no_topk_down = 0, no_xcd = 0, lr_slabs = 0, dec_ipw = 0, ud_order = 0, no_masked_dense = 0;
 };
 
 static int env_int(const char* name) {
@@ -536,7 +547,7 @@ void b_from_slabs(GemmDesc& g, const ffn_sparse_handle* h, int nslabs) {
 // `list` is set (dense backup) with the device count m_dev.
 hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const int32_t* list,
                             const int32_t* m_dev, const float* bias, float bias_scalar,
-                            const float* tau, int kind, hipStream_t s) {
+                            const float* tau, int kind, hipStream_t s, bool keep_g = false, int gate_kind = -1) {
   const auto& c = h->cfg;
   if (one_token_stream(h, m, list, m_dev)) {
     // one token: the up rows with the gate rows (W_gate with x, or U with
@@ -585,6 +596,7 @@ hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const in
     g.K = c.d_model;
     g.B = x;
     g.ldb = c.d_model;
+    if (keep_g) e.g_debug = h->ws.g_ext;           // the gate values [m x F], for a pack built from them
     if (!plan_plain(g, h)) return hipErrorInvalidValue;
     Timed tm(h, kind, s);
     return launch_gemm(g, e, s);
@@ -609,7 +621,7 @@ hipError_t run_dense_hidden(ffn_sparse_handle* h, const void* x, int m, const in
     eg.F = c.d_ff;
     eg.out = h->ws.g_ext;
     eg.ldo = c.d_ff;
-    Timed tm(h, kind, s);
+    Timed tm(h, gate_kind >= 0 ? gate_kind : kind, s);
     err = launch_gemm(gu, eg, s);
     if (err != hipSuccess) return err;
   }
@@ -1196,6 +1208,7 @@ ffn_status ffn_sparse_init(const ffn_sparse_config* cfg, const void* w_gate_or_u
   h->tune.no_pf = env_int("FFN_SPARSE_NO_PREFILL_GEMM");
   h->tune.no_topk_down = env_int("FFN_SPARSE_NO_TOPK_DOWN");
   h->tune.no_xcd = env_int("FFN_SPARSE_NO_XCD");
+  h->tune.no_masked_dense = env_int("FFN_SPARSE_NO_MASKED_DENSE");
 #ifdef FFN_SPARSE_TUNING
   h->tune.gate_nt = env_int("FFN_SPARSE_GATE_NT");
   h->tune.gate_waves = env_int("FFN_SPARSE_GATE_WAVES");
@@ -1332,6 +1345,50 @@ static int topk_down_kind(const ffn_sparse_handle* h, int m) {
   return (m == 1 && topk_list_desc(h, nullptr, &ld)) ? 1 : 2;
 }
 
+// The masked dense sequence (bf16 bias / threshold selection, 17..127
+// tokens): the dense hidden activations h = a(z) * (W_up x) with the
+// selection applied to every neuron, the gate values kept in g_ext; the TwELL
+// pack built from those same gate values (so the pack and y take the same
+// decisions); the route pass; a dense down GEMM. Every token is evaluated this
+// way, routed or not.
+static bool masked_dense_ok(const ffn_sparse_handle* h, int m) {
+  const auto& c = h->cfg;
+  return c.dtype == FFN_BF16 && c.sel != FFN_SEL_TOPK_WINA && c.in_keep == 0 && !h->tune.no_masked_dense &&
+         m > kDecMaxM && m <= kMaskedDenseMaxM && m <= c.max_m;
+}
+
+static ffn_status masked_dense_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
+                                       float bias_scalar, const float* tau, ffn_twell_pack* pack, void* y,
+                                       hipStream_t s) {
+  const auto& c = h->cfg;
+  if (run_dense_hidden(h, x, m, nullptr, nullptr, bias, bias_scalar, tau, FFN_K_UP, s, true, FFN_K_GATE) !=
+      hipSuccess)
+    return FFN_E_HIP;
+  PackGDesc pd{};
+  pd.M = m;
+  pd.F = c.d_ff;
+  pd.T = c.tile_w;
+  pd.E = c.ell_w;
+  pd.sel = c.sel;
+  pd.out_f32 = 0;
+  pd.g = h->ws.g_ext;
+  pd.bias = bias;
+  pd.bias_scalar = bias_scalar;
+  pd.tau = tau;
+  pd.cnt = pack->cnt;
+  pd.idx = pack->idx;
+  pd.val = pack->val;
+  {
+    Timed tm(h, FFN_K_ROUTE, s);
+    if (launch_pack_g(pd, s) != hipSuccess) return FFN_E_HIP;
+  }
+  {
+    Timed tm(h, FFN_K_ROUTE, s);
+    if (launch_route(route_desc(h, m, pack), s) != hipSuccess) return FFN_E_HIP;
+  }
+  return hip_status(run_dense_down(h, m, nullptr, nullptr, y, FFN_K_UPDOWN, s));
+}
+
 static ffn_status forward_impl(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,
                               float bias_scalar, const float* tau, int32_t k, ffn_twell_pack* pack,
                               void* y, void* stream) {
@@ -1356,6 +1413,7 @@ static ffn_status forward_impl(ffn_sparse_handle* h, const void* x, int32_t m, c
     if (dd.mode == DEC_SPLIT) return hip_status(launch_dec_down2(dd, s));
     return hip_status(launch_dec_down(dd, s));
   }
+  if (masked_dense_ok(h, m)) return masked_dense_forward(h, x, m, bias, bias_scalar, tau, pack, y, s);
   const auto& c = h->cfg;
   // top-k selection keeps a fixed share of every token's neurons: one token's
   // kept rows go to the list-driven down kernel; from two tokens the union of
@@ -1508,6 +1566,7 @@ int32_t ffn_sparse_forward_path(const ffn_sparse_handle* h, int32_t m) {
   if (plan_decode(h, m, &dd)) return 1 + dd.mode;
   if (topk_down_kind(h, m) == 1) return 4;
   if (topk_down_kind(h, m) == 2) return 5;
+  if (masked_dense_ok(h, m)) return 7;
   return 0;
 }
 

@@ -179,6 +179,7 @@ __device__ __forceinline__ void epi_dense_h(const EpiDesc& e, const TileView& v)
     if (NMAT == 2) {
       gv = v.t[r * v.ldt + m];
       uv = v.t[(v.rpm + r) * v.ldt + m];
+      if (e.g_debug) e.g_debug[(size_t)slot * e.F + n] = gv;   // the gate values, for a pack built from them
     } else {
       gv = e.g_ext[(size_t)slot * e.F + n];
       uv = v.t[r * v.ldt + m];

@@ -94,4 +94,56 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// TwELL pack from stored gate values (the masked dense sequence): wave w of
+// the grid takes (token, tile) = (w / ntiles, w % ntiles) and walks the tile
+// 64 neurons at a time. A neuron is active when z = g + b exceeds the cut
+// (max(tau, 0) for a threshold, 0 for a bias); its slot is the count of
+// active neurons before it in the tile (ballot prefix), kept while below E.
+// [Sparser/Faster/Lighter page, "TwELL 減掉轉換開銷": the tile-wise ELL layout.]
+__global__ __launch_bounds__(256) void k_pack_g(const PackGDesc d) {
+  const int lane = threadIdx.x & 63;
+  const int ntiles = d.F / d.T;
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long long)d.M * ntiles) return;                 // whole waves
+  const int tok = (int)(w / ntiles), j = (int)(w - (long long)tok * ntiles);
+  const float b = d.bias ? d.bias[tok] : d.bias_scalar;
+  const float cut = d.sel == SEL_THRESH ? fmaxf(d.tau[tok], 0.f) : 0.f;
+  const float* gr = d.g + (size_t)tok * d.F + (size_t)j * d.T;
+  const size_t slot0 = ((size_t)tok * ntiles + j) * d.E;
+  int run = 0;
+  for (int c0 = 0; c0 < d.T; c0 += 64) {
+    const int r = c0 + lane;
+    float z = 0.f;
+    bool act = false;
+    if (r < d.T) {
+      z = gr[r] + b;
+      act = z > cut;
+    }
+    const uint64_t bal = ballot64(act);
+    const int pos = run + __popcll(bal & lanemask_lt());
+    if (act && pos < d.E) {
+      d.idx[slot0 + pos] = (uint16_t)r;
+      if (d.out_f32) reinterpret_cast<float*>(d.val)[slot0 + pos] = z;
+      else reinterpret_cast<uint16_t*>(d.val)[slot0 + pos] = (uint16_t)f2bf(z);
+    }
+    run += __popcll(bal);
+  }
+  if (lane == 0) d.cnt[(size_t)tok * ntiles + j] = run;
+  for (int sl = min(run, d.E) + lane; sl < d.E; sl += 64) {
+    d.idx[slot0 + sl] = 0xFFFF;
+    if (d.out_f32) reinterpret_cast<float*>(d.val)[slot0 + sl] = 0.f;
+    else reinterpret_cast<uint16_t*>(d.val)[slot0 + sl] = 0;
+  }
+}
+
+hipError_t launch_pack_g(const PackGDesc& d, hipStream_t s) {
+  if (d.M <= 0) return hipSuccess;
+  if (d.T <= 0 || d.T > 65535 || d.F % d.T != 0 || d.E < 0 || !d.g || !d.cnt || !d.idx || !d.val ||
+      (d.sel == SEL_THRESH && !d.tau))
+    return hipErrorInvalidValue;
+  const long long waves = (long long)d.M * (d.F / d.T);
+  ffn_launch(k_pack_g, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, d);
+  return hipGetLastError();
+}
+
 }  // namespace ffn

@@ -127,6 +127,18 @@ struct RouteDesc {
 };
 hipError_t launch_route(const RouteDesc& r, hipStream_t s);
 
+// TwELL pack of m tokens from their gate values g [m x F] (fp32, before the
+// bias), one wave per (token, TwELL tile): the selection z = g + b > cut of
+// the other epilogues, the first min(cnt, E) active offsets ascending, values
+// rounded to the pack type, padding, and the true count.
+struct PackGDesc {
+  int M, F, T, E, sel, out_f32;
+  const float* g;
+  const float* bias; float bias_scalar; const float* tau;
+  int32_t* cnt; uint16_t* idx; void* val;
+};
+hipError_t launch_pack_g(const PackGDesc& d, hipStream_t s);
+
 struct UpdownDesc {
   int dtype, M, d, F, T, E;
   int down_only;          // TOPK: pack values are h, no up product

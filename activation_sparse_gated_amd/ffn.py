@@ -167,13 +167,13 @@ class SparseFFN:
     def forward_path(self, m: int) -> str:
         """Kernel sequence forward() runs for m tokens: 'general',
         'decode-chunk' / 'decode-part' / 'decode-split', (top-k selection)
-        'topk-list' / 'topk-masked-dense', or 'input-gate' (input-side gate
-        selection; see the C header)."""
+        'topk-list' / 'topk-masked-dense', 'input-gate' (input-side gate
+        selection) or 'masked-dense' (17..127 tokens; see the C header)."""
         r = self.lib.ffn_sparse_forward_path(self.handle, int(m))
         if r < 0:
             raise ValueError(f"invalid token count {m}")
         return {0: "general", 1: "decode-chunk", 2: "decode-part", 3: "decode-split",
-                4: "topk-list", 5: "topk-masked-dense", 6: "input-gate"}[r]
+                4: "topk-list", 5: "topk-masked-dense", 6: "input-gate", 7: "masked-dense"}[r]
 
     def device_status(self, stream=None) -> int:
         """FFN_OK, or FFN_E_HIP when a launch failed or a bounded wait gave up

@@ -277,6 +277,12 @@ def main():
         # HBM minimum of the sparse pass: each union neuron's up and down rows
         # once (the per-entry re-reads are cache traffic)
         alg["updown"] = n_union * row_bytes + m * d * 2 + m * d * 2 + pack_bytes
+    elif path == "masked-dense":
+        # the dense products with the selection applied to every neuron: each
+        # weight byte once, the gate values [m x F] written and read, h [m x F]
+        alg["gate"] = F * r * 2 + m * r * 4 + m * F * 4              # U t (low rank)
+        alg["up"] = (F * d * 2 if r else 2 * F * d * 2) + m * d * 2 + m * F * (4 + 2)
+        alg["updown"] = F * d * 2 + m * F * 2 + m * d * 2
     elif path == "topk-masked-dense":
         alg["updown"] = F * d * 2 + m * F * 2 + m * d * 2      # all of W_down, the masked h rows, y
     if wl.sel == "topk":

@@ -293,6 +293,11 @@ ffn_status ffn_sparse_moe_forward(ffn_sparse_handle *const *experts, int32_t n_e
  *     channels per token, the gate from their rows of the input-major W_gate
  *     (or V) in channel groups, the selection and pack (or, low rank, t and
  *     then U t), the sparse up + down over the pack;
+ * 7 = masked dense (bf16 bias / threshold selection, 17..127 tokens): the
+ *     dense gate and up products with the selection applied to every neuron
+ *     (the gate values kept), the TwELL pack built from those gate values,
+ *     then a dense down GEMM; past 16 tokens the union of the tokens' active
+ *     neurons covers most rows, so no sparse pass reads fewer weight bytes;
  * 0 = the general sequence (gate, sparse up + down over the TwELL pack,
  * partial-row sum, dense backup); -1 = invalid handle or m. */
 int32_t ffn_sparse_forward_path(const ffn_sparse_handle *h, int32_t m);

@@ -93,6 +93,47 @@ def test_reduced(cid, m, kw):
     run_full(wl, ref)
 
 
+# 17..127 tokens run the masked dense sequence; the general sequence (sparse
+# up + down over the pack, dense backup of routed tokens) is kept reachable
+# by a path switch and must agree with it and with the oracle
+MIDSIZE = [
+    ("c2", 19, dict(d=512, f=2048, T=64, E=8)),
+    ("c3", 37, dict(d=256, f=1024, rank=32, T=64, E=8)),
+    ("c3", 64, dict(d=1024, f=4096, rank=128, T=128, E=64)),
+    ("c5", 67, dict(d=256, f=2048, T=256, E=32)),
+]
+
+
+@pytest.mark.parametrize("cid,m,kw", MIDSIZE, ids=[f"{c}-m{m}" for c, m, _ in MIDSIZE])
+def test_masked_dense_and_general_agree(cid, m, kw):
+    say("masked dense vs general", cid, m, kw)
+    import os
+
+    import torch
+    wl = make_workload(cid, m, 1, **kw)
+    ref = O.forward(wl)
+    x = to_dev(wl, wl.x)
+    outs = []
+    for env, path in (({}, "masked-dense"), ({"FFN_SPARSE_NO_MASKED_DENSE": "1"}, "general")):
+        os.environ.update(env)
+        try:
+            ffn = make_ffn(wl)
+        finally:
+            for k in env:
+                os.environ.pop(k, None)
+        assert ffn.forward_path(wl.m) == path
+        y, pack = ffn.forward(x, **sel_args(wl))
+        torch.cuda.synchronize()
+        check_pack(wl, pack, ref)
+        check_y(y_to_f64(wl, y)[: wl.m], ref["y"])
+        y_again, _ = ffn.forward(x, **sel_args(wl))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y_again), host(y))
+        outs.append((host(pack.cnt).copy(), host(pack.idx).copy(), host(pack.route).copy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("E", [0, 4, 8, 64])
 def test_tiny_fp32_ell_widths(E):
     say("c1 E", E)

@@ -65,7 +65,7 @@ def test_noalloc_refuses_other_sequences():
     from activation_sparse_gated_amd._lib import FFN_E_UNSUPPORTED, FFNError
     wl = make_workload("c2", 24, 0, d=256, f=1024, T=128, E=16)
     ffn = make_ffn(wl)
-    assert ffn.forward_path(24) == "general"
+    assert ffn.forward_path(24) == "masked-dense"
     with pytest.raises(FFNError) as e:
         ffn.forward_noalloc(to_dev(wl, wl.x), ffn.new_pack(24), ffn.new_output(24), **sel_args(wl))
     assert e.value.status == FFN_E_UNSUPPORTED
