@@ -18,9 +18,22 @@ __device__ inline void route_pass(const RouteDesc& r) {
     const int n = min(1024, r.M - c0);
     for (int i = threadIdx.x; i < 1024; i += blockDim.x) s_over[i] = 0;
     __syncthreads();
-    for (int p = threadIdx.x; p < n * r.ntiles; p += blockDim.x) {
-      const int t = p / r.ntiles;
-      if (r.cnt[(size_t)(c0 + t) * r.ntiles + (p % r.ntiles)] > r.E) s_over[t] = 1;
+    // sixteen counts per thread in flight, then tested: one memory round per
+    // 16 * blockDim counts instead of one per blockDim
+    const int np = n * r.ntiles;
+    const int32_t* cb = r.cnt + (size_t)c0 * r.ntiles;   // the chunk's tokens are consecutive rows
+    for (int p0 = threadIdx.x; p0 < np; p0 += 16 * blockDim.x) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int p = p0 + u * blockDim.x;
+        v[u] = p < np ? cb[p] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int p = p0 + u * blockDim.x;
+        if (p < np && v[u] > r.E) s_over[p / r.ntiles] = 1;
+      }
     }
     __syncthreads();
     int o[4], ro = 0;
