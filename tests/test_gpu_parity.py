@@ -101,6 +101,10 @@ MIDSIZE = [
     ("c3", 37, dict(d=256, f=1024, rank=32, T=64, E=8)),
     ("c3", 64, dict(d=1024, f=4096, rank=128, T=128, E=64)),
     ("c5", 67, dict(d=256, f=2048, T=256, E=32)),
+    # the prefill shape at 100 tokens: two token blocks; forced onto the
+    # general path, the routed tokens' dense down product runs on the skinny
+    # GEMM with K split four ways, a device-side token count and scattered rows
+    ("c5", 100, dict(T=1024, E=128)),
 ]
 
 
