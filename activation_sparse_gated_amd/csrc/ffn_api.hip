@@ -125,6 +125,39 @@ constexpr int kDecodeMaxM = 64;
 // fewer weight bytes than the dense products, and below the prefill shapes
 // (128 tokens) the products are weight streams.
 constexpr int kMaskedDenseMaxM = 127;
+// Up to 256 tokens the masked dense sequence also replaces the general path
+// of configurations whose pack the XCD-sliced pair cannot hold (more than 64
+// TwELL tiles, or 1024 slots a token), where the per-token sparse kernel would
+// gather every union row once per token (LoPA, 256 tokens: 695 us against
+// 293 us for the dense FFN).
+constexpr int kMaskedDenseMaxMNoXcd = 256;
+
+// Whether the XCD-sliced pair takes this configuration's pack (its shape
+// limits only; the token count and pointers are checked at the call).
+bool xcd_config_ok(const ffn_sparse_config& c) {
+  if (c.dtype != FFN_BF16 || c.sel == FFN_SEL_TOPK_WINA || c.tile_w <= 0 || c.ell_w <= 0) return false;
+  static char dummy[16];
+  XcdDesc x{};
+  x.M = 128;
+  x.d = c.d_model;
+  x.T = c.tile_w;
+  x.E = c.ell_w;
+  x.ntiles = c.d_ff / c.tile_w;
+  x.lg_e = 0;
+  while ((1 << x.lg_e) < x.E) ++x.lg_e;
+  x.x = x.w_up = x.w_down_nm = dummy;
+  x.cnt = reinterpret_cast<const int32_t*>(dummy);
+  x.idx = reinterpret_cast<const uint16_t*>(dummy);
+  x.val = dummy;
+  x.hp = reinterpret_cast<float*>(dummy);
+  x.y = dummy;
+  return xcd_ok(x);
+}
+
+// Largest token count of the masked dense sequence for a configuration.
+int masked_dense_max_m(const ffn_sparse_config& c) {
+  return xcd_config_ok(c) ? kMaskedDenseMaxM : kMaskedDenseMaxMNoXcd;
+}
 
 struct Workspace {
   uint32_t* ctrl;       // kCtrlWords control words + kTicketWords tickets
@@ -187,7 +220,8 @@ Workspace carve(const ffn_sparse_config& c, char* base, int cus) {
   // gate values [tokens x F] fp32: the dense paths of a low-rank gate, and
   // the masked dense sequence (17..127 tokens; see masked_dense_ok)
   const bool md = c.dtype == FFN_BF16 && c.sel != FFN_SEL_TOPK_WINA && c.in_keep == 0 && M > (size_t)kDecMaxM;
-  w.g_ext = (float*)take(r ? M * F * sizeof(float) : (md ? std::min<size_t>(M, kMaskedDenseMaxM) * F * sizeof(float) : 16));
+  const size_t md_rows = std::min<size_t>(M, masked_dense_max_m(c));
+  w.g_ext = (float*)take(r ? M * F * sizeof(float) : (md ? md_rows * F * sizeof(float) : 16));
   const bool topk = c.sel == FFN_SEL_TOPK_WINA;
   w.wina_s = (float*)take(topk ? M * F * sizeof(float) : 16);
   w.wina_h = (float*)take(topk ? M * F * sizeof(float) : 16);
@@ -1354,7 +1388,7 @@ static int topk_down_kind(const ffn_sparse_handle* h, int m) {
 static bool masked_dense_ok(const ffn_sparse_handle* h, int m) {
   const auto& c = h->cfg;
   return c.dtype == FFN_BF16 && c.sel != FFN_SEL_TOPK_WINA && c.in_keep == 0 && !h->tune.no_masked_dense &&
-         m > kDecMaxM && m <= kMaskedDenseMaxM && m <= c.max_m;
+         m > kDecMaxM && m <= masked_dense_max_m(c) && m <= c.max_m;
 }
 
 static ffn_status masked_dense_forward(ffn_sparse_handle* h, const void* x, int32_t m, const float* bias,

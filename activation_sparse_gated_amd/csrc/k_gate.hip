@@ -5,6 +5,8 @@
 
 namespace ffn {
 
+constexpr int kSkPreferMaxM = 256;
+
 hipError_t launch_gemm_pack(const GemmDesc& g, const EpiDesc& e, hipStream_t s) {
   const dim3 grid = gemm_grid(g);
   if (g.dtype == DT_F32) {
@@ -21,7 +23,12 @@ hipError_t launch_gemm_pack(const GemmDesc& g, const EpiDesc& e, hipStream_t s) 
 
 hipError_t launch_gemm(const GemmDesc& g, const EpiDesc& e, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
-  if (pf_ok(g, e) && !g.no_pf) return launch_gemm_pf(g, e, s);
+  // up to 256 tokens the skinny kernel's 64-token blocks beat the 128 x 128
+  // prefill tiles, which leave most CUs idle there (LoPA shape, dense FFN: 128
+  // tokens 371 -> 166 us, 256 tokens 377 -> 293 us; at 512 tokens 407 vs
+  // 526 us); the TwELL gate keeps the prefill kernel's epilogue
+  const bool sk_first = g.M <= kSkPreferMaxM && e.kind != EPI_TWELL && sk_ok(g, e);
+  if (pf_ok(g, e) && !g.no_pf && !sk_first) return launch_gemm_pf(g, e, s);
   if (sk_ok(g, e)) return launch_gemm_sk(g, e, s);
   if (g.nwaves != 4 && g.nwaves != 16) return hipErrorInvalidValue;
   if (e.kind == EPI_STORE_F32 || e.kind == EPI_TWELL) return launch_gemm_pack(g, e, s);

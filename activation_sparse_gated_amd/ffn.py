@@ -168,7 +168,8 @@ class SparseFFN:
         """Kernel sequence forward() runs for m tokens: 'general',
         'decode-chunk' / 'decode-part' / 'decode-split', (top-k selection)
         'topk-list' / 'topk-masked-dense', 'input-gate' (input-side gate
-        selection) or 'masked-dense' (17..127 tokens; see the C header)."""
+        selection) or 'masked-dense' (17..127 tokens, up to 256 for packs the
+        XCD-sliced kernels cannot hold; see the C header)."""
         r = self.lib.ffn_sparse_forward_path(self.handle, int(m))
         if r < 0:
             raise ValueError(f"invalid token count {m}")

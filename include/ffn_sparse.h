@@ -293,7 +293,9 @@ ffn_status ffn_sparse_moe_forward(ffn_sparse_handle *const *experts, int32_t n_e
  *     channels per token, the gate from their rows of the input-major W_gate
  *     (or V) in channel groups, the selection and pack (or, low rank, t and
  *     then U t), the sparse up + down over the pack;
- * 7 = masked dense (bf16 bias / threshold selection, 17..127 tokens): the
+ * 7 = masked dense (bf16 bias / threshold selection, 17..127 tokens, or up
+ *     to 256 when the pack has more than 64 TwELL tiles or 1024 slots a
+ *     token, which the prefill sequence's XCD-sliced kernels cannot hold): the
  *     dense gate and up products with the selection applied to every neuron
  *     (the gate values kept), the TwELL pack built from those gate values,
  *     then a dense down GEMM; past 16 tokens the union of the tokens' active

@@ -108,6 +108,9 @@ MIDSIZE = [
     # ELL width 0 (every token with an active neuron is routed) and TwELL
     # tiles narrower than a wave
     ("c2", 20, dict(d=256, f=1024, T=32, E=0)),
+    # 72 TwELL tiles, more than the XCD-sliced pair holds: the masked dense
+    # sequence up to 256 tokens, three token blocks
+    ("c3", 160, dict(d=512, f=9216, rank=64, T=128, E=64)),
 ]
 
 
